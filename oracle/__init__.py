@@ -1,0 +1,96 @@
+"""fp64 CPU oracle for the attention forward pass.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the bench's
+CPU-baseline leg are the only callers. The GPU path does not import this
+package, and this package imports nothing from the GPU path.
+
+The arithmetic lives in ``fa_oracle.c`` (plain C, double precision); this
+module builds it with gcc and marshals arrays through ctypes. See the header
+of ``fa_oracle.c`` for the definition it follows and the passages it cites.
+"""
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(src=_SRC, out=_LIB, extra_flags=()):
+    """Compile the oracle (or a variant of its source) into a shared library."""
+    cmd = ["gcc", "-O2", "-std=c11", "-shared", "-fPIC", "-pthread", *extra_flags,
+           src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _bind(lib):
+    fn = lib.fa_oracle_fwd
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 4 + [
+        ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    return lib
+
+
+def load(path=None):
+    """Load the built oracle, building it first if it is missing."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def default_threads():
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def _as_f32(x):
+    """dtype-rounded tensor/array -> contiguous fp32 numpy (exact for fp16/bf16)."""
+    if hasattr(x, "detach"):  # torch tensor, possibly bf16
+        import torch
+        x = x.detach().to("cpu", torch.float32).contiguous().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def attention_fwd(q, k, v, causal, scale, rows=None, tile_n=0, nthreads=None, lib=None):
+    """fp64 attention forward on the CPU.
+
+    q, k, v : ``[B, H, N, d]`` (torch or numpy; values already in the storage
+              dtype). ``scale`` is applied to Q.K^T before the softmax.
+    rows    : optional sorted list of query rows to evaluate (all by default).
+    tile_n  : 0 for the two-pass definition, > 0 for the online order.
+    Returns ``(o, lse)`` as float64 numpy arrays of shape ``[B, H, R, d]`` and
+    ``[B, H, R]``, where ``R`` is ``len(rows)`` or ``N``; lse is natural-log.
+    """
+    lib = lib or load()
+    qf, kf, vf = _as_f32(q), _as_f32(k), _as_f32(v)
+    B, H, N, d = qf.shape
+    assert kf.shape == qf.shape and vf.shape == qf.shape
+    if rows is None:
+        R, rows_arr, rows_ptr = N, None, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        R, rows_ptr = rows_arr.size, rows_arr.ctypes.data
+    o = np.empty((B, H, R, d), dtype=np.float64)
+    lse = np.empty((B, H, R), dtype=np.float64)
+    rc = lib.fa_oracle_fwd(qf.ctypes.data, kf.ctypes.data, vf.ctypes.data, B, H, N, d,
+                           1 if causal else 0, float(scale), rows_ptr,
+                           0 if rows_arr is None else R, int(tile_n), o.ctypes.data,
+                           lse.ctypes.data, int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"fa_oracle_fwd failed with status {rc}")
+    return o, lse

@@ -1,0 +1,249 @@
+/*
+ * fa_oracle.c -- plain fp64 CPU reference for the attention forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * bench's CPU-baseline leg may load this library. The GPU path never calls
+ * it, includes it or shares code with it.
+ *
+ * What it computes, per batch b, head h and query row i (all independent):
+ *
+ *   s_j   = scale * sum_c q[b,h,i,c] * k[b,h,j,c]      for visible keys j
+ *   O_i   = sum_j softmax(s)_j * v[b,h,j,:]
+ *   lse_i = ln sum_j exp(s_j)
+ *
+ * The definition of attention with its scale applied to Q.K^T before the
+ * softmax is the one in "Programming an attention kernel in Triton",
+ * section "Kernel 4: bringing it together, a self-attention kernel"; the
+ * max subtraction before the exponential is from the same page, "Kernel 3:
+ * fused softmax". A causal row i sees keys j <= i (the keep test of the
+ * causal mask in "How to optimise a Triton FlashAttention-2 kernel step by
+ * step with a profiler", Round 4, "Causal tile-skipping"). The per-row
+ * logsumexp is stored in natural-log units (same page, Round 4, "exp2": the
+ * kernel converts its base-2 state back because its tests compare against a
+ * natural-log logsumexp).
+ *
+ * Two evaluation orders are provided:
+ *   - two-pass (tile_n == 0): all scores of a row, then their max, then the
+ *     exponentials and the weighted sum. This is the plain definition.
+ *   - online over key tiles (tile_n > 0): a running max m, running sum l and
+ *     unnormalised output O, rescaled whenever a tile raises the max; the
+ *     method named at the end of "Programming an attention kernel in
+ *     Triton" ("The wall, named honestly") and kept as fp32 state by the
+ *     FlashAttention-2 kernel of the profiler page ("Where the last article
+ *     left off"). In exact arithmetic both orders give the same result.
+ *
+ * Inputs are fp32 arrays holding values that were already rounded to the
+ * storage dtype (fp16/bf16 values are exact in fp32); every product and sum
+ * is carried out in double. Nothing here is blocked, fused or reordered
+ * beyond the steps named above.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ROWS_PER_ITEM 16
+
+typedef struct {
+    const float *q, *k, *v;
+    int64_t B, H, N, d;
+    int causal;
+    double scale;
+    const int64_t *rows; /* NULL: all rows 0..N-1 */
+    int64_t n_rows;      /* rows per (b, h) in the output */
+    int64_t tile_n;      /* 0: two-pass; > 0: online over key tiles */
+    double *o, *lse;
+    int64_t n_items;
+    int64_t next_item; /* shared work counter */
+    pthread_mutex_t lock;
+    int status;
+} job_t;
+
+/* Score of query row i against key row j: scale * <q_i, k_j>, in double. */
+static double score(const float *qi, const float *kj, int64_t d, double scale)
+{
+    double acc = 0.0;
+    for (int64_t c = 0; c < d; ++c)
+        acc += (double)qi[c] * (double)kj[c];
+    return scale * acc;
+}
+
+/* Number of keys row i may attend to: all N, or keys 0..i when causal. */
+static int64_t visible_keys(int64_t i, int64_t N, int causal)
+{
+    return causal ? i + 1 : N;
+}
+
+/* The plain definition, evaluated in two passes over the scores. */
+static void row_two_pass(const float *qi, const float *kh, const float *vh,
+                         int64_t nvis, int64_t d, double scale, double *s,
+                         double *o_row, double *lse_out)
+{
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nvis; ++j) {
+        s[j] = score(qi, kh + j * d, d, scale);
+        if (s[j] > m)
+            m = s[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < nvis; ++j) {
+        s[j] = exp(s[j] - m);
+        l += s[j];
+    }
+    for (int64_t c = 0; c < d; ++c)
+        o_row[c] = 0.0;
+    for (int64_t j = 0; j < nvis; ++j) {
+        const float *vj = vh + j * d;
+        for (int64_t c = 0; c < d; ++c)
+            o_row[c] += s[j] * (double)vj[c];
+    }
+    for (int64_t c = 0; c < d; ++c)
+        o_row[c] /= l;
+    *lse_out = m + log(l);
+}
+
+/* The same quantity with the online softmax: key tiles [t0, t0 + tile_n) in
+ * order, each folded into the running (m, l, O). Keys at or past nvis are
+ * masked out; a tile with no visible key is not visited. */
+static void row_online(const float *qi, const float *kh, const float *vh,
+                       int64_t nvis, int64_t d, double scale, int64_t tile_n,
+                       double *s, double *o_row, double *lse_out)
+{
+    double m = 0.0, l = 0.0;
+    int started = 0;
+    for (int64_t c = 0; c < d; ++c)
+        o_row[c] = 0.0;
+    for (int64_t t0 = 0; t0 < nvis; t0 += tile_n) {
+        int64_t t1 = t0 + tile_n < nvis ? t0 + tile_n : nvis;
+        double m_tile = -INFINITY;
+        for (int64_t j = t0; j < t1; ++j) {
+            s[j - t0] = score(qi, kh + j * d, d, scale);
+            if (s[j - t0] > m_tile)
+                m_tile = s[j - t0];
+        }
+        double m_new = (!started || m_tile > m) ? m_tile : m;
+        double alpha = started ? exp(m - m_new) : 0.0;
+        l *= alpha;
+        for (int64_t c = 0; c < d; ++c)
+            o_row[c] *= alpha;
+        for (int64_t j = t0; j < t1; ++j) {
+            double p = exp(s[j - t0] - m_new);
+            const float *vj = vh + j * d;
+            l += p;
+            for (int64_t c = 0; c < d; ++c)
+                o_row[c] += p * (double)vj[c];
+        }
+        m = m_new;
+        started = 1;
+    }
+    for (int64_t c = 0; c < d; ++c)
+        o_row[c] /= l;
+    *lse_out = m + log(l);
+}
+
+static void *worker(void *arg)
+{
+    job_t *job = (job_t *)arg;
+    const int64_t d = job->d, N = job->N;
+    int64_t scratch_n = job->tile_n > 0 ? job->tile_n : N;
+    double *s = (double *)malloc(sizeof(double) * (size_t)scratch_n);
+    if (!s) {
+        pthread_mutex_lock(&job->lock);
+        job->status = -2;
+        pthread_mutex_unlock(&job->lock);
+        return NULL;
+    }
+    const int64_t chunks = (job->n_rows + ROWS_PER_ITEM - 1) / ROWS_PER_ITEM;
+    for (;;) {
+        pthread_mutex_lock(&job->lock);
+        int64_t item = job->next_item++;
+        pthread_mutex_unlock(&job->lock);
+        if (item >= job->n_items)
+            break;
+        int64_t bh = item / chunks;
+        int64_t r0 = (item % chunks) * ROWS_PER_ITEM;
+        int64_t r1 = r0 + ROWS_PER_ITEM < job->n_rows ? r0 + ROWS_PER_ITEM : job->n_rows;
+        const float *qh = job->q + bh * N * d;
+        const float *kh = job->k + bh * N * d;
+        const float *vh = job->v + bh * N * d;
+        for (int64_t r = r0; r < r1; ++r) {
+            int64_t i = job->rows ? job->rows[r] : r;
+            int64_t nvis = visible_keys(i, N, job->causal);
+            double *o_row = job->o + (bh * job->n_rows + r) * d;
+            double *lse_out = job->lse + bh * job->n_rows + r;
+            if (job->tile_n > 0)
+                row_online(qh + i * d, kh, vh, nvis, d, job->scale, job->tile_n, s, o_row,
+                           lse_out);
+            else
+                row_two_pass(qh + i * d, kh, vh, nvis, d, job->scale, s, o_row, lse_out);
+        }
+    }
+    free(s);
+    return NULL;
+}
+
+/*
+ * fa_oracle_fwd: O and lse for the rows listed in `rows` (NULL = every row)
+ * of every (b, h).
+ *   q, k, v : fp32, [B, H, N, d] contiguous (dtype-rounded values).
+ *   o       : double, [B, H, R, d] with R = n_rows (or N when rows is NULL).
+ *   lse     : double, [B, H, R], natural log.
+ *   tile_n  : 0 for the two-pass definition, > 0 for the online order.
+ * Returns 0 on success, -1 on a bad argument, -2 when memory runs out.
+ */
+int fa_oracle_fwd(const float *q, const float *k, const float *v, int64_t B, int64_t H,
+                  int64_t N, int64_t d, int causal, double scale, const int64_t *rows,
+                  int64_t n_rows, int64_t tile_n, double *o, double *lse, int nthreads)
+{
+    if (!q || !k || !v || !o || !lse || B < 1 || H < 1 || N < 1 || d < 1 || tile_n < 0)
+        return -1;
+    if (rows) {
+        if (n_rows < 1)
+            return -1;
+        for (int64_t r = 0; r < n_rows; ++r)
+            if (rows[r] < 0 || rows[r] >= N)
+                return -1;
+    } else {
+        n_rows = N;
+    }
+    if (nthreads < 1)
+        nthreads = 1;
+    job_t job;
+    memset(&job, 0, sizeof(job));
+    job.q = q;
+    job.k = k;
+    job.v = v;
+    job.B = B;
+    job.H = H;
+    job.N = N;
+    job.d = d;
+    job.causal = causal ? 1 : 0;
+    job.scale = scale;
+    job.rows = rows;
+    job.n_rows = n_rows;
+    job.tile_n = tile_n;
+    job.o = o;
+    job.lse = lse;
+    job.n_items = B * H * ((n_rows + ROWS_PER_ITEM - 1) / ROWS_PER_ITEM);
+    pthread_mutex_init(&job.lock, NULL);
+    if (nthreads > job.n_items)
+        nthreads = (int)job.n_items;
+    pthread_t *tids = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!tids) {
+        pthread_mutex_destroy(&job.lock);
+        return -2;
+    }
+    int started = 0;
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&tids[t], NULL, worker, &job) != 0)
+            break;
+        ++started;
+    }
+    worker(&job);
+    for (int t = 1; t <= started; ++t)
+        pthread_join(tids[t], NULL);
+    free(tids);
+    pthread_mutex_destroy(&job.lock);
+    return job.status;
+}

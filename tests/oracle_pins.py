@@ -1,0 +1,241 @@
+"""Pins for the fp64 oracle: checks against facts other than the oracle itself.
+
+Each pin takes ``fwd`` (a callable with the signature of
+``oracle.attention_fwd``) and raises ``AssertionError`` when the oracle
+disagrees with what the pages and the mathematics fix. They are run against
+the real oracle in ``test_oracle_pins.py`` and against deliberately broken
+copies of it in ``test_oracle_mutants.py`` (every broken copy must fail at
+least one pin).
+
+What pins what:
+  decimal_bruteforce   the definition itself, at 50 digits, on tiny shapes
+  torch_sdpa           a library routine computing the same definition (fp64)
+  keys_zero            closed form: uniform softmax, O = mean of visible V, lse = ln|J|
+  causal_row0          row 0 attends only to itself: O_0 = V_0 exactly
+  causal_last_row      causal row N-1 sees every key: equals the non-causal row
+  prefix_truncation    causal rows < N' do not depend on keys >= N'
+  v_ones               rows of the softmax sum to one
+  v_identity           O = P when V = I; checked against scipy's softmax
+  online_equals_twopass  the online-softmax identity, several tile sizes
+  linearity            O is linear in V
+  permutation          non-causal O is invariant to permuting keys with values
+  single_key           N = 1: O = V, lse = s_00
+  shift                adding a vector to every key shifts each row's scores
+                       by a constant: O unchanged, lse shifted (also needs the
+                       max subtraction at scores of several thousand)
+"""
+
+from decimal import Decimal, getcontext
+
+import numpy as np
+import scipy.special
+import torch
+
+from fa_inputs import make_qkv
+
+
+def _f(x):
+    return x.float().numpy().astype(np.float64) if hasattr(x, "float") else np.asarray(x, np.float64)
+
+
+def _close(a, b, rtol, what):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    err = np.max(np.abs(a - b) / np.maximum(1.0, np.abs(b))) if a.size else 0.0
+    assert err <= rtol, f"{what}: max scaled error {err:.3e} > {rtol:.1e}"
+
+
+def _decimal_attention(q, k, v, causal, scale):
+    """Attention of one head, [N, d] float inputs, evaluated in 50-digit decimal."""
+    getcontext().prec = 50
+    N, d = q.shape
+    Q = [[Decimal(float(x)) for x in row] for row in q]
+    K = [[Decimal(float(x)) for x in row] for row in k]
+    V = [[Decimal(float(x)) for x in row] for row in v]
+    sc = Decimal(float(scale))
+    o = np.zeros((N, d))
+    lse = np.zeros(N)
+    for i in range(N):
+        J = range(i + 1) if causal else range(N)
+        s = [sc * sum(Q[i][c] * K[j][c] for c in range(d)) for j in J]
+        e = [x.exp() for x in s]
+        den = sum(e)
+        for c in range(d):
+            o[i, c] = float(sum(e[t] * V[j][c] for t, j in enumerate(J)) / den)
+        lse[i] = float(den.ln())
+    return o, lse
+
+
+def decimal_bruteforce(fwd):
+    for seed, (B, H, N, d) in enumerate([(1, 1, 1, 4), (1, 1, 5, 3), (2, 2, 8, 8), (1, 3, 7, 1)]):
+        q, k, v = make_qkv(B, H, N, d, "fp16", 100 + seed)
+        scale = float(np.float32(1.0 / np.sqrt(d)))
+        for causal in (False, True):
+            o, lse = fwd(q, k, v, causal, scale)
+            for b in range(B):
+                for h in range(H):
+                    od, ld = _decimal_attention(_f(q[b, h]), _f(k[b, h]), _f(v[b, h]), causal, scale)
+                    _close(o[b, h], od, 1e-14, f"decimal O {B,H,N,d} causal={causal}")
+                    _close(lse[b, h], ld, 1e-14, f"decimal lse {B,H,N,d} causal={causal}")
+
+
+def _torch_reference(q, k, v, causal, scale):
+    q64, k64, v64 = (t.to(torch.float64) for t in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(q64, k64, v64, is_causal=causal, scale=scale)
+    s = torch.matmul(q64, k64.transpose(-1, -2).contiguous()) * scale
+    if causal:
+        n = s.shape[-1]
+        s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+    return o.numpy(), torch.logsumexp(s, dim=-1).numpy()
+
+
+def torch_sdpa(fwd):
+    for dtype, (B, H, N, d), qs in [("fp16", (2, 3, 67, 16), 1.0), ("bf16", (1, 2, 130, 64), 1.0),
+                                   ("bf16", (1, 2, 96, 32), 4.0)]:
+        q, k, v = make_qkv(B, H, N, d, dtype, 7, q_scale=qs)
+        scale = float(np.float32(1.0 / np.sqrt(d)))
+        for causal in (False, True):
+            o, lse = fwd(q, k, v, causal, scale)
+            ot, lt = _torch_reference(q, k, v, causal, scale)
+            _close(o, ot, 1e-12, f"sdpa O {dtype} {B,H,N,d} q*{qs} causal={causal}")
+            _close(lse, lt, 1e-12, f"sdpa lse {dtype} {B,H,N,d} q*{qs} causal={causal}")
+
+
+def keys_zero(fwd):
+    B, H, N, d = 2, 2, 1000, 64
+    q, _, v = make_qkv(B, H, N, d, "bf16", 11)
+    k = torch.zeros_like(q)
+    scale = 0.125
+    vf = _f(v)
+    counts = np.arange(1, N + 1, dtype=np.float64)
+    for causal in (False, True):
+        o, lse = fwd(q, k, v, causal, scale)
+        if causal:
+            mean = np.cumsum(vf, axis=2) / counts[None, None, :, None]
+            lse_exp = np.broadcast_to(np.log(counts), (B, H, N))
+        else:
+            mean = np.broadcast_to(vf.mean(axis=2, keepdims=True), vf.shape)
+            lse_exp = np.full((B, H, N), np.log(N))
+        _close(o, mean, 1e-12, f"K=0 mean of V causal={causal}")
+        _close(lse, lse_exp, 1e-13, f"K=0 lse = ln|J| causal={causal}")
+
+
+def causal_row0(fwd):
+    for dtype in ("fp16", "bf16"):
+        q, k, v = make_qkv(2, 3, 50, 64, dtype, 12)
+        scale = 0.125
+        o, lse = fwd(q, k, v, True, scale)
+        assert np.array_equal(o[:, :, 0, :], _f(v[:, :, 0, :])), "causal row 0 must equal V[0] exactly"
+        s00 = scale * np.einsum("bhc,bhc->bh", _f(q[:, :, 0, :]), _f(k[:, :, 0, :]))
+        _close(lse[:, :, 0], s00, 1e-14, "causal lse_0 = s_00")
+
+
+def causal_last_row(fwd):
+    q, k, v = make_qkv(1, 2, 333, 64, "fp16", 13)
+    o_c, l_c = fwd(q, k, v, True, 0.125)
+    o_n, l_n = fwd(q, k, v, False, 0.125)
+    assert np.array_equal(o_c[:, :, -1], o_n[:, :, -1]), "causal last row != non-causal last row"
+    assert np.array_equal(l_c[:, :, -1], l_n[:, :, -1])
+    assert not np.allclose(o_c[:, :, :-1], o_n[:, :, :-1]), "causal and non-causal must differ above"
+
+
+def prefix_truncation(fwd):
+    q, k, v = make_qkv(1, 2, 1024, 64, "bf16", 14)
+    o_full, l_full = fwd(q, k, v, True, 0.125)
+    n2 = 1000
+    o_pre, l_pre = fwd(q[:, :, :n2].contiguous(), k[:, :, :n2].contiguous(), v[:, :, :n2].contiguous(),
+                       True, 0.125)
+    assert np.array_equal(o_full[:, :, :n2], o_pre), "causal rows < N' depend on keys >= N'"
+    assert np.array_equal(l_full[:, :, :n2], l_pre)
+
+
+def v_ones(fwd):
+    q, k, _ = make_qkv(2, 2, 257, 64, "fp16", 15)
+    v = torch.ones_like(q)
+    for causal in (False, True):
+        o, _ = fwd(q, k, v, causal, 0.125)
+        _close(o, np.ones_like(o), 1e-14, f"V=1 gives O=1 causal={causal}")
+
+
+def v_identity(fwd):
+    N = d = 64
+    q, k, _ = make_qkv(1, 1, N, d, "bf16", 16)
+    v = torch.eye(N, dtype=torch.float32).reshape(1, 1, N, N)
+    s = 0.125 * (_f(q[0, 0]) @ _f(k[0, 0]).T)
+    for causal in (False, True):
+        o, _ = fwd(q, k, v, causal, 0.125)
+        p = o[0, 0]
+        _close(p.sum(axis=1), np.ones(N), 1e-14, f"rows of P sum to 1 causal={causal}")
+        sm = s.copy()
+        if causal:
+            sm[np.triu_indices(N, 1)] = -np.inf
+            assert np.all(p[np.triu_indices(N, 1)] == 0.0), "causal P must be 0 above the diagonal"
+        _close(p, scipy.special.softmax(sm, axis=1), 1e-13, f"P vs scipy softmax causal={causal}")
+
+
+def online_equals_twopass(fwd):
+    q, k, v = make_qkv(1, 2, 1000, 64, "fp16", 17)
+    for causal in (False, True):
+        o2, l2 = fwd(q, k, v, causal, 0.125)
+        for tn in (1, 7, 16, 64, 128, 1000, 1024):
+            ot, lt = fwd(q, k, v, causal, 0.125, tile_n=tn)
+            _close(ot, o2, 1e-12, f"online (tile {tn}) vs two-pass O causal={causal}")
+            _close(lt, l2, 1e-12, f"online (tile {tn}) vs two-pass lse causal={causal}")
+
+
+def linearity(fwd):
+    g = torch.Generator().manual_seed(18)
+    q, k, _ = make_qkv(1, 2, 200, 32, "fp16", 18)
+    v1 = torch.randint(-8, 9, (1, 2, 200, 32), generator=g).float()
+    v2 = torch.randint(-8, 9, (1, 2, 200, 32), generator=g).float()
+    for causal in (False, True):
+        o1, _ = fwd(q, k, v1, causal, 0.125)
+        o2, _ = fwd(q, k, v2, causal, 0.125)
+        o3, _ = fwd(q, k, 3 * v1 - 2 * v2, causal, 0.125)
+        _close(o3, 3 * o1 - 2 * o2, 1e-12, f"linearity in V causal={causal}")
+
+
+def permutation(fwd):
+    q, k, v = make_qkv(1, 2, 300, 64, "bf16", 19)
+    g = torch.Generator().manual_seed(19)
+    perm = torch.randperm(300, generator=g)
+    o, lse = fwd(q, k, v, False, 0.125)
+    o_k, lse_k = fwd(q, k[:, :, perm].contiguous(), v[:, :, perm].contiguous(), False, 0.125)
+    _close(o_k, o, 1e-13, "permuting keys with values leaves O unchanged")
+    _close(lse_k, lse, 1e-13, "permuting keys with values leaves lse unchanged")
+    o_q, lse_q = fwd(q[:, :, perm].contiguous(), k, v, False, 0.125)
+    assert np.array_equal(o_q, o[:, :, perm.numpy()]), "permuting queries must permute O rows"
+    assert np.array_equal(lse_q, lse[:, :, perm.numpy()])
+
+
+def single_key(fwd):
+    q, k, v = make_qkv(2, 2, 1, 64, "fp16", 20)
+    for causal in (False, True):
+        o, lse = fwd(q, k, v, causal, 0.125)
+        assert np.array_equal(o, _f(v)), "N=1: O must equal V"
+        s00 = 0.125 * np.einsum("bhnc,bhnc->bhn", _f(q), _f(k))
+        _close(lse, s00, 1e-14, "N=1: lse = s_00")
+
+
+def shift(fwd):
+    g = torch.Generator().manual_seed(21)
+    B, H, N, d = 1, 2, 96, 64
+    # values on a 1/8 grid: every product and sum below is exact in double
+    q = torch.round(torch.randn(B, H, N, d, generator=g) * 8) / 8
+    k = torch.round(torch.randn(B, H, N, d, generator=g) * 8) / 8
+    v = torch.randn(B, H, N, d, generator=g)
+    for mag in (1.0, 4096.0):
+        u = torch.round(torch.randn(d, generator=g) * 4) / 4 * mag
+        qu = 0.125 * (_f(q) @ _f(u))  # [B, H, N]: the per-row constant added to the scores
+        for causal in (False, True):
+            o, lse = fwd(q, k, v, causal, 0.125)
+            o_s, lse_s = fwd(q, k + u, v, causal, 0.125)
+            _close(o_s, o, 1e-12, f"shifted keys leave O unchanged (|u|~{mag}) causal={causal}")
+            _close(lse_s, lse + qu, 1e-12, f"shifted keys shift lse (|u|~{mag}) causal={causal}")
+
+
+ALL_PINS = [decimal_bruteforce, torch_sdpa, keys_zero, causal_row0, causal_last_row,
+            prefix_truncation, v_ones, v_identity, online_equals_twopass, linearity,
+            permutation, single_key, shift]
