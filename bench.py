@@ -1,0 +1,328 @@
+"""Benchmark of libfa's attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload (the headline configuration): B=4, H=16, N=4096, d=128, bf16
+inputs/outputs with fp32 softmax and accumulation, Q/K/V iid N(0,1) from a
+fixed seed, scale = 1/sqrt(d). One step is one non-causal forward followed by
+one causal forward on the same resident inputs, so a step covers every stage
+of the path including the causal tile skip.
+
+FLOPs follow the pages' convention, 4*B*H*N^2*d per forward, halved for
+causal. ``value`` is the step's FLOPs over the step's wall time (HIP events
+around the K timed steps). Per-kernel durations come from HIP events recorded
+around every launch on the launch stream; the roofline entry uses the
+non-causal kernel's average duration.
+
+Other modes (used to collect counters; each runs a few launches only):
+    --profile-kernels   a few launches of each headline kernel, nothing else
+    --copy-calibration  a plain device-to-device copy of a known size
+    --sweep             medians of 50 for every configuration of the workload
+                        list, with peak memory (one extra JSON object)
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk/CU x 2.4 GHz, dense (no sparsity)
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_forward_fwd_amd", "csrc", f)
+                  for f in ("fa_fwd_kernel.hip", "fa_tiles.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_bf16_d128_N4096.txt")
+
+HEADLINE = dict(B=4, H=16, N=4096, d=128, dtype="bf16", seed=7)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the non-causal headline kernel, from the
+    committed rocprofv3 counter summary, if it was taken on this kernel source."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m_hash = re.search(r"^kernel_source_sha256_16:\s*(\w+)", text, re.M)
+    m_bytes = re.search(r"^hbm_bytes_per_launch_noncausal:\s*([0-9.eE+]+)", text, re.M)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def make_inputs(cfg, device):
+    from fa_inputs import make_qkv
+    q, k, v = make_qkv(cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["dtype"], cfg["seed"],
+                       q_scale=cfg.get("q_scale", 1.0))
+    return q, k, v, q.to(device), k.to(device), v.to(device)
+
+
+def timed_launches(fn, n, stream):
+    """Run fn n times, each bracketed by HIP events on `stream`; returns ms list."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def warm(fn, min_calls, min_seconds):
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while n < min_calls or time.perf_counter() - t0 < min_seconds:
+        fn()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def cpu_baseline(cfg, q, k, v, stride):
+    """The fp64 oracle on a bounded row sample of the workload (host cores)."""
+    import oracle
+    import tiled_attention_forward_fwd_amd as fa
+    N = cfg["N"]
+    rows = list(range(0, N, stride))
+    scale = fa.default_scale(cfg["d"])
+    threads = oracle.default_threads()
+    flops = 0.0
+    t0 = time.perf_counter()
+    for causal in (False, True):
+        oracle.attention_fwd(q, k, v, causal, scale, rows=rows, nthreads=threads)
+        keys = sum((r + 1) if causal else N for r in rows)
+        flops += 4.0 * cfg["B"] * cfg["H"] * keys * cfg["d"]
+    dt = time.perf_counter() - t0
+    # the same convention as the GPU: the causal pass counts half of the full rows' keys
+    conv = 4.0 * cfg["B"] * cfg["H"] * len(rows) * N * cfg["d"] * 1.5
+    return {"value": conv / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"B={cfg['B']} H={cfg['H']} N={N} d={cfg['d']} {cfg['dtype']}: every "
+                       f"{stride}th query row ({len(rows)} rows per head, all heads), one "
+                       f"non-causal and one causal pass, fp64 two-pass; {dt:.1f} s wall; FLOPs "
+                       f"counted like the GPU step (causal = half the rows' full key count); "
+                       f"exact visited-key FLOPs {flops / 1e9:.1f} G"),
+            "seconds": dt}
+
+
+def headline(args):
+    import torch
+    import tiled_attention_forward_fwd_amd as fa
+    cfg = HEADLINE
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v, qd, kd, vd = make_inputs(cfg, dev)
+    B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, N), device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream(dev)
+    plan_nc = fa.fa_plan(B, H, N, d, 0, fa.FA_DTYPE_BF16)
+    plan_c = fa.fa_plan(B, H, N, d, 1, fa.FA_DTYPE_BF16)
+
+    def nc():
+        fa.fwd(qd, kd, vd, causal=False, out=o, lse=lse)
+
+    def c():
+        fa.fwd(qd, kd, vd, causal=True, out=o, lse=lse)
+
+    def step():
+        nc()
+        c()
+
+    # warmup: W steps plus at least one second of back-to-back launches
+    warm(step, args.warmup, 1.0)
+    torch.cuda.reset_peak_memory_stats(dev)
+
+    ev_nc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    ev_c = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        ev_nc[i][0].record(stream)
+        nc()
+        ev_nc[i][1].record(stream)
+        ev_c[i][0].record(stream)
+        c()
+        ev_c[i][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    t_nc = [a.elapsed_time(b) for a, b in ev_nc]
+    t_c = [a.elapsed_time(b) for a, b in ev_c]
+    peak_mem = torch.cuda.max_memory_allocated(dev)
+
+    flops_step = plan_nc["algo_flops"] + plan_c["algo_flops"]
+    ms_step = total_ms / args.steps
+    value = flops_step / (ms_step * 1e-3) / 1e12
+
+    def kstats(ts, plan):
+        avg, med = sum(ts) / len(ts), statistics.median(ts)
+        return {"avg_ms": avg, "median_ms": med, "min_ms": min(ts), "max_ms": max(ts),
+                "tflops_median": plan["algo_flops"] / (med * 1e-3) / 1e12,
+                "frac_peak_median": plan["algo_flops"] / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                "mfma_flops_executed": plan["mfma_flops"], "algo_flops": plan["algo_flops"],
+                "workgroups": plan["workgroups"]}
+
+    k_nc, k_c = kstats(t_nc, plan_nc), kstats(t_c, plan_c)
+    achieved = plan_nc["algo_flops"] / (k_nc["avg_ms"] * 1e-3) / 1e12
+    traffic = measured_traffic()
+    out = {
+        "metric": "attention fwd TFLOP/s at N=4096 bf16 (causal/non-causal); % of MFMA peak",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded iid N(0,1) Q/K/V, rounded to bf16)",
+        "config": {"workload": "attention forward B=4 H=16 N=4096 d=128 bf16, one non-causal + "
+                               "one causal pass per step",
+                   "B": B, "H": H, "N": N, "d": d, "scale": fa.default_scale(d),
+                   "parallelism": "single GPU"},
+        "frac_peak": value / PEAK_BF16_TFLOPS,
+        "kernels": {"noncausal": k_nc, "causal": k_c},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic, "kernel": "non-causal d=128 bf16",
+                     "algorithmic_flops_per_launch": plan_nc["algo_flops"],
+                     "algorithmic_bytes_per_launch": plan_nc["algo_bytes"],
+                     "hbm_gbs_compulsory": plan_nc["algo_bytes"] / (k_nc["avg_ms"] * 1e-3) / 1e9},
+        "peak_mem_bytes": peak_mem,
+        "wall_s_timed": wall,
+        "kernel_source_sha256_16": kernel_hash(),
+        "device": torch.cuda.get_device_name(dev),
+    }
+    return out, (q, k, v)
+
+
+def sweep(args):
+    """Medians of 50 (after a separate warmup) for each configuration, with peak memory."""
+    import torch
+    import tiled_attention_forward_fwd_amd as fa
+    dev = torch.device("cuda:0")
+    rows = []
+    configs = [
+        dict(B=1, H=1, N=128, d=64, dtype="fp16", seed=1, flags=(0, 1)),
+        dict(B=2, H=4, N=1000, d=64, dtype="bf16", seed=2, flags=(0, 1)),
+        dict(B=2, H=4, N=1000, d=64, dtype="fp16", seed=2, flags=(0, 1)),
+        dict(B=4, H=16, N=512, d=64, dtype="fp16", seed=3, flags=(0, 1)),
+        dict(B=4, H=16, N=2048, d=64, dtype="fp16", seed=4, flags=(0, 1)),
+        dict(B=4, H=16, N=8192, d=64, dtype="fp16", seed=5, flags=(0, 1)),
+        dict(B=4, H=16, N=4096, d=64, dtype="bf16", seed=6, flags=(0, 1)),
+        dict(B=4, H=16, N=4096, d=128, dtype="bf16", seed=7, flags=(0, 1)),
+        dict(B=1, H=32, N=16384, d=128, dtype="bf16", seed=8, flags=(1,)),
+        dict(B=1, H=32, N=16384, d=128, dtype="bf16", seed=9, q_scale=4.0, flags=(1,)),
+    ]
+    for cfg in configs:
+        _, _, _, qd, kd, vd = make_inputs(cfg, dev)
+        for causal in cfg["flags"]:
+            fn = lambda: fa.fwd(qd, kd, vd, causal=bool(causal))  # noqa: E731
+            warm(fn, 20, 0.5)
+            torch.cuda.reset_peak_memory_stats(dev)
+            ts = timed_launches(fn, 50, torch.cuda.current_stream(dev))
+            plan = fa.fa_plan(cfg["B"], cfg["H"], cfg["N"], cfg["d"], causal,
+                              fa.FA_DTYPE_BF16 if cfg["dtype"] == "bf16" else fa.FA_DTYPE_F16)
+            med = statistics.median(ts)
+            rows.append({"B": cfg["B"], "H": cfg["H"], "N": cfg["N"], "d": cfg["d"],
+                         "dtype": cfg["dtype"], "q_scale": cfg.get("q_scale", 1.0),
+                         "causal": bool(causal), "median_ms": med, "min_ms": min(ts),
+                         "max_ms": max(ts),
+                         "tflops": plan["algo_flops"] / (med * 1e-3) / 1e12,
+                         "frac_peak": plan["algo_flops"] / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         "hbm_gbs_compulsory": plan["algo_bytes"] / (med * 1e-3) / 1e9,
+                         "peak_mem_bytes": torch.cuda.max_memory_allocated(dev)})
+            print(json.dumps({"sweep_row": rows[-1]}), flush=True)
+        del qd, kd, vd
+        torch.cuda.empty_cache()
+    return rows
+
+
+def profile_kernels(args):
+    """A few launches of each headline kernel (for rocprofv3 counter passes)."""
+    import torch
+    import tiled_attention_forward_fwd_amd as fa
+    dev = torch.device("cuda:0")
+    _, _, _, qd, kd, vd = make_inputs(HEADLINE, dev)
+    for causal in (False, True):
+        for _ in range(args.steps):
+            fa.fwd(qd, kd, vd, causal=causal)
+    torch.cuda.synchronize()
+    print(json.dumps({"profiled": "fa_fwd bf16 d=128 N=4096 B=4 H=16", "launches_each": args.steps}))
+
+
+def copy_calibration(args):
+    """A plain copy of a known size, to scale the HBM byte counters."""
+    import torch
+    dev = torch.device("cuda:0")
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).normal_()
+    dst = torch.empty_like(src)
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes,
+                      "launches": args.steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-stride", type=int, default=2,
+                    help="oracle baseline evaluates every Nth query row")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--profile-kernels", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this attention forward is built and measured on a "
+              "single MI355X (heads shard across GPUs with no exchange, so N>1 adds nothing to "
+              "measure here). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import tiled_attention_forward_fwd_amd as fa
+    fa.load_library()  # fails loudly if the HIP library is missing
+
+    if args.profile_kernels:
+        return profile_kernels(args)
+    if args.copy_calibration:
+        return copy_calibration(args)
+
+    out, (q, k, v) = headline(args)
+    if args.sweep:
+        out["sweep"] = sweep(args)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(HEADLINE, q, k, v, args.cpu_stride)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,126 @@
+/*
+ * fa.h -- C ABI of libfa: fused attention forward (FlashAttention-2 form)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation, from "How to optimise a Triton FlashAttention-2 kernel step
+ * by step with a profiler" (sections "Where the last article left off" and
+ * Round 4) and "Programming an attention kernel in Triton" (Kernel 4):
+ *
+ *   O   = softmax(scale * Q K^T [+ causal mask]) V
+ *   lse = per-row logsumexp of scale * Q K^T over the visible keys (natural log)
+ *
+ * One workgroup owns a tile of query rows, streams K and V tiles through LDS
+ * and keeps the running max, running sum and unnormalised output in fp32
+ * registers (online softmax); O and lse are written once.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are dense, row-major [B, H, N, d] (q, k, v, o) and [B, H, N]
+ *     (lse); the same N for queries and keys. No strides are taken.
+ *   - Device pointers are HIP device memory owned by the caller; libfa
+ *     allocates nothing, frees nothing and keeps no pointer after a call.
+ *   - A causal query row i attends to keys j <= i.
+ *   - Functions return an fa_status; nothing is thrown across the ABI.
+ *     Argument errors are reported before any HIP call is made.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1, /* NULL/misaligned/overlapping pointer, bad size, dtype or scale */
+    FA_ERR_UNSUPPORTED = 2, /* well-formed but not built: head dim other than 64 or 128 */
+    FA_ERR_HIP = 3          /* the HIP runtime reported an error (see fa_status_string) */
+} fa_status;
+
+typedef enum {
+    FA_DTYPE_F16 = 0,  /* IEEE binary16 inputs and output */
+    FA_DTYPE_BF16 = 1  /* bfloat16 inputs and output */
+} fa_dtype;
+
+/*
+ * fa_fwd -- attention forward pass.
+ *
+ *   q, k, v : device, [B, H, N, d] contiguous, element type `dtype`,
+ *             16-byte aligned. Read only.
+ *   o       : device, [B, H, N, d] contiguous, element type `dtype`,
+ *             16-byte aligned, must not overlap q, k, v or lse. Every element
+ *             is overwritten with O rounded to nearest-even.
+ *   lse     : device, [B, H, N] fp32, 4-byte aligned, must not overlap the
+ *             others. Every element is overwritten with the row's
+ *             logsumexp in natural-log units (kept for a backward pass, as
+ *             in "How to optimise a Triton FlashAttention-2 kernel step by
+ *             step with a profiler", Round 4, "exp2").
+ *   B, H, N : >= 1.  d : 64 or 128 (other values: FA_ERR_UNSUPPORTED).
+ *   causal  : 0 or 1.
+ *   scale   : finite and > 0; multiplies Q K^T before the softmax
+ *             (1/sqrt(d) is the usual choice, the caller computes it).
+ *   dtype   : an fa_dtype.
+ *   stream  : hipStream_t to launch on (NULL: the default stream).
+ *
+ * The call is asynchronous: it enqueues one kernel on `stream` and returns.
+ * Softmax and accumulation are fp32; P is rounded to `dtype` before the
+ * P.V product. Results are deterministic (no atomics, no split over keys).
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+           int N, int d, int causal, float scale, int dtype, void *stream);
+
+/*
+ * fa_status_string -- human-readable text for a status code. For FA_ERR_HIP
+ * and FA_ERR_INVALID_ARG it names the HIP error or the failed check of the
+ * last failing call on the calling thread. The returned pointer stays valid
+ * until the next libfa call on the same thread.
+ */
+const char *fa_status_string(int status);
+
+/*
+ * fa_tile_counts -- (query tile, key tile) pairs of one head, for a tiling of
+ * block_m query rows by block_n keys (host only, no HIP call). Causal
+ * attention visits, for the query tile starting at q0, the key tiles that
+ * need no mask (those ending at or before the block_n-aligned start of q0)
+ * and then the tiles up to key min(q0 + block_m, N) - 1, which get the mask;
+ * key tiles above the diagonal are never visited. Non-causal attention
+ * masks only a ragged last key tile. This is the split described in
+ * "How to optimise a Triton FlashAttention-2 kernel step by step with a
+ * profiler", Round 4, "Causal tile-skipping".
+ *
+ *   counts[0] = all pairs, ceil(N/block_m) * ceil(N/block_n)
+ *   counts[1] = visited pairs
+ *   counts[2] = visited pairs that need no mask
+ *   counts[3] = visited pairs that get the mask
+ * Returns FA_ERR_INVALID_ARG for N < 1, non-positive tile sizes or NULL.
+ */
+int fa_tile_counts(int64_t N, int block_m, int block_n, int causal, int64_t counts[4]);
+
+/* Launch plan of fa_fwd for a problem (host only, no HIP call). */
+typedef struct {
+    int block_m;            /* query rows per workgroup */
+    int block_n;            /* keys per K/V tile in LDS */
+    int threads;            /* threads per workgroup (wave64) */
+    int lds_bytes;          /* LDS per workgroup */
+    int64_t workgroups;     /* grid size */
+    int64_t pairs_visited;  /* visited (query tile, key tile) pairs, all heads */
+    double mfma_flops;      /* FLOPs the matrix cores execute: 4*d per (row, key)
+                               of every visited tile pair, masked ones included */
+    double algo_flops;      /* 4*B*H*N*N*d, halved for causal (the pages' convention) */
+    double algo_bytes;      /* compulsory HBM bytes: q, k, v read and o written
+                               once (8*B*H*N*d for 2-byte types) plus lse */
+} fa_plan_t;
+
+/*
+ * fa_plan -- fill `plan` for the given problem; the same argument rules as
+ * fa_fwd apart from the pointers. Returns FA_OK, FA_ERR_INVALID_ARG or
+ * FA_ERR_UNSUPPORTED.
+ */
+int fa_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t *plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

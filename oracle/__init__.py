@@ -51,11 +51,15 @@ def load(path=None):
     return _lib
 
 
+MAX_THREADS = 16  # the CPU share of one GPU on the test machines
+
+
 def default_threads():
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    return max(1, min(MAX_THREADS, n))
 
 
 def _as_f32(x):

@@ -1,0 +1,148 @@
+"""CPU checks of the C ABI: the library loads, exports what include/fa.h
+declares, rejects bad arguments before touching the device, and its host
+logic (tile ranges, FLOP counts) reproduces the figures the pages print."""
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import tiled_attention_forward_fwd_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = json.load(open(os.path.join(ROOT, "tests", "golden", "page_counts.json")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        from tiled_attention_forward_fwd_amd import build
+        build.build()
+    return fa.load_library()
+
+
+def declared_functions():
+    names = []
+    for hdr in os.listdir(os.path.join(ROOT, "include")):
+        text = open(os.path.join(ROOT, "include", hdr)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_binding_names():
+    assert sorted(fa.EXPORTED) == declared_functions()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libfa.so does not export {name}"
+
+
+# 16-byte aligned fake addresses: every call below fails validation first,
+# so nothing is ever dereferenced or launched.
+P = [0x10000, 0x20000, 0x30000, 0x40000, 0x50000]
+
+
+def call(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, N=16, d=64, causal=0,
+             scale=0.125, dtype=fa.FA_DTYPE_BF16, stream=None)
+    a.update(kw)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                     a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(k=P[1] + 8), fa.FA_ERR_INVALID_ARG),      # misaligned
+    (dict(lse=P[4] + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),              # empty sequence
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(o=P[0]), fa.FA_ERR_INVALID_ARG),           # o aliases q
+    (dict(o=P[2] + 16), fa.FA_ERR_INVALID_ARG),      # o overlaps v
+    (dict(lse=P[3] + 64), fa.FA_ERR_INVALID_ARG),    # lse inside o
+    (dict(B=65536, H=65536), fa.FA_ERR_INVALID_ARG),  # grid too large
+])
+def test_fa_fwd_rejects_before_any_hip_call(lib, kw, status):
+    assert call(**kw) == status
+    assert fa.fa_status_string(status)
+
+
+def test_status_strings(lib):
+    assert fa.fa_status_string(fa.FA_OK) == "FA_OK"
+    assert "unknown" in fa.fa_status_string(99)
+
+
+def test_tile_counts_match_the_causal_skip_figures(lib):
+    g = GOLDEN["causal_tile_pairs_BM64_BN32_N4096"]
+    assert fa.fa_tile_counts(4096, 64, 32, 1) == (g["all"], g["visited"], g["unmasked"],
+                                                  g["diagonal_masked"])
+
+
+def test_executed_ops_with_pages_tiling(lib):
+    g = GOLDEN["causal_executed_ops_BM64_BN32_B4_H8_N4096_D64"]
+    _, visited, _, _ = fa.fa_tile_counts(4096, 64, 32, 1)
+    ops = 4 * 64 * 64 * 32 * visited * 4 * 8
+    assert abs(ops - g["value"]) <= g["printed_digits"]
+
+
+@pytest.mark.parametrize("N,bm,bn", [(1000, 128, 64), (1000, 64, 32), (1, 128, 64), (129, 128, 128),
+                                     (4096, 128, 64), (16384, 128, 64), (777, 64, 128)])
+def test_tile_counts_cover_every_visible_key_once(lib, N, bm, bn):
+    total, visited, unmasked, masked = fa.fa_tile_counts(N, bm, bn, 0)
+    n_qt, n_kt = -(-N // bm), -(-N // bn)
+    assert total == n_qt * n_kt and visited == total
+    assert masked == (n_qt if N % bn else 0)
+    # causal: brute-force the pairs that hold at least one visible (q, k <= q) entry
+    need = 0
+    for i in range(n_qt):
+        last_q = min(N, (i + 1) * bm) - 1
+        need += last_q // bn + 1
+    total, visited, unmasked, masked = fa.fa_tile_counts(N, bm, bn, 1)
+    assert visited == need
+    # an unmasked pair must be fully visible: inside [0, N) and its last key at
+    # or below the tile's first query; the rest of the visited pairs get the mask
+    fully_visible = sum(1 for i in range(n_qt) for j in range(n_kt)
+                        if (j + 1) * bn <= N and (j + 1) * bn - 1 <= i * bm)
+    assert unmasked <= fully_visible
+    assert unmasked + masked == visited
+    assert masked <= n_qt * (-(-bm // bn) + 1)
+
+
+def test_plan_flops_match_printed_counts(lib):
+    nc = fa.fa_plan(4, 8, 4096, 64, 0, fa.FA_DTYPE_BF16)
+    c = fa.fa_plan(4, 8, 4096, 64, 1, fa.FA_DTYPE_BF16)
+    g = GOLDEN["flops_noncausal_B4_H8_N4096_D64"]
+    assert abs(nc["algo_flops"] - g["value"]) <= g["printed_digits"]
+    g = GOLDEN["flops_causal_needed_B4_H8_N4096_D64"]
+    assert abs(c["algo_flops"] - g["value"]) <= g["printed_digits"]
+    # non-causal with tile-divisible N: the matrix cores execute exactly the algorithm's FLOPs
+    assert nc["mfma_flops"] == nc["algo_flops"]
+    assert c["mfma_flops"] > c["algo_flops"]
+
+
+def test_plan_flop_convention_matches_t4_table(lib):
+    g = GOLDEN["t4_sequence_sweep"]
+    for N, impl, ms, tflops in g["rows"]:
+        flops = fa.fa_plan(1, 16, N, 64, 0, fa.FA_DTYPE_F16)["algo_flops"]  # B*H*d = 1024
+        assert abs(flops / (ms * 1e-3) / 1e12 - tflops) <= 0.006 + 0.005 * tflops, (N, impl)
+
+
+def test_plan_rejects_like_fa_fwd(lib):
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_plan(1, 1, 16, 80, 0, fa.FA_DTYPE_BF16)
+    assert e.value.status == fa.FA_ERR_UNSUPPORTED
+    with pytest.raises(fa.FaError):
+        fa.fa_plan(1, 1, 0, 64, 0, fa.FA_DTYPE_BF16)

@@ -1,0 +1,158 @@
+"""Python binding of libfa, the gfx950 attention-forward library.
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels of ``libfa.so``. PyTorch provides device memory and the stream.
+There is no fallback: if the library is missing or fails to load, the
+functions here raise.
+
+    o, lse = fwd(q, k, v, causal=False, scale=None)
+
+The C entry points are exposed under their own names (``fa_fwd``,
+``fa_status_string``, ``fa_tile_counts``, ``fa_plan``) for callers that
+manage their own buffers.
+"""
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1
+
+# Entry points declared in include/fa.h.
+EXPORTED = ("fa_fwd", "fa_status_string", "fa_tile_counts", "fa_plan")
+
+
+class FaPlan(ctypes.Structure):
+    _fields_ = [("block_m", ctypes.c_int), ("block_n", ctypes.c_int), ("threads", ctypes.c_int),
+                ("lds_bytes", ctypes.c_int), ("workgroups", ctypes.c_int64),
+                ("pairs_visited", ctypes.c_int64), ("mfma_flops", ctypes.c_double),
+                ("algo_flops", ctypes.c_double), ("algo_bytes", ctypes.c_double)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"libfa status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libfa.so (built by ``tiled_attention_forward_fwd_amd.build``)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libfa.so not found at {path}; build it with "
+                          "`python -m tiled_attention_forward_fwd_amd.build`")
+    import torch  # noqa: F401  (load torch's HIP runtime first so both share it)
+    lib = ctypes.CDLL(path)
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_status_string.argtypes = [ctypes.c_int]
+    lib.fa_tile_counts.restype = ctypes.c_int
+    lib.fa_tile_counts.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.POINTER(ctypes.c_int64)]
+    lib.fa_plan.restype = ctypes.c_int
+    lib.fa_plan.argtypes = [ctypes.c_int] * 6 + [ctypes.POINTER(FaPlan)]
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def fa_status_string(status):
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def _check(rc):
+    if rc != FA_OK:
+        raise FaError(rc, fa_status_string(rc))
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, stream):
+    """Direct call of the C entry point with raw pointers (ints); returns the status."""
+    return load_library().fa_fwd(q, k, v, o, lse, int(B), int(H), int(N), int(d), int(causal),
+                                 float(scale), int(dtype), stream)
+
+
+def fa_tile_counts(N, block_m, block_n, causal):
+    """(all pairs, visited, visited without mask, visited with mask) for one head."""
+    out = (ctypes.c_int64 * 4)()
+    _check(load_library().fa_tile_counts(int(N), int(block_m), int(block_n), int(causal), out))
+    return tuple(out)
+
+
+def fa_plan(B, H, N, d, causal, dtype):
+    plan = FaPlan()
+    _check(load_library().fa_plan(int(B), int(H), int(N), int(d), int(causal), int(dtype),
+                                  ctypes.byref(plan)))
+    return plan.as_dict()
+
+
+def dtype_code(torch_dtype):
+    import torch
+    if torch_dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if torch_dtype == torch.float16:
+        return FA_DTYPE_F16
+    raise TypeError(f"unsupported dtype {torch_dtype}; libfa takes float16 or bfloat16")
+
+
+def default_scale(d):
+    """1/sqrt(d) rounded to fp32, the value passed to the kernel."""
+    import numpy as np
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
+    """Attention forward on the GPU: returns ``(o, lse)``.
+
+    q, k, v : CUDA (HIP) tensors ``[B, H, N, d]``, contiguous, float16 or
+              bfloat16, all the same shape and dtype.
+    scale   : defaults to 1/sqrt(d) in fp32.
+    out/lse : optional preallocated outputs (``[B, H, N, d]`` dtype and
+              ``[B, H, N]`` float32).
+    The kernel is enqueued on ``stream`` (default: torch's current stream).
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, d]")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must have the same dtype")
+    B, H, N, d = q.shape
+    code = dtype_code(q.dtype)
+    if scale is None:
+        scale = default_scale(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, H, N, d, causal, scale, code, handle)
+    _check(rc)
+    return out, lse

@@ -1,0 +1,137 @@
+// fa_api.hip -- the C ABI of libfa (declared in include/fa.h): argument
+// checks, launch plan, dispatch to the gfx950 kernels and error strings.
+// Every argument check happens before the first HIP call, so misuse is
+// reported without touching the device.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "fa.h"
+#include "fa_launch.h"
+#include "fa_tiles.h"
+
+namespace {
+
+thread_local char g_msg[256];
+
+int fail(int status, const char* what)
+{
+    snprintf(g_msg, sizeof g_msg, "%s", what);
+    return status;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Shape/dtype/scale checks shared by fa_fwd and fa_plan.
+int check_problem(int B, int H, int N, int d, int causal, int dtype)
+{
+    if (B < 1 || H < 1 || N < 1) return fail(FA_ERR_INVALID_ARG, "B, H and N must be >= 1");
+    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+        return fail(FA_ERR_INVALID_ARG, "dtype must be FA_DTYPE_F16 or FA_DTYPE_BF16");
+    if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+    const int64_t bh = (int64_t)B * H;
+    const int64_t n_qt = ((int64_t)N + fa::block_m() - 1) / fa::block_m();
+    if (bh > INT32_MAX || bh * n_qt > (int64_t)UINT32_MAX)
+        return fail(FA_ERR_INVALID_ARG, "B*H*ceil(N/128) exceeds the grid limit");
+    const int64_t elems = bh * (int64_t)N * d;
+    if (elems > INT64_MAX / 4) return fail(FA_ERR_INVALID_ARG, "B*H*N*d too large");
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status)
+{
+    switch (status) {
+    case FA_OK:
+        return "FA_OK";
+    case FA_ERR_INVALID_ARG:
+    case FA_ERR_UNSUPPORTED:
+    case FA_ERR_HIP:
+        return g_msg[0] ? g_msg : (status == FA_ERR_HIP ? "HIP error" : "invalid argument");
+    default:
+        return "unknown fa_status";
+    }
+}
+
+int fa_tile_counts(int64_t N, int block_m, int block_n, int causal, int64_t counts[4])
+{
+    if (!counts || N < 1 || block_m < 1 || block_n < 1)
+        return fail(FA_ERR_INVALID_ARG, "fa_tile_counts: N, block sizes must be >= 1, counts non-NULL");
+    const int64_t n_qt = (N + block_m - 1) / block_m, n_kt = (N + block_n - 1) / block_n;
+    int64_t visited = 0, unmasked = 0;
+    for (int64_t i = 0; i < n_qt; ++i) {
+        const fa::TileSpan s = fa::tile_span(i * block_m, block_m, block_n, N, causal != 0);
+        visited += s.total;
+        unmasked += s.unmasked;
+    }
+    counts[0] = n_qt * n_kt;
+    counts[1] = visited;
+    counts[2] = unmasked;
+    counts[3] = visited - unmasked;
+    return FA_OK;
+}
+
+int fa_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t* plan)
+{
+    if (!plan) return fail(FA_ERR_INVALID_ARG, "plan is NULL");
+    const int rc = check_problem(B, H, N, d, causal, dtype);
+    if (rc != FA_OK) return rc;
+    const int bm = fa::block_m(), bn = fa::block_n(d);
+    int64_t counts[4];
+    fa_tile_counts(N, bm, bn, causal, counts);
+    const int64_t bh = (int64_t)B * H;
+    plan->block_m = bm;
+    plan->block_n = bn;
+    plan->threads = fa::threads_per_block();
+    plan->lds_bytes = fa::lds_bytes(d);
+    plan->workgroups = bh * ((N + bm - 1) / bm);
+    plan->pairs_visited = bh * counts[1];
+    plan->mfma_flops = 4.0 * d * (double)bm * bn * (double)plan->pairs_visited;
+    const double nn = (double)N * (double)N;
+    plan->algo_flops = 4.0 * (double)bh * nn * d * (causal ? 0.5 : 1.0);
+    plan->algo_bytes = 8.0 * (double)bh * N * d + 4.0 * (double)bh * N;
+    return FA_OK;
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, int causal, float scale, int dtype, void* stream)
+{
+    g_msg[0] = 0;
+    if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+        return fail(FA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+    if (!aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    const int rc = check_problem(B, H, N, d, causal, dtype);
+    if (rc != FA_OK) return rc;
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    const size_t tb = (size_t)B * H * N * d * 2, lb = (size_t)B * H * N * 4;
+    if (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb))
+        return fail(FA_ERR_INVALID_ARG, "o overlaps q, k or v");
+    if (overlap(lse, lb, q, tb) || overlap(lse, lb, k, tb) || overlap(lse, lb, v, tb) ||
+        overlap(lse, lb, o, tb))
+        return fail(FA_ERR_INVALID_ARG, "lse overlaps q, k, v or o");
+    const hipError_t e = fa::launch_fwd(q, k, v, o, lse, B, H, N, d, causal != 0, scale,
+                                        dtype == FA_DTYPE_BF16, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        snprintf(g_msg, sizeof g_msg, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+        return FA_ERR_HIP;
+    }
+    return FA_OK;
+}
+
+}  // extern "C"
