@@ -138,20 +138,27 @@ struct TileRegs {
     u32x4 v[Cfg<D>::V_ITEMS][4];
 };
 
-// Global -> registers for key tile starting at key k0 (rows >= N read as 0).
-template <typename T, int D>
+// Global -> registers for the key tile starting at key k0. CHECK: the tile
+// reaches past N, so rows >= N are replaced by zeros (only a ragged last tile).
+template <typename T, int D, bool CHECK>
 __device__ __forceinline__ void load_tile(TileRegs<T, D>& r, const T* __restrict__ kh,
                                           const T* __restrict__ vh, int k0, int N, int tid)
 {
     typedef Cfg<D> C;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < C::K_CHUNKS; ++i) {
         const int id = tid + i * kThreads;
         const int row = id / C::CPR, c8 = id % C::CPR;
         const int key = k0 + row;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (key < N) x = *(const u32x4*)(kh + (int64_t)key * D + c8 * 8);
-        r.k[i] = x;
+        if (CHECK) {
+            // clamped address, then select: no divergent branch around the load
+            const int kc = key < N ? key : N - 1;
+            const u32x4 x = *(const u32x4*)(kh + (int64_t)kc * D + c8 * 8);
+            r.k[i] = key < N ? x : zero;
+        } else {
+            r.k[i] = *(const u32x4*)(kh + (int64_t)key * D + c8 * 8);
+        }
     }
 #pragma unroll
     for (int i = 0; i < C::V_ITEMS; ++i) {
@@ -160,11 +167,26 @@ __device__ __forceinline__ void load_tile(TileRegs<T, D>& r, const T* __restrict
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int key = k0 + 4 * g4 + t;
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (key < N) x = *(const u32x4*)(vh + (int64_t)key * D + c8 * 8);
-            r.v[i][t] = x;
+            if (CHECK) {
+                const int kc = key < N ? key : N - 1;
+                const u32x4 x = *(const u32x4*)(vh + (int64_t)kc * D + c8 * 8);
+                r.v[i][t] = key < N ? x : zero;
+            } else {
+                r.v[i][t] = *(const u32x4*)(vh + (int64_t)key * D + c8 * 8);
+            }
         }
     }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void load_tile_any(TileRegs<T, D>& r, const T* __restrict__ kh,
+                                              const T* __restrict__ vh, int tile, int n_full,
+                                              int N, int tid)
+{
+    if (tile < n_full)
+        load_tile<T, D, false>(r, kh, vh, tile * Cfg<D>::BN, N, tid);
+    else
+        load_tile<T, D, true>(r, kh, vh, tile * Cfg<D>::BN, N, tid);
 }
 
 // Registers -> LDS stage: K row-major (padded), V transposed to V^T with the
@@ -209,7 +231,15 @@ __device__ __forceinline__ __bf16 to_elem<__bf16>(float x) { return (__bf16)x; }
 template <>
 __device__ __forceinline__ _Float16 to_elem<_Float16>(float x) { return (_Float16)x; }
 
-// One key tile: S^T = K Q^T, mask, online-softmax update, O^T += V^T P^T.
+// Largest growth of the row max, in log2 units, that the running state may
+// absorb without rescaling O and l: P then reaches at most 2^8, far inside the
+// fp16/bf16 range, and the final O / l is unchanged (both carry the same
+// factor). Rescaling only when some row of the wave passes this keeps the
+// O * alpha multiplies off the common path.
+constexpr float kRescaleSlack = 8.0f;
+
+// One key tile: S^T = K Q^T, mask (diagonal / ragged tiles only), online
+// softmax update, O^T += V^T P^T.
 template <typename T, int D, bool CAUSAL, bool MASKED>
 __device__ __forceinline__ void attend_tile(const uint16_t* __restrict__ ks,
                                             const uint16_t* __restrict__ vts,
@@ -249,25 +279,32 @@ __device__ __forceinline__ void attend_tile(const uint16_t* __restrict__ ks,
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = swap_halves_max(mx);
-    const float m_new = fmaxf(m_run, mx * c_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    mx = swap_halves_max(mx) * c_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack)) {
+        // wave-uniform: some row's max grew past the slack; move every row of
+        // the wave to its true running max
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
+    }
 
+    // P = 2^(s * c - m); l is summed from fp32 P, then P is rounded to the
+    // input type for the P.V product (Round 4, "The P cast")
     vec8 p[C::KT];
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c_log2, -m_new));
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c_log2, -m_run));
             rs += e;
             p[kb * 2 + (r >> 3)][r & 7] = to_elem<T>(e);
         }
     }
-    l_run = l_run * alpha + rs;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
+    l_run += rs;
 
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
@@ -321,6 +358,7 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 
     const TileSpan span = tile_span(q0, kBlockM, C::BN, N, CAUSAL);
     const int n_unmasked = (int)span.unmasked, n_tiles = (int)span.total;
+    const int n_full = N / C::BN;  // key tiles wholly inside [0, N)
 
     f32x16 oacc[C::DB];
 #pragma unroll
@@ -328,21 +366,31 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     float m_run = -1e30f, l_run = 0.f;
 
     TileRegs<T, D> regs;
-    load_tile<T, D>(regs, kh, vh, 0, N, tid);
+    load_tile_any<T, D>(regs, kh, vh, 0, n_full, N, tid);
     store_tile<T, D>(regs, smem, smem + C::K_ELEMS, tid);
     __syncthreads();
 
-    for (int j = 0; j < n_tiles; ++j) {
+    // Tiles [0, n_unmasked) need no mask, [n_unmasked, n_tiles) get it. The
+    // next tile's global loads are in flight while the current one is used.
+    int j = 0;
+    for (; j < n_unmasked; ++j) {
         const bool more = j + 1 < n_tiles;
-        if (more) load_tile<T, D>(regs, kh, vh, (j + 1) * C::BN, N, tid);
+        if (more) load_tile_any<T, D>(regs, kh, vh, j + 1, n_full, N, tid);
         const uint16_t* ks = smem + (j & 1) * C::STAGE;
-        const uint16_t* vts = ks + C::K_ELEMS;
-        if (j < n_unmasked)
-            attend_tile<T, D, CAUSAL, false>(ks, vts, qf, oacc, m_run, l_run, c_log2, j * C::BN,
-                                             qrow, N, l32, hh);
-        else
-            attend_tile<T, D, CAUSAL, true>(ks, vts, qf, oacc, m_run, l_run, c_log2, j * C::BN,
-                                            qrow, N, l32, hh);
+        attend_tile<T, D, CAUSAL, false>(ks, ks + C::K_ELEMS, qf, oacc, m_run, l_run, c_log2,
+                                         j * C::BN, qrow, N, l32, hh);
+        if (more) {
+            uint16_t* nks = smem + ((j + 1) & 1) * C::STAGE;
+            store_tile<T, D>(regs, nks, nks + C::K_ELEMS, tid);
+        }
+        __syncthreads();
+    }
+    for (; j < n_tiles; ++j) {
+        const bool more = j + 1 < n_tiles;
+        if (more) load_tile_any<T, D>(regs, kh, vh, j + 1, n_full, N, tid);
+        const uint16_t* ks = smem + (j & 1) * C::STAGE;
+        attend_tile<T, D, CAUSAL, true>(ks, ks + C::K_ELEMS, qf, oacc, m_run, l_run, c_log2,
+                                        j * C::BN, qrow, N, l32, hh);
         if (more) {
             uint16_t* nks = smem + ((j + 1) & 1) * C::STAGE;
             store_tile<T, D>(regs, nks, nks + C::K_ELEMS, tid);
