@@ -23,11 +23,19 @@
 //     is written to LDS with its keys permuted the same way, so every operand
 //     is one 16-byte LDS read and P never goes through LDS.
 //   * Q is loaded once into registers in B-operand layout.
-//   * K tiles are copied to LDS with 128-bit loads and stores; V tiles are
-//     loaded with 128-bit loads, transposed 4 keys x 8 dims in registers and
-//     stored as V^T. Rows are padded by 16 bytes so the 32 lanes of an operand
-//     read hit distinct banks. Two LDS stages: the next tile's global loads are
-//     issued before the current tile's MFMAs, one barrier per tile.
+//   * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4,
+//     16 bytes per lane, no staging registers), row-major and dense. The
+//     16-byte chunks of each row are XOR-swizzled by a function of the row so
+//     that the operand reads below hit distinct banks.
+//   * K is read as the A operand of S^T = K Q^T with one ds_read_b128 per
+//     MFMA. V is read as the A operand of O^T = V^T P^T with two
+//     ds_read_b64_tr_b16: within each 16-lane group that instruction hands
+//     lane j element (j mod 4) of the 8-byte chunk addressed by lane
+//     4e + j/4, so 16 lanes addressing 4 keys x 4 dim-quads receive 4 keys of
+//     one dim each: a transposed read of the row-major tile.
+//   * Two LDS stages: the next tile's loads are in flight while the current
+//     tile is used; one barrier per tile. A ragged last tile clamps its row
+//     addresses to N - 1; those keys are masked, so their P is exactly 0.
 //   * exp2 with the softmax scale and log2(e) folded into one constant
 //     (Round 4, "exp2"); the running max is kept in log2 units; the row max is
 //     taken on the scaled scores so the maximal term is 2^0 = 1.
@@ -79,29 +87,40 @@ struct Mma<_Float16> {
 };
 
 constexpr int kThreads = 256;  // 4 waves of 64
+constexpr int kWaves = 4;
 constexpr int kBlockM = 128;   // query rows per workgroup (32 per wave)
 constexpr int kXcds = 8;       // XCDs of an MI355X
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct Cfg {
     static_assert(D == 64 || D == 128, "head dim");
     static constexpr int BN = 8192 / D;           // keys per tile: 64 at d=128, 128 at d=64
-    static constexpr int KSTRIDE = D + 8;         // LDS row of K, elements (16 B pad)
-    static constexpr int VSTRIDE = BN + 8;        // LDS row of V^T, elements (16 B pad)
-    static constexpr int K_ELEMS = BN * KSTRIDE;
-    static constexpr int V_ELEMS = D * VSTRIDE;
-    static constexpr int STAGE = K_ELEMS + V_ELEMS;
+    static constexpr int CPR = D / 8;             // 16-byte chunks per row
+    static constexpr int TILE = BN * D;           // elements of one K or V tile (dense)
+    static constexpr int STAGE = 2 * TILE;        // K tile, then V tile
     static constexpr int LDS_BYTES = 2 * STAGE * 2;
     static constexpr int KB = BN / 32;            // 32-key blocks per tile
     static constexpr int DS = D / 16;             // MFMA k-steps of S^T = K Q^T
     static constexpr int DB = D / 32;             // 32-row blocks of O^T
     static constexpr int KT = BN / 16;            // MFMA k-steps of O^T += V^T P^T
-    static constexpr int CPR = D / 8;             // 16-byte chunks per row
-    static constexpr int K_CHUNKS = BN * CPR / kThreads;  // K chunks per thread
-    static constexpr int V_ITEMS = (BN / 4) * CPR / kThreads;  // 4-key x 8-dim V blocks per thread
-    static_assert(K_CHUNKS * kThreads == BN * CPR, "K tile split");
-    static_assert(V_ITEMS * kThreads == (BN / 4) * CPR, "V tile split");
+    static constexpr int LOADS = BN * CPR / kThreads;  // 16-byte loads per thread, each of K and V
+    static_assert(LOADS * kThreads == BN * CPR, "tile split");
+    static_assert(BN * CPR % (64 * kWaves) == 0, "whole wave loads");
 };
+
+// Chunk swizzle: 16-byte chunk c of tile row r is stored at chunk c ^ swz(r).
+// d=128 (16 chunks/row): 16 consecutive rows map one chunk to 16 distinct
+// chunks (K operand reads), and 4 consecutive rows x 2 adjacent chunks map to
+// 8 distinct chunks (V transposed reads). d=64 (8 chunks/row) likewise.
+template <int D>
+__device__ __forceinline__ int swz(int row)
+{
+    if (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
+    return ((row & 3) << 1) | ((row >> 2) & 1);
+}
 
 __device__ __forceinline__ float swap_halves_max(float x)
 {
@@ -124,104 +143,44 @@ __device__ __forceinline__ V8 as_vec8(u32x4 x)
     return __builtin_bit_cast(V8, x);
 }
 
-// Slot of key kappa (0..15) inside a 16-key group of a V^T row. Lane half h,
-// element j of the P^T operand holds key 8*(j/4) + 4*h + (j%4) of the group
-// (the order of the 32x32 accumulator rows), so slot 8*h + j holds that key.
-__device__ __forceinline__ int vt_slot_of_4group(int g)  // g = kappa / 4, kappa multiple of 4
+// 16 bytes per lane from global memory to LDS at lds_base + 16 * lane
+// (lds_base must be wave-uniform). The builtin exists only in the device pass.
+__device__ __forceinline__ void copy16_to_lds(const void* g, uint16_t* lds_base)
 {
-    return 8 * (g & 1) + 4 * (g >> 1);
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr)lds_base, 16, 0, 0);
+#endif
 }
 
+// Issue the HBM -> LDS copies of key tile [k0, k0 + BN) of K and V into one
+// stage. Wave w, load i covers 64 consecutive LDS chunks (wave-uniform base);
+// lane l fetches the global chunk that the swizzle places there. Rows past
+// N - 1 re-read row N - 1 (masked later, so their values never count).
 template <typename T, int D>
-struct TileRegs {
-    u32x4 k[Cfg<D>::K_CHUNKS];
-    u32x4 v[Cfg<D>::V_ITEMS][4];
-};
-
-// Global -> registers for the key tile starting at key k0. CHECK: the tile
-// reaches past N, so rows >= N are replaced by zeros (only a ragged last tile).
-template <typename T, int D, bool CHECK>
-__device__ __forceinline__ void load_tile(TileRegs<T, D>& r, const T* __restrict__ kh,
-                                          const T* __restrict__ vh, int k0, int N, int tid)
-{
-    typedef Cfg<D> C;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < C::K_CHUNKS; ++i) {
-        const int id = tid + i * kThreads;
-        const int row = id / C::CPR, c8 = id % C::CPR;
-        const int key = k0 + row;
-        if (CHECK) {
-            // clamped address, then select: no divergent branch around the load
-            const int kc = key < N ? key : N - 1;
-            const u32x4 x = *(const u32x4*)(kh + (int64_t)kc * D + c8 * 8);
-            r.k[i] = key < N ? x : zero;
-        } else {
-            r.k[i] = *(const u32x4*)(kh + (int64_t)key * D + c8 * 8);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < C::V_ITEMS; ++i) {
-        const int id = tid + i * kThreads;
-        const int g4 = id / C::CPR, c8 = id % C::CPR;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int key = k0 + 4 * g4 + t;
-            if (CHECK) {
-                const int kc = key < N ? key : N - 1;
-                const u32x4 x = *(const u32x4*)(vh + (int64_t)kc * D + c8 * 8);
-                r.v[i][t] = key < N ? x : zero;
-            } else {
-                r.v[i][t] = *(const u32x4*)(vh + (int64_t)key * D + c8 * 8);
-            }
-        }
-    }
-}
-
-template <typename T, int D>
-__device__ __forceinline__ void load_tile_any(TileRegs<T, D>& r, const T* __restrict__ kh,
-                                              const T* __restrict__ vh, int tile, int n_full,
-                                              int N, int tid)
-{
-    if (tile < n_full)
-        load_tile<T, D, false>(r, kh, vh, tile * Cfg<D>::BN, N, tid);
-    else
-        load_tile<T, D, true>(r, kh, vh, tile * Cfg<D>::BN, N, tid);
-}
-
-// Registers -> LDS stage: K row-major (padded), V transposed to V^T with the
-// keys of each 16-key group permuted to the P^T operand order.
-template <typename T, int D>
-__device__ __forceinline__ void store_tile(const TileRegs<T, D>& r, uint16_t* __restrict__ ks,
-                                           uint16_t* __restrict__ vts, int tid)
+__device__ __forceinline__ void issue_tile(uint16_t* stage, const T* __restrict__ kh,
+                                           const T* __restrict__ vh, int k0, int N, int wave,
+                                           int lane)
 {
     typedef Cfg<D> C;
 #pragma unroll
-    for (int i = 0; i < C::K_CHUNKS; ++i) {
-        const int id = tid + i * kThreads;
-        const int row = id / C::CPR, c8 = id % C::CPR;
-        *(u32x4*)(ks + row * C::KSTRIDE + c8 * 8) = r.k[i];
+    for (int i = 0; i < C::LOADS; ++i) {
+        const int chunk0 = (i * kWaves + wave) * 64;
+        const int c = chunk0 + lane;
+        const int row = c / C::CPR, pc = c % C::CPR;
+        int key = k0 + row;
+        key = key < N ? key : N - 1;
+        const int64_t goff = (int64_t)key * D + (pc ^ swz<D>(row)) * 8;
+        copy16_to_lds(kh + goff, stage + chunk0 * 8);
+        copy16_to_lds(vh + goff, stage + C::TILE + chunk0 * 8);
     }
-#pragma unroll
-    for (int i = 0; i < C::V_ITEMS; ++i) {
-        const int id = tid + i * kThreads;
-        const int g4 = id / C::CPR, c8 = id % C::CPR;
-        const int slot = 16 * (g4 >> 2) + vt_slot_of_4group(g4 & 3);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int w = e >> 1;
-            uint32_t a0 = r.v[i][0][w], a1 = r.v[i][1][w], a2 = r.v[i][2][w], a3 = r.v[i][3][w];
-            u32x2 out;
-            if (e & 1) {
-                out[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-                out[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-            } else {
-                out[0] = (a0 & 0xffffu) | (a1 << 16);
-                out[1] = (a2 & 0xffffu) | (a3 << 16);
-            }
-            *(u32x2*)(vts + (c8 * 8 + e) * C::VSTRIDE + slot) = out;
-        }
-    }
+}
+
+// Waits for this thread's outstanding LDS copies and LDS reads, then for the
+// whole workgroup.
+__device__ __forceinline__ void stage_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 }
 
 template <typename T>
@@ -245,7 +204,7 @@ __device__ __forceinline__ void attend_tile(const uint16_t* __restrict__ ks,
                                             const uint16_t* __restrict__ vts,
                                             const typename Mma<T>::vec8 (&qf)[Cfg<D>::DS],
                                             f32x16 (&o)[Cfg<D>::DB], float& m_run, float& l_run,
-                                            float c_log2, int k0, int qrow, int N, int l32, int hh)
+                                            float c_log2, int k0, int qrow, int N, int lane, int l32, int hh)
 {
     typedef Cfg<D> C;
     typedef typename Mma<T>::vec8 vec8;
@@ -254,10 +213,12 @@ __device__ __forceinline__ void attend_tile(const uint16_t* __restrict__ ks,
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
         s[kb] = (f32x16){};
-        const uint16_t* krow = ks + (kb * 32 + l32) * C::KSTRIDE + hh * 8;
+        const int row = kb * 32 + l32;
+        const uint16_t* krow = ks + row * D;
+        const int sw = swz<D>(row);
 #pragma unroll
         for (int ds = 0; ds < C::DS; ++ds) {
-            vec8 a = as_vec8<vec8>(*(const u32x4*)(krow + ds * 16));
+            vec8 a = as_vec8<vec8>(*(const u32x4*)(krow + (((2 * ds + hh) ^ sw) * 8)));
             s[kb] = Mma<T>::run(a, qf[ds], s[kb]);
         }
     }
@@ -306,13 +267,29 @@ __device__ __forceinline__ void attend_tile(const uint16_t* __restrict__ ks,
     }
     l_run += rs;
 
+    // V^T operand, lane l = 16g + i: dim 32*db + (l % 32); elements 0..3 are
+    // keys 16t + 4h + [0,4), elements 4..7 keys 16t + 8 + 4h + [0,4) (h = g/2),
+    // the key order of P^T. Each of the two transposed reads has lane i address
+    // key (base + i/4), dims 4*(i%4) + [0,4) of the group's 16 dims.
+    const int gi = lane & 15, g1 = (lane >> 4) & 1;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
-        const uint16_t* vrow = vts + (db * 32 + l32) * C::VSTRIDE + hh * 8;
+        const int chunk = 4 * db + 2 * g1 + ((gi & 3) >> 1);
+        const int half = (gi & 1) * 4;
 #pragma unroll
         for (int t = 0; t < C::KT; ++t) {
-            vec8 a = as_vec8<vec8>(*(const u32x4*)(vrow + t * 16));
-            o[db] = Mma<T>::run(a, p[t], o[db]);
+            const int key0 = 16 * t + 4 * hh + (gi >> 2);
+            const int key1 = key0 + 8;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(vts + key0 * D + ((chunk ^ swz<D>(key0)) * 8) + half));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(vts + key1 * D + ((chunk ^ swz<D>(key1)) * 8) + half));
+            u32x4 w;
+            w[0] = __builtin_bit_cast(u32x2, lo)[0];
+            w[1] = __builtin_bit_cast(u32x2, lo)[1];
+            w[2] = __builtin_bit_cast(u32x2, hi)[0];
+            w[3] = __builtin_bit_cast(u32x2, hi)[1];
+            o[db] = Mma<T>::run(as_vec8<vec8>(w), p[t], o[db]);
         }
     }
 }
@@ -358,44 +335,33 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 
     const TileSpan span = tile_span(q0, kBlockM, C::BN, N, CAUSAL);
     const int n_unmasked = (int)span.unmasked, n_tiles = (int)span.total;
-    const int n_full = N / C::BN;  // key tiles wholly inside [0, N)
 
     f32x16 oacc[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) oacc[db] = (f32x16){};
     float m_run = -1e30f, l_run = 0.f;
 
-    TileRegs<T, D> regs;
-    load_tile_any<T, D>(regs, kh, vh, 0, n_full, N, tid);
-    store_tile<T, D>(regs, smem, smem + C::K_ELEMS, tid);
-    __syncthreads();
+    issue_tile<T, D>(smem, kh, vh, 0, N, wave, lane);
+    stage_barrier();
 
     // Tiles [0, n_unmasked) need no mask, [n_unmasked, n_tiles) get it. The
-    // next tile's global loads are in flight while the current one is used.
+    // next tile's copies are in flight while the current one is used.
     int j = 0;
     for (; j < n_unmasked; ++j) {
-        const bool more = j + 1 < n_tiles;
-        if (more) load_tile_any<T, D>(regs, kh, vh, j + 1, n_full, N, tid);
+        if (j + 1 < n_tiles)
+            issue_tile<T, D>(smem + ((j + 1) & 1) * C::STAGE, kh, vh, (j + 1) * C::BN, N, wave, lane);
         const uint16_t* ks = smem + (j & 1) * C::STAGE;
-        attend_tile<T, D, CAUSAL, false>(ks, ks + C::K_ELEMS, qf, oacc, m_run, l_run, c_log2,
-                                         j * C::BN, qrow, N, l32, hh);
-        if (more) {
-            uint16_t* nks = smem + ((j + 1) & 1) * C::STAGE;
-            store_tile<T, D>(regs, nks, nks + C::K_ELEMS, tid);
-        }
-        __syncthreads();
+        attend_tile<T, D, CAUSAL, false>(ks, ks + C::TILE, qf, oacc, m_run, l_run, c_log2,
+                                         j * C::BN, qrow, N, lane, l32, hh);
+        stage_barrier();
     }
     for (; j < n_tiles; ++j) {
-        const bool more = j + 1 < n_tiles;
-        if (more) load_tile_any<T, D>(regs, kh, vh, j + 1, n_full, N, tid);
+        if (j + 1 < n_tiles)
+            issue_tile<T, D>(smem + ((j + 1) & 1) * C::STAGE, kh, vh, (j + 1) * C::BN, N, wave, lane);
         const uint16_t* ks = smem + (j & 1) * C::STAGE;
-        attend_tile<T, D, CAUSAL, true>(ks, ks + C::K_ELEMS, qf, oacc, m_run, l_run, c_log2,
-                                        j * C::BN, qrow, N, l32, hh);
-        if (more) {
-            uint16_t* nks = smem + ((j + 1) & 1) * C::STAGE;
-            store_tile<T, D>(regs, nks, nks + C::K_ELEMS, tid);
-        }
-        __syncthreads();
+        attend_tile<T, D, CAUSAL, true>(ks, ks + C::TILE, qf, oacc, m_run, l_run, c_log2,
+                                        j * C::BN, qrow, N, lane, l32, hh);
+        stage_barrier();
     }
 
     // Epilogue: O = O_acc / l in the input type, lse = (m + log2 l) * ln 2.
