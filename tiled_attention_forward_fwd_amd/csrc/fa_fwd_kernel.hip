@@ -23,7 +23,7 @@
 //     is written to LDS with its keys permuted the same way, so every operand
 //     is one 16-byte LDS read and P never goes through LDS.
 //   * Q is loaded once into registers in B-operand layout.
-//   * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4,
+//   * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 ... lds,
 //     16 bytes per lane, no staging registers), row-major and dense. The
 //     16-byte chunks of each row are XOR-swizzled by a function of the row so
 //     that the operand reads below hit distinct banks.
@@ -33,9 +33,12 @@
 //     lane j element (j mod 4) of the 8-byte chunk addressed by lane
 //     4e + j/4, so 16 lanes addressing 4 keys x 4 dim-quads receive 4 keys of
 //     one dim each: a transposed read of the row-major tile.
-//   * Two LDS stages: the next tile's loads are in flight while the current
-//     tile is used; one barrier per tile. A ragged last tile clamps its row
-//     addresses to N - 1; those keys are masked, so their P is exactly 0.
+//   * Software pipeline over key tiles, two K and two V buffers in LDS:
+//     iteration j computes the scores of tile j+1 on the matrix cores while
+//     the vector units run the softmax of tile j, then P_j V_j; the copies of
+//     K_{j+2} and V_{j+1} are in flight meanwhile; one barrier per tile. The
+//     copies go through a buffer descriptor bounded to the head, so the rows
+//     of a ragged last tile past N arrive as zeros (and are masked).
 //   * exp2 with the softmax scale and log2(e) folded into one constant
 //     (Round 4, "exp2"); the running max is kept in log2 units; the row max is
 //     taken on the scaled scores so the maximal term is 2^0 = 1.
@@ -52,6 +55,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "fa_launch.h"
 #include "fa_tiles.h"
@@ -97,11 +102,10 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 template <int D>
 struct Cfg {
     static_assert(D == 64 || D == 128, "head dim");
-    static constexpr int BN = 8192 / D;           // keys per tile: 64 at d=128, 128 at d=64
+    static constexpr int BN = 64;                 // keys per tile
     static constexpr int CPR = D / 8;             // 16-byte chunks per row
     static constexpr int TILE = BN * D;           // elements of one K or V tile (dense)
-    static constexpr int STAGE = 2 * TILE;        // K tile, then V tile
-    static constexpr int LDS_BYTES = 2 * STAGE * 2;
+    static constexpr int LDS_BYTES = 4 * TILE * 2;  // two K and two V tile buffers
     static constexpr int KB = BN / 32;            // 32-key blocks per tile
     static constexpr int DS = D / 16;             // MFMA k-steps of S^T = K Q^T
     static constexpr int DB = D / 32;             // 32-row blocks of O^T
@@ -143,36 +147,51 @@ __device__ __forceinline__ V8 as_vec8(u32x4 x)
     return __builtin_bit_cast(V8, x);
 }
 
-// 16 bytes per lane from global memory to LDS at lds_base + 16 * lane
-// (lds_base must be wave-uniform). The builtin exists only in the device pass.
-__device__ __forceinline__ void copy16_to_lds(const void* g, uint16_t* lds_base)
+// K/V tiles are copied with the buffer form of the LDS DMA: a descriptor
+// covering one head (base, size in bytes), a wave-uniform byte offset and one
+// per-lane byte offset. Bytes at or past the head's size read as zero, so a
+// ragged last tile is zero-filled and no copy can leave its head.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRawBufferWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
+
+__device__ __forceinline__ rsrc_t head_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRawBufferWord3);
+}
+
+// 16 bytes per lane into LDS at lds_base + 16 * lane (lds_base wave-uniform).
+// The builtin exists only in the device pass.
+__device__ __forceinline__ void copy16_to_lds(rsrc_t r, uint16_t* lds_base, uint32_t lane_off,
+                                              uint32_t tile_off)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(g, (lds_ptr)lds_base, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds_base, 16, lane_off, tile_off, 0, 0);
 #endif
 }
 
-// Issue the HBM -> LDS copies of key tile [k0, k0 + BN) of K and V into one
-// stage. Wave w, load i covers 64 consecutive LDS chunks (wave-uniform base);
-// lane l fetches the global chunk that the swizzle places there. Rows past
-// N - 1 re-read row N - 1 (masked later, so their values never count).
-template <typename T, int D>
-__device__ __forceinline__ void issue_tile(uint16_t* stage, const T* __restrict__ kh,
-                                           const T* __restrict__ vh, int k0, int N, int wave,
-                                           int lane)
+// HBM -> LDS copy of rows [k0, k0 + BN) of one K or V head. Wave w, load i
+// fills 64 consecutive LDS chunks; lane l fetches the global chunk that the
+// swizzle places there. Load i is 256/CPR rows below load 0, which leaves the
+// swizzle unchanged, so every load of a lane is one per-lane byte offset plus
+// a wave-uniform k0 * D * 2 + i * 4096.
+template <int D>
+__device__ __forceinline__ uint32_t tile_lane_offset(int wave, int lane)
+{
+    typedef Cfg<D> C;
+    const int c = wave * 64 + lane;
+    const int r0 = c / C::CPR, pc = c % C::CPR;
+    return (uint32_t)(r0 * D * 2 + (pc ^ swz<D>(r0)) * 16);
+}
+
+template <int D>
+__device__ __forceinline__ void issue_tile(uint16_t* buf, rsrc_t src, int k0, int wave,
+                                           uint32_t lane_off)
 {
     typedef Cfg<D> C;
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-        const int chunk0 = (i * kWaves + wave) * 64;
-        const int c = chunk0 + lane;
-        const int row = c / C::CPR, pc = c % C::CPR;
-        int key = k0 + row;
-        key = key < N ? key : N - 1;
-        const int64_t goff = (int64_t)key * D + (pc ^ swz<D>(row)) * 8;
-        copy16_to_lds(kh + goff, stage + chunk0 * 8);
-        copy16_to_lds(vh + goff, stage + C::TILE + chunk0 * 8);
-    }
+    for (int i = 0; i < C::LOADS; ++i)
+        copy16_to_lds(src, buf + (i * kWaves + wave) * 64 * 8, lane_off,
+                      (uint32_t)k0 * (D * 2) + i * 4096);
 }
 
 // Waits for this thread's outstanding LDS copies and LDS reads, then for the
@@ -197,19 +216,15 @@ __device__ __forceinline__ _Float16 to_elem<_Float16>(float x) { return (_Float1
 // O * alpha multiplies off the common path.
 constexpr float kRescaleSlack = 8.0f;
 
-// One key tile: S^T = K Q^T, mask (diagonal / ragged tiles only), online
-// softmax update, O^T += V^T P^T.
-template <typename T, int D, bool CAUSAL, bool MASKED>
-__device__ __forceinline__ void attend_tile(const uint16_t* __restrict__ ks,
-                                            const uint16_t* __restrict__ vts,
-                                            const typename Mma<T>::vec8 (&qf)[Cfg<D>::DS],
-                                            f32x16 (&o)[Cfg<D>::DB], float& m_run, float& l_run,
-                                            float c_log2, int k0, int qrow, int N, int lane, int l32, int hh)
+// S^T = K Q^T for one key tile: s[kb] holds keys 32*kb + (accumulator rows)
+// of this lane's query.
+template <typename T, int D>
+__device__ __forceinline__ void scores(f32x16 (&s)[Cfg<D>::KB], const uint16_t* __restrict__ ks,
+                                       const typename Mma<T>::vec8 (&qf)[Cfg<D>::DS], int l32,
+                                       int hh)
 {
     typedef Cfg<D> C;
     typedef typename Mma<T>::vec8 vec8;
-
-    f32x16 s[C::KB];
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
         s[kb] = (f32x16){};
@@ -222,19 +237,32 @@ __device__ __forceinline__ void attend_tile(const uint16_t* __restrict__ ks,
             s[kb] = Mma<T>::run(a, qf[ds], s[kb]);
         }
     }
+}
 
-    if (MASKED) {
+// Diagonal / ragged tiles: keys past N, and for causal attention keys after
+// the lane's query, get score -inf.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[Cfg<D>::KB], int k0, int qrow, int N, int hh)
+{
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
+    for (int kb = 0; kb < Cfg<D>::KB; ++kb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const bool hide = key >= N || (CAUSAL && key > qrow);
-                if (hide) s[kb][r] = -INFINITY;
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const bool hide = key >= N || (CAUSAL && key > qrow);
+            if (hide) s[kb][r] = -INFINITY;
         }
     }
+}
 
+// Online-softmax update for one tile of scores, then O^T += V^T P^T.
+// Rows whose max grew past the slack trigger a wave-uniform rescale first.
+template <typename T, int D>
+__device__ __forceinline__ void rescale_if_needed(const f32x16 (&s)[Cfg<D>::KB],
+                                                  f32x16 (&o)[Cfg<D>::DB], float& m_run,
+                                                  float& l_run, float c_log2)
+{
+    typedef Cfg<D> C;
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
@@ -242,8 +270,8 @@ __device__ __forceinline__ void attend_tile(const uint16_t* __restrict__ ks,
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = swap_halves_max(mx) * c_log2;
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack)) {
-        // wave-uniform: some row's max grew past the slack; move every row of
-        // the wave to its true running max
+        // some row's max grew past the slack: move every row of the wave to
+        // its true running max
         const float m_new = fmaxf(m_run, mx);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
@@ -251,7 +279,16 @@ __device__ __forceinline__ void attend_tile(const uint16_t* __restrict__ ks,
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
     }
+}
 
+template <typename T, int D>
+__device__ __forceinline__ void softmax_pv(const f32x16 (&s)[Cfg<D>::KB],
+                                           const uint16_t* __restrict__ vts,
+                                           f32x16 (&o)[Cfg<D>::DB], float m_run, float& l_run,
+                                           float c_log2, int lane, int hh)
+{
+    typedef Cfg<D> C;
+    typedef typename Mma<T>::vec8 vec8;
     // P = 2^(s * c - m); l is summed from fp32 P, then P is rounded to the
     // input type for the P.V product (Round 4, "The P cast")
     vec8 p[C::KT];
@@ -301,7 +338,7 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 {
     typedef Cfg<D> C;
     typedef typename Mma<T>::vec8 vec8;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * C::TILE];
 
     // blockIdx -> (b*H + h, query tile), XCD-aware: hardware id i runs on XCD
     // i % 8; give each XCD a contiguous range of logical ids.
@@ -341,28 +378,54 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     for (int db = 0; db < C::DB; ++db) oacc[db] = (f32x16){};
     float m_run = -1e30f, l_run = 0.f;
 
-    issue_tile<T, D>(smem, kh, vh, 0, N, wave, lane);
-    stage_barrier();
+    // LDS: K tiles in buffers 0/1, V tiles in buffers 2/3. Iteration j reads
+    // K_{j+1} (scores of the next tile) and V_j (P.V of this tile) while the
+    // copies of K_{j+2} and V_{j+1} are in flight; one barrier per tile.
+    auto kbuf = [&](int i) { return smem + (i & 1) * C::TILE; };
+    auto vbuf = [&](int i) { return smem + (2 + (i & 1)) * C::TILE; };
 
-    // Tiles [0, n_unmasked) need no mask, [n_unmasked, n_tiles) get it. The
-    // next tile's copies are in flight while the current one is used.
+    const uint32_t head_bytes = (uint32_t)N * (D * 2);
+    const rsrc_t krs = head_rsrc(kh, head_bytes), vrs = head_rsrc(vh, head_bytes);
+    const uint32_t lane_off = tile_lane_offset<D>(wave, lane);
+    issue_tile<D>(kbuf(0), krs, 0, wave, lane_off);
+    issue_tile<D>(vbuf(0), vrs, 0, wave, lane_off);
+    if (n_tiles > 1) issue_tile<D>(kbuf(1), krs, C::BN, wave, lane_off);
+    stage_barrier();
+    f32x16 sa[C::KB], sb[C::KB];
+    scores<T, D>(sa, kbuf(0), qf, l32, hh);
+    stage_barrier();  // K_0's buffer is refilled in the first iteration
+
+    // One tile: sc holds the scores of tile j; sn receives those of tile j+1
+    // (past the last tile it reads a stale buffer and is never used).
+    auto step = [&](auto masked, int j, f32x16 (&sc)[C::KB], f32x16 (&sn)[C::KB]) {
+        if (j + 2 < n_tiles) issue_tile<D>(kbuf(j), krs, (j + 2) * C::BN, wave, lane_off);
+        if (j + 1 < n_tiles) issue_tile<D>(vbuf(j + 1), vrs, (j + 1) * C::BN, wave, lane_off);
+        if (decltype(masked)::value) mask_scores<D, CAUSAL>(sc, j * C::BN, qrow, N, hh);
+        rescale_if_needed<T, D>(sc, oacc, m_run, l_run, c_log2);
+        scores<T, D>(sn, kbuf(j + 1), qf, l32, hh);
+        softmax_pv<T, D>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
+        stage_barrier();
+    };
+    typedef std::integral_constant<bool, false> unmasked_t;
+    typedef std::integral_constant<bool, true> masked_t;
+
+    // tiles [0, n_unmasked) need no mask, [n_unmasked, n_tiles) get it
     int j = 0;
-    for (; j < n_unmasked; ++j) {
-        if (j + 1 < n_tiles)
-            issue_tile<T, D>(smem + ((j + 1) & 1) * C::STAGE, kh, vh, (j + 1) * C::BN, N, wave, lane);
-        const uint16_t* ks = smem + (j & 1) * C::STAGE;
-        attend_tile<T, D, CAUSAL, false>(ks, ks + C::TILE, qf, oacc, m_run, l_run, c_log2,
-                                         j * C::BN, qrow, N, lane, l32, hh);
-        stage_barrier();
+    for (; j + 2 <= n_unmasked; j += 2) {
+        step(unmasked_t(), j, sa, sb);
+        step(unmasked_t(), j + 1, sb, sa);
     }
-    for (; j < n_tiles; ++j) {
-        if (j + 1 < n_tiles)
-            issue_tile<T, D>(smem + ((j + 1) & 1) * C::STAGE, kh, vh, (j + 1) * C::BN, N, wave, lane);
-        const uint16_t* ks = smem + (j & 1) * C::STAGE;
-        attend_tile<T, D, CAUSAL, true>(ks, ks + C::TILE, qf, oacc, m_run, l_run, c_log2,
-                                        j * C::BN, qrow, N, lane, l32, hh);
-        stage_barrier();
+    if (j < n_unmasked) {
+        step(unmasked_t(), j, sa, sb);
+        ++j;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) sa[kb] = sb[kb];
     }
+    for (; j + 2 <= n_tiles; j += 2) {
+        step(masked_t(), j, sa, sb);
+        step(masked_t(), j + 1, sb, sa);
+    }
+    if (j < n_tiles) step(masked_t(), j, sa, sb);
 
     // Epilogue: O = O_acc / l in the input type, lse = (m + log2 l) * ln 2.
     const float l_tot = swap_halves_sum(l_run);
