@@ -56,7 +56,8 @@ typedef enum {
  *             logsumexp in natural-log units (kept for a backward pass, as
  *             in "How to optimise a Triton FlashAttention-2 kernel step by
  *             step with a profiler", Round 4, "exp2").
- *   B, H, N : >= 1.  d : 64 or 128 (other values: FA_ERR_UNSUPPORTED).
+ *   B, H, N : >= 1, with N*d*2 < 2^32 (one head below 4 GiB).
+ *   d       : 64 or 128 (other values: FA_ERR_UNSUPPORTED).
  *   causal  : 0 or 1.
  *   scale   : finite and > 0; multiplies Q K^T before the softmax
  *             (1/sqrt(d) is the usual choice, the caller computes it).
@@ -106,7 +107,9 @@ typedef struct {
     int64_t workgroups;     /* grid size */
     int64_t pairs_visited;  /* visited (query tile, key tile) pairs, all heads */
     double mfma_flops;      /* FLOPs the matrix cores execute: 4*d per (row, key)
-                               of every visited tile pair, masked ones included */
+                               of every visited tile pair, masked ones included,
+                               plus one surplus score tile (2*d per row and key)
+                               per query tile from the software pipeline */
     double algo_flops;      /* 4*B*H*N*N*d, halved for causal (the pages' convention) */
     double algo_bytes;      /* compulsory HBM bytes: q, k, v read and o written
                                once (8*B*H*N*d for 2-byte types) plus lse */

@@ -46,6 +46,8 @@ int check_problem(int B, int H, int N, int d, int causal, int dtype)
         return fail(FA_ERR_INVALID_ARG, "B*H*ceil(N/128) exceeds the grid limit");
     const int64_t elems = bh * (int64_t)N * d;
     if (elems > INT64_MAX / 4) return fail(FA_ERR_INVALID_ARG, "B*H*N*d too large");
+    if ((int64_t)N * d * 2 > (int64_t)UINT32_MAX)
+        return fail(FA_ERR_INVALID_ARG, "one head (N*d*2 bytes) must be below 4 GiB");
     return FA_OK;
 }
 
@@ -100,7 +102,10 @@ int fa_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t* plan)
     plan->lds_bytes = fa::lds_bytes(d);
     plan->workgroups = bh * ((N + bm - 1) / bm);
     plan->pairs_visited = bh * counts[1];
-    plan->mfma_flops = 4.0 * d * (double)bm * bn * (double)plan->pairs_visited;
+    // every visited pair costs S = Q K^T and P V; the pipeline also computes
+    // one surplus score tile per query tile past the last key tile
+    plan->mfma_flops = 4.0 * d * (double)bm * bn * (double)plan->pairs_visited +
+                       2.0 * d * (double)bm * bn * (double)plan->workgroups;
     const double nn = (double)N * (double)N;
     plan->algo_flops = 4.0 * (double)bh * nn * d * (causal ? 0.5 : 1.0);
     plan->algo_bytes = 8.0 * (double)bh * N * d + 4.0 * (double)bh * N;
