@@ -116,14 +116,23 @@ struct Cfg {
 };
 
 // Chunk swizzle: 16-byte chunk c of tile row r is stored at chunk c ^ swz(r).
-// d=128 (16 chunks/row): 16 consecutive rows map one chunk to 16 distinct
-// chunks (K operand reads), and 4 consecutive rows x 2 adjacent chunks map to
-// 8 distinct chunks (V transposed reads). d=64 (8 chunks/row) likewise.
+// The LDS has 64 four-byte banks; a 16-byte read is served 16 lanes at a
+// time, an 8-byte read 32 lanes at a time.
+//  * K operand (ds_read_b128): 16 consecutive rows read one logical chunk;
+//    swz is a bijection on r mod 16 (d=128) or maps the 8 even and the 8 odd
+//    rows (the two bank halves of a 128-byte row pair, d=64) to distinct
+//    chunks, so the 16 lanes hit 16 distinct bank quads.
+//  * V operand (ds_read_b64_tr_b16): a half-wave reads rows 4a..4a+3 at
+//    logical chunks {4b, 4b+1} (lanes 0-15) and {4b+2, 4b+3} (lanes 16-31);
+//    swz changes bits 2-3 between those rows and leaves bit 1 alone, so the
+//    two lane groups fall in disjoint halves of the 64 banks.
+// Rows 256/CPR apart have the same swizzle (tile_lane_offset relies on it).
 template <int D>
 __device__ __forceinline__ int swz(int row)
 {
-    if (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
-    return ((row & 3) << 1) | ((row >> 2) & 1);
+    if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    const int m = (row >> 1) & 7;
+    return ((m & 1) << 2) | ((m >> 1) & 3);
 }
 
 __device__ __forceinline__ float swap_halves_max(float x)
