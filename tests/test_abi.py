@@ -131,7 +131,7 @@ def test_plan_flops_match_printed_counts(lib):
     assert abs(c["algo_flops"] - g["value"]) <= g["printed_digits"]
     # non-causal with tile-divisible N: the matrix cores execute the algorithm's FLOPs
     # plus one surplus 64-key score tile per 128-row query tile (pipeline tail)
-    tail = 2 * 64 * 128 * 64 * nc["workgroups"]
+    tail = 2 * 64 * nc["block_m"] * 64 * nc["workgroups"]
     assert nc["mfma_flops"] == nc["algo_flops"] + tail
     assert c["mfma_flops"] > c["algo_flops"] + tail
 
@@ -149,3 +149,14 @@ def test_plan_rejects_like_fa_fwd(lib):
     assert e.value.status == fa.FA_ERR_UNSUPPORTED
     with pytest.raises(fa.FaError):
         fa.fa_plan(1, 1, 0, 64, 0, fa.FA_DTYPE_BF16)
+
+
+def test_plan_picks_workgroup_shape(lib):
+    # non-causal problems that give every CU a 256-row workgroup use 8 waves
+    big = fa.fa_plan(4, 16, 4096, 128, 0, fa.FA_DTYPE_BF16)
+    assert (big["block_m"], big["threads"], big["workgroups"]) == (256, 512, 1024)
+    # causal problems and small grids keep 128-row, 4-wave workgroups
+    causal = fa.fa_plan(4, 16, 4096, 128, 1, fa.FA_DTYPE_BF16)
+    assert (causal["block_m"], causal["threads"], causal["workgroups"]) == (128, 256, 2048)
+    small = fa.fa_plan(2, 4, 1000, 64, 0, fa.FA_DTYPE_F16)
+    assert (small["block_m"], small["threads"], small["workgroups"]) == (128, 256, 64)

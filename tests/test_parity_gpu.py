@@ -98,6 +98,16 @@ def test_edge_lengths(N, d):
         check(q, k, v, causal, label=f"edge N={N} d={d} {dtype}")
 
 
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "fp16")])
+def test_large_grid_ragged_length(d, dtype):
+    # enough heads that non-causal runs the 256-row workgroup shape, with a
+    # sequence length that is not a multiple of any tile
+    assert fa.fa_plan(8, 16, 1000, d, 0, fa.dtype_code(getattr(torch, {"bf16": "bfloat16", "fp16": "float16"}[dtype])))["block_m"] == 256
+    q, k, v = make_qkv(8, 16, 1000, d, dtype, 51)
+    for causal in (False, True):
+        check(q, k, v, causal, label=f"B8 H16 N1000 d{d} {dtype}")
+
+
 def test_many_heads_ragged_grid():
     # 3*100 heads x 3 query tiles = 900 workgroups: not a multiple of the 8 XCDs
     q, k, v = make_qkv(3, 100, 300, 128, "bf16", 40)

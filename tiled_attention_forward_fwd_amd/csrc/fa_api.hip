@@ -41,7 +41,7 @@ int check_problem(int B, int H, int N, int d, int causal, int dtype)
         return fail(FA_ERR_INVALID_ARG, "dtype must be FA_DTYPE_F16 or FA_DTYPE_BF16");
     if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
     const int64_t bh = (int64_t)B * H;
-    const int64_t n_qt = ((int64_t)N + fa::block_m() - 1) / fa::block_m();
+    const int64_t n_qt = ((int64_t)N + 127) / 128;  // the smallest workgroup tile
     if (bh > INT32_MAX || bh * n_qt > (int64_t)UINT32_MAX)
         return fail(FA_ERR_INVALID_ARG, "B*H*ceil(N/128) exceeds the grid limit");
     const int64_t elems = bh * (int64_t)N * d;
@@ -92,13 +92,14 @@ int fa_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t* plan)
     if (!plan) return fail(FA_ERR_INVALID_ARG, "plan is NULL");
     const int rc = check_problem(B, H, N, d, causal, dtype);
     if (rc != FA_OK) return rc;
-    const int bm = fa::block_m(), bn = fa::block_n(d);
+    const fa::Shape sh = fa::pick_shape(B, H, N, d, causal != 0);
+    const int bm = sh.block_m, bn = fa::block_n(d);
     int64_t counts[4];
     fa_tile_counts(N, bm, bn, causal, counts);
     const int64_t bh = (int64_t)B * H;
     plan->block_m = bm;
     plan->block_n = bn;
-    plan->threads = fa::threads_per_block();
+    plan->threads = sh.threads;
     plan->lds_bytes = fa::lds_bytes(d);
     plan->workgroups = bh * ((N + bm - 1) / bm);
     plan->pairs_visited = bh * counts[1];

@@ -9,9 +9,10 @@
 // written once.
 //
 // gfx950 mapping (our design, not the pages'):
-//   * A workgroup is 4 waves (256 threads) and owns 128 query rows; each wave
-//     owns 32 whole rows, so row reductions never leave the wave (the pages'
-//     rule that every warp must own whole rows, Round 0 / Round 1).
+//   * A workgroup is WAVES waves; each wave owns QB blocks of 32 whole query
+//     rows, so row reductions never leave the wave (the pages' rule that every
+//     warp must own whole rows, Round 0 / Round 1). With QB = 2 every K and V
+//     operand read from LDS feeds two MFMAs.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_{bf16,f16}: keys on the M axis, queries on N. In the
 //     32x32 accumulator each lane holds 16 keys of ONE query, and the other 16
@@ -19,9 +20,9 @@
 //     in-lane plus one v_permlane32_swap, and the rescale of O by alpha is one
 //     scalar per lane.
 //   * O^T += V^T P^T takes P^T straight from the score registers as the B
-//     operand. The score accumulator hands each lane keys {8g + 4h + t}; V^T
-//     is written to LDS with its keys permuted the same way, so every operand
-//     is one 16-byte LDS read and P never goes through LDS.
+//     operand: the accumulator hands lane half h, element e the key
+//     16t + 8(e/4) + 4h + (e%4), and the V^T operand is read in that key
+//     order, so P never goes through LDS.
 //   * Q is loaded once into registers in B-operand layout.
 //   * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 ... lds,
 //     16 bytes per lane, no staging registers), row-major and dense. The
@@ -35,10 +36,11 @@
 //     one dim each: a transposed read of the row-major tile.
 //   * Software pipeline over key tiles, two K and two V buffers in LDS:
 //     iteration j computes the scores of tile j+1 on the matrix cores while
-//     the vector units run the softmax of tile j, then P_j V_j; the copies of
-//     K_{j+2} and V_{j+1} are in flight meanwhile; one barrier per tile. The
-//     copies go through a buffer descriptor bounded to the head, so the rows
-//     of a ragged last tile past N arrive as zeros (and are masked).
+//     the vector units reduce the row max of tile j, then runs the exp2 work
+//     and P_j V_j; the copies of K_{j+2} and V_{j+1} are in flight meanwhile;
+//     one barrier per tile. The copies go through a buffer descriptor bounded
+//     to the head, so the rows of a ragged last tile past N arrive as zeros
+//     (and are masked).
 //   * exp2 with the softmax scale and log2(e) folded into one constant
 //     (Round 4, "exp2"); the running max is kept in log2 units; the row max is
 //     taken on the scaled scores so the maximal term is 2^0 = 1.
@@ -69,6 +71,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
 template <typename T>
 struct Mma;
@@ -91,17 +95,15 @@ struct Mma<_Float16> {
     }
 };
 
-constexpr int kThreads = 256;  // 4 waves of 64
-constexpr int kWaves = 4;
-constexpr int kBlockM = 128;   // query rows per workgroup (32 per wave)
-constexpr int kXcds = 8;       // XCDs of an MI355X
+constexpr int kXcds = 8;  // XCDs of an MI355X
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-template <int D>
+// Tile shape: head dim D, WAVES waves per workgroup, QB 32-row query blocks
+// per wave, BN = 64 keys per K/V tile.
+template <int D, int WAVES, int QB>
 struct Cfg {
     static_assert(D == 64 || D == 128, "head dim");
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int BM = 32 * QB * WAVES;    // query rows per workgroup
     static constexpr int BN = 64;                 // keys per tile
     static constexpr int CPR = D / 8;             // 16-byte chunks per row
     static constexpr int TILE = BN * D;           // elements of one K or V tile (dense)
@@ -110,9 +112,10 @@ struct Cfg {
     static constexpr int DS = D / 16;             // MFMA k-steps of S^T = K Q^T
     static constexpr int DB = D / 32;             // 32-row blocks of O^T
     static constexpr int KT = BN / 16;            // MFMA k-steps of O^T += V^T P^T
-    static constexpr int LOADS = BN * CPR / kThreads;  // 16-byte loads per thread, each of K and V
-    static_assert(LOADS * kThreads == BN * CPR, "tile split");
-    static_assert(BN * CPR % (64 * kWaves) == 0, "whole wave loads");
+    static constexpr int LOADS = BN * CPR / THREADS;  // 16-byte copies per thread, each of K and V
+    static_assert(LOADS * THREADS == BN * CPR, "tile split");
+    // rows between a lane's consecutive copies keep the swizzle (period 16)
+    static_assert((64 * WAVES / CPR) % 16 == 0 || LOADS == 1, "copy stride");
 };
 
 // Chunk swizzle: 16-byte chunk c of tile row r is stored at chunk c ^ swz(r).
@@ -126,7 +129,7 @@ struct Cfg {
 //    logical chunks {4b, 4b+1} (lanes 0-15) and {4b+2, 4b+3} (lanes 16-31);
 //    swz changes bits 2-3 between those rows and leaves bit 1 alone, so the
 //    two lane groups fall in disjoint halves of the 64 banks.
-// Rows 256/CPR apart have the same swizzle (tile_lane_offset relies on it).
+// swz has period 16 in r (tile_lane_offset relies on it).
 template <int D>
 __device__ __forceinline__ int swz(int row)
 {
@@ -178,29 +181,28 @@ __device__ __forceinline__ void copy16_to_lds(rsrc_t r, uint16_t* lds_base, uint
 #endif
 }
 
-// HBM -> LDS copy of rows [k0, k0 + BN) of one K or V head. Wave w, load i
+// HBM -> LDS copy of rows [k0, k0 + BN) of one K or V head. Wave w, copy i
 // fills 64 consecutive LDS chunks; lane l fetches the global chunk that the
-// swizzle places there. Load i is 256/CPR rows below load 0, which leaves the
-// swizzle unchanged, so every load of a lane is one per-lane byte offset plus
-// a wave-uniform k0 * D * 2 + i * 4096.
+// swizzle places there. Copy i is 64*WAVES/CPR rows below copy 0, a multiple
+// of the swizzle period, so every copy of a lane is one per-lane byte offset
+// plus a wave-uniform k0 * D * 2 + i * WAVES * 64 * 16.
 template <int D>
 __device__ __forceinline__ uint32_t tile_lane_offset(int wave, int lane)
 {
-    typedef Cfg<D> C;
     const int c = wave * 64 + lane;
-    const int r0 = c / C::CPR, pc = c % C::CPR;
+    const int r0 = c / (D / 8), pc = c % (D / 8);
     return (uint32_t)(r0 * D * 2 + (pc ^ swz<D>(r0)) * 16);
 }
 
-template <int D>
+template <int D, int WAVES, int QB>
 __device__ __forceinline__ void issue_tile(uint16_t* buf, rsrc_t src, int k0, int wave,
                                            uint32_t lane_off)
 {
-    typedef Cfg<D> C;
+    typedef Cfg<D, WAVES, QB> C;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i)
-        copy16_to_lds(src, buf + (i * kWaves + wave) * 64 * 8, lane_off,
-                      (uint32_t)k0 * (D * 2) + i * 4096);
+        copy16_to_lds(src, buf + (i * WAVES + wave) * 64 * 8, lane_off,
+                      (uint32_t)k0 * (D * 2) + i * (WAVES * 64 * 16));
 }
 
 // Waits for this thread's outstanding LDS copies and LDS reads, then for the
@@ -225,36 +227,36 @@ __device__ __forceinline__ _Float16 to_elem<_Float16>(float x) { return (_Float1
 // O * alpha multiplies off the common path.
 constexpr float kRescaleSlack = 8.0f;
 
-// S^T = K Q^T for one key tile: s[kb] holds keys 32*kb + (accumulator rows)
-// of this lane's query.
-template <typename T, int D>
-__device__ __forceinline__ void scores(f32x16 (&s)[Cfg<D>::KB], const uint16_t* __restrict__ ks,
-                                       const typename Mma<T>::vec8 (&qf)[Cfg<D>::DS], int l32,
-                                       int hh)
+// S^T = K Q^T for one key tile: s[qb][kb] holds keys 32*kb + (accumulator
+// rows) of this lane's query in block qb. Each K operand read feeds QB MFMAs.
+template <typename T, int D, int QB, int KB, int DS>
+__device__ __forceinline__ void scores(f32x16 (&s)[QB][KB], const uint16_t* __restrict__ ks,
+                                       const typename Mma<T>::vec8 (&qf)[QB][DS], int l32, int hh)
 {
-    typedef Cfg<D> C;
     typedef typename Mma<T>::vec8 vec8;
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-        s[kb] = (f32x16){};
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = (f32x16){};
         const int row = kb * 32 + l32;
         const uint16_t* krow = ks + row * D;
         const int sw = swz<D>(row);
 #pragma unroll
-        for (int ds = 0; ds < C::DS; ++ds) {
+        for (int ds = 0; ds < DS; ++ds) {
             vec8 a = as_vec8<vec8>(*(const u32x4*)(krow + (((2 * ds + hh) ^ sw) * 8)));
-            s[kb] = Mma<T>::run(a, qf[ds], s[kb]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) s[qb][kb] = Mma<T>::run(a, qf[qb][ds], s[qb][kb]);
         }
     }
 }
 
 // Diagonal / ragged tiles: keys past N, and for causal attention keys after
 // the lane's query, get score -inf.
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void mask_scores(f32x16 (&s)[Cfg<D>::KB], int k0, int qrow, int N, int hh)
+template <int KB, bool CAUSAL>
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[KB], int k0, int qrow, int N, int hh)
 {
 #pragma unroll
-    for (int kb = 0; kb < Cfg<D>::KB; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -264,68 +266,78 @@ __device__ __forceinline__ void mask_scores(f32x16 (&s)[Cfg<D>::KB], int k0, int
     }
 }
 
-// Online-softmax update for one tile of scores, then O^T += V^T P^T.
-// Rows whose max grew past the slack trigger a wave-uniform rescale first.
-template <typename T, int D>
-__device__ __forceinline__ void rescale_if_needed(const f32x16 (&s)[Cfg<D>::KB],
-                                                  f32x16 (&o)[Cfg<D>::DB], float& m_run,
-                                                  float& l_run, float c_log2)
+// Row max of one block of scores in log2 units (both lane halves of a row).
+template <int KB>
+__device__ __forceinline__ float row_max_log2(const f32x16 (&s)[KB], float c_log2)
 {
-    typedef Cfg<D> C;
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = swap_halves_max(mx) * c_log2;
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack)) {
-        // some row's max grew past the slack: move every row of the wave to
-        // its true running max
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
+    return swap_halves_max(mx) * c_log2;
+}
+
+// Online-softmax rescale: when some row of the wave grew past the slack, every
+// row of the wave moves to its true running max (wave-uniform branch).
+template <int DB, int QB>
+__device__ __forceinline__ void rescale_if_needed(const float (&mx)[QB], f32x16 (&o)[QB][DB],
+                                                  float (&m_run)[QB], float (&l_run)[QB])
+{
+    bool grew = false;
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
+    for (int qb = 0; qb < QB; ++qb) grew = grew || (mx[qb] > m_run[qb] + kRescaleSlack);
+    if (__builtin_amdgcn_ballot_w64(grew)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float m_new = fmaxf(m_run[qb], mx[qb]);
+            const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+            m_run[qb] = m_new;
+            l_run[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
+        }
     }
 }
 
-template <typename T, int D>
-__device__ __forceinline__ void softmax_pv(const f32x16 (&s)[Cfg<D>::KB],
-                                           const uint16_t* __restrict__ vts,
-                                           f32x16 (&o)[Cfg<D>::DB], float m_run, float& l_run,
-                                           float c_log2, int lane, int hh)
+// P = 2^(s * c - m) rounded to the input type (l summed from fp32 P first,
+// Round 4 "The P cast"), then O^T += V^T P^T. V^T operand, lane l = 16g + i:
+// dim 32*db + (l % 32); elements 0..3 are keys 16t + 4h + [0,4), elements
+// 4..7 keys 16t + 8 + 4h + [0,4) (h = g/2), the key order of P^T. Each of the
+// two transposed reads has lane i address key (base + i/4), dims
+// 4*(i%4) + [0,4) of the group's 16 dims. Each V operand feeds QB MFMAs; the
+// t-major order consumes P in the order it is produced.
+template <typename T, int D, int QB, int KB, int DB, int KT>
+__device__ __forceinline__ void softmax_pv(const f32x16 (&s)[QB][KB], const uint16_t* __restrict__ vts,
+                                           f32x16 (&o)[QB][DB], const float (&m_run)[QB],
+                                           float (&l_run)[QB], float c_log2, int lane, int hh)
 {
-    typedef Cfg<D> C;
     typedef typename Mma<T>::vec8 vec8;
-    // P = 2^(s * c - m); l is summed from fp32 P, then P is rounded to the
-    // input type for the P.V product (Round 4, "The P cast")
-    vec8 p[C::KT];
-    float rs = 0.f;
+    vec8 p[QB][KT];
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
+    for (int qb = 0; qb < QB; ++qb) {
+        float rs = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c_log2, -m_run));
-            rs += e;
-            p[kb * 2 + (r >> 3)][r & 7] = to_elem<T>(e);
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r], c_log2, -m_run[qb]));
+                rs += e;
+                p[qb][kb * 2 + (r >> 3)][r & 7] = to_elem<T>(e);
+            }
         }
+        l_run[qb] += rs;
     }
-    l_run += rs;
 
-    // V^T operand, lane l = 16g + i: dim 32*db + (l % 32); elements 0..3 are
-    // keys 16t + 4h + [0,4), elements 4..7 keys 16t + 8 + 4h + [0,4) (h = g/2),
-    // the key order of P^T. Each of the two transposed reads has lane i address
-    // key (base + i/4), dims 4*(i%4) + [0,4) of the group's 16 dims.
     const int gi = lane & 15, g1 = (lane >> 4) & 1;
+    const int half = (gi & 1) * 4;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-        const int chunk = 4 * db + 2 * g1 + ((gi & 3) >> 1);
-        const int half = (gi & 1) * 4;
+    for (int t = 0; t < KT; ++t) {
+        const int key0 = 16 * t + 4 * hh + (gi >> 2);
+        const int key1 = key0 + 8;
 #pragma unroll
-        for (int t = 0; t < C::KT; ++t) {
-            const int key0 = 16 * t + 4 * hh + (gi >> 2);
-            const int key1 = key0 + 8;
+        for (int db = 0; db < DB; ++db) {
+            const int chunk = 4 * db + 2 * g1 + ((gi & 3) >> 1);
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) s16x4*)(vts + key0 * D + ((chunk ^ swz<D>(key0)) * 8) + half));
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -335,17 +347,58 @@ __device__ __forceinline__ void softmax_pv(const f32x16 (&s)[Cfg<D>::KB],
             w[1] = __builtin_bit_cast(u32x2, lo)[1];
             w[2] = __builtin_bit_cast(u32x2, hi)[0];
             w[3] = __builtin_bit_cast(u32x2, hi)[1];
-            o[db] = Mma<T>::run(as_vec8<vec8>(w), p[t], o[db]);
+            const vec8 a = as_vec8<vec8>(w);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) o[qb][db] = Mma<T>::run(a, p[qb][t], o[qb][db]);
         }
     }
 }
 
-template <typename T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+// Instruction order of a pipelined tile. The scores of the next tile are
+// issued first (MFMAs that need only K and Q) so the matrix cores work while
+// the row max of this tile is reduced; the score MFMAs keep their K operand
+// reads a few MFMAs ahead. After the (rare) rescale branch, the P.V MFMAs
+// follow their exp2/convert work with their transposed V reads issued ahead.
+// Vector instructions are left to the scheduler.
+template <int D, int WAVES, int QB>
+__device__ __forceinline__ void order_scores_block()
+{
+    typedef Cfg<D, WAVES, QB> C;
+    constexpr int n_reads = C::KB * C::DS;  // one K read per QB MFMAs
+    constexpr int lead = 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, lead, 0);
+#pragma unroll
+    for (int i = 0; i < n_reads - lead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < lead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+}
+
+template <int D, int WAVES, int QB>
+__device__ __forceinline__ void order_pv_block()
+{
+    typedef Cfg<D, WAVES, QB> C;
+    constexpr int n_ops = C::DB * C::KT;  // two V reads per QB MFMAs
+    constexpr int lead = 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * lead, 0);
+#pragma unroll
+    for (int i = 0; i < n_ops - lead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < lead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+}
+
+template <typename T, int D, bool CAUSAL, int WAVES, int QB>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
+                          amdgpu_waves_per_eu(2 / QB, 2 / QB)))
 void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                    T* __restrict__ o, float* __restrict__ lse, int N, int n_qt, float c_log2)
 {
-    typedef Cfg<D> C;
+    typedef Cfg<D, WAVES, QB> C;
     typedef typename Mma<T>::vec8 vec8;
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * C::TILE];
 
@@ -359,7 +412,7 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     const uint32_t bh = logical / (uint32_t)n_qt;
     uint32_t qt = logical % (uint32_t)n_qt;
     if (CAUSAL) qt = (uint32_t)n_qt - 1 - qt;  // longest causal tiles first
-    const int q0 = (int)qt * kBlockM;
+    const int q0 = (int)qt * C::BM;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -369,23 +422,33 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     const T* kh = k + head_off;
     const T* vh = v + head_off;
 
-    // Q fragment: B operand of S^T = K Q^T, query qrow, dims 16*ds + 8*hh + [0, 8).
-    const int qrow = q0 + wave * 32 + l32;
-    vec8 qf[C::DS];
+    // Q fragments: B operand of S^T = K Q^T, query qrow[qb], dims
+    // 16*ds + 8*hh + [0, 8). Rows past N are zero (their outputs are not stored).
+    int qrow[QB];
+    vec8 qf[QB][C::DS];
 #pragma unroll
-    for (int ds = 0; ds < C::DS; ++ds) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (qrow < N) x = *(const u32x4*)(qh + (int64_t)qrow * D + ds * 16 + hh * 8);
-        qf[ds] = as_vec8<vec8>(x);
+    for (int qb = 0; qb < QB; ++qb) {
+        qrow[qb] = q0 + (wave * QB + qb) * 32 + l32;
+#pragma unroll
+        for (int ds = 0; ds < C::DS; ++ds) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (qrow[qb] < N) x = *(const u32x4*)(qh + (int64_t)qrow[qb] * D + ds * 16 + hh * 8);
+            qf[qb][ds] = as_vec8<vec8>(x);
+        }
     }
 
-    const TileSpan span = tile_span(q0, kBlockM, C::BN, N, CAUSAL);
+    const TileSpan span = tile_span(q0, C::BM, C::BN, N, CAUSAL);
     const int n_unmasked = (int)span.unmasked, n_tiles = (int)span.total;
 
-    f32x16 oacc[C::DB];
+    f32x16 oacc[QB][C::DB];
+    float m_run[QB], l_run[QB];
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) oacc[db] = (f32x16){};
-    float m_run = -1e30f, l_run = 0.f;
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) oacc[qb][db] = (f32x16){};
+        m_run[qb] = -1e30f;
+        l_run[qb] = 0.f;
+    }
 
     // LDS: K tiles in buffers 0/1, V tiles in buffers 2/3. Iteration j reads
     // K_{j+1} (scores of the next tile) and V_j (P.V of this tile) while the
@@ -396,29 +459,39 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     const uint32_t head_bytes = (uint32_t)N * (D * 2);
     const rsrc_t krs = head_rsrc(kh, head_bytes), vrs = head_rsrc(vh, head_bytes);
     const uint32_t lane_off = tile_lane_offset<D>(wave, lane);
-    issue_tile<D>(kbuf(0), krs, 0, wave, lane_off);
-    issue_tile<D>(vbuf(0), vrs, 0, wave, lane_off);
-    if (n_tiles > 1) issue_tile<D>(kbuf(1), krs, C::BN, wave, lane_off);
+    issue_tile<D, WAVES, QB>(kbuf(0), krs, 0, wave, lane_off);
+    issue_tile<D, WAVES, QB>(vbuf(0), vrs, 0, wave, lane_off);
+    if (n_tiles > 1) issue_tile<D, WAVES, QB>(kbuf(1), krs, C::BN, wave, lane_off);
     stage_barrier();
-    f32x16 sa[C::KB], sb[C::KB];
-    scores<T, D>(sa, kbuf(0), qf, l32, hh);
+    f32x16 sa[QB][C::KB], sb[QB][C::KB];
+    scores<T, D, QB, C::KB, C::DS>(sa, kbuf(0), qf, l32, hh);
     stage_barrier();  // K_0's buffer is refilled in the first iteration
 
     // One tile: sc holds the scores of tile j; sn receives those of tile j+1
     // (past the last tile it reads a stale buffer and is never used).
-    auto step = [&](auto masked, int j, f32x16 (&sc)[C::KB], f32x16 (&sn)[C::KB]) {
-        if (j + 2 < n_tiles) issue_tile<D>(kbuf(j), krs, (j + 2) * C::BN, wave, lane_off);
-        if (j + 1 < n_tiles) issue_tile<D>(vbuf(j + 1), vrs, (j + 1) * C::BN, wave, lane_off);
-        if (decltype(masked)::value) mask_scores<D, CAUSAL>(sc, j * C::BN, qrow, N, hh);
-        rescale_if_needed<T, D>(sc, oacc, m_run, l_run, c_log2);
-        scores<T, D>(sn, kbuf(j + 1), qf, l32, hh);
-        softmax_pv<T, D>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
+    auto step = [&](auto masked, int j, f32x16 (&sc)[QB][C::KB], f32x16 (&sn)[QB][C::KB]) {
+        if (j + 2 < n_tiles)
+            issue_tile<D, WAVES, QB>(kbuf(j), krs, (j + 2) * C::BN, wave, lane_off);
+        if (j + 1 < n_tiles)
+            issue_tile<D, WAVES, QB>(vbuf(j + 1), vrs, (j + 1) * C::BN, wave, lane_off);
+        scores<T, D, QB, C::KB, C::DS>(sn, kbuf(j + 1), qf, l32, hh);
+        float mx[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            if (decltype(masked)::value) mask_scores<C::KB, CAUSAL>(sc[qb], j * C::BN, qrow[qb], N, hh);
+            mx[qb] = row_max_log2<C::KB>(sc[qb], c_log2);
+        }
+        order_scores_block<D, WAVES, QB>();
+        rescale_if_needed<C::DB, QB>(mx, oacc, m_run, l_run);
+        softmax_pv<T, D, QB, C::KB, C::DB, C::KT>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
+        order_pv_block<D, WAVES, QB>();
         stage_barrier();
     };
     typedef std::integral_constant<bool, false> unmasked_t;
     typedef std::integral_constant<bool, true> masked_t;
 
-    // tiles [0, n_unmasked) need no mask, [n_unmasked, n_tiles) get it
+    // tiles [0, n_unmasked) need no mask, [n_unmasked, n_tiles) get it; the
+    // loops are unrolled by two so the score registers alternate
     int j = 0;
     for (; j + 2 <= n_unmasked; j += 2) {
         step(unmasked_t(), j, sa, sb);
@@ -428,7 +501,9 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
         step(unmasked_t(), j, sa, sb);
         ++j;
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) sa[kb] = sb[kb];
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < C::KB; ++kb) sa[qb][kb] = sb[qb][kb];
     }
     for (; j + 2 <= n_tiles; j += 2) {
         step(masked_t(), j, sa, sb);
@@ -437,52 +512,85 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     if (j < n_tiles) step(masked_t(), j, sa, sb);
 
     // Epilogue: O = O_acc / l in the input type, lse = (m + log2 l) * ln 2.
-    const float l_tot = swap_halves_sum(l_run);
-    if (qrow < N) {
-        const float inv = 1.0f / l_tot;
-        T* orow = o + head_off + (int64_t)qrow * D;
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
+    for (int qb = 0; qb < QB; ++qb) {
+        const float l_tot = swap_halves_sum(l_run[qb]);
+        if (qrow[qb] < N) {
+            const float inv = 1.0f / l_tot;
+            T* orow = o + head_off + (int64_t)qrow[qb] * D;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                T vals[4];
+            for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) vals[t] = to_elem<T>(oacc[db][4 * g + t] * inv);
-                u32x2 packed = __builtin_bit_cast(u32x2, vals);
-                *(u32x2*)(orow + db * 32 + 8 * g + 4 * hh) = packed;
+                for (int g = 0; g < 4; ++g) {
+                    T vals[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) vals[t] = to_elem<T>(oacc[qb][db][4 * g + t] * inv);
+                    u32x2 packed = __builtin_bit_cast(u32x2, vals);
+                    *(u32x2*)(orow + db * 32 + 8 * g + 4 * hh) = packed;
+                }
             }
+            if (hh == 0)
+                lse[(int64_t)bh * N + qrow[qb]] = (m_run[qb] + log2f(l_tot)) * 0.69314718055994531f;
         }
-        if (hh == 0) lse[(int64_t)bh * N + qrow] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
     }
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, int WAVES, int QB>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                       int N, float scale, hipStream_t stream)
 {
-    const int n_qt = (N + kBlockM - 1) / kBlockM;
+    typedef Cfg<D, WAVES, QB> C;
+    const int n_qt = (N + C::BM - 1) / C::BM;
     const float c_log2 = scale * 1.4426950408889634f;
-    dim3 grid((unsigned)((int64_t)n_qt * BH)), block(kThreads);
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL>), grid, block, 0, stream, (const T*)q,
+    dim3 grid((unsigned)((int64_t)n_qt * BH)), block(C::THREADS);
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, WAVES, QB>), grid, block, 0, stream, (const T*)q,
                        (const T*)k, (const T*)v, (T*)o, lse, N, n_qt, c_log2);
     return hipGetLastError();
 }
 
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_shape(const Shape& sh, const void* q, const void* k, const void* v, void* o,
+                        float* lse, int BH, int N, float scale, hipStream_t stream)
+{
+    if (sh.waves == 8) return launch_one<T, D, CAUSAL, 8, 1>(q, k, v, o, lse, BH, N, scale, stream);
+    return launch_one<T, D, CAUSAL, 4, 1>(q, k, v, o, lse, BH, N, scale, stream);
+}
+
 }  // namespace
 
-int block_m() { return kBlockM; }
-int block_n(int d) { return d == 64 ? Cfg<64>::BN : Cfg<128>::BN; }
-int threads_per_block() { return kThreads; }
-int lds_bytes(int d) { return d == 64 ? Cfg<64>::LDS_BYTES : Cfg<128>::LDS_BYTES; }
+// Workgroup shape per problem. 256-row workgroups (8 waves) stream each K/V
+// tile from L2 once for twice the rows, which lowers L2 and LDS-fill traffic
+// and, the chip being power-limited under this load, raises the clock it
+// holds; they are used for non-causal problems whose grid still gives every
+// CU a workgroup. Causal problems keep 128-row workgroups (less work above
+// the diagonal), as do small grids.
+Shape pick_shape(int B, int H, int N, int d, bool causal)
+{
+    (void)d;
+    Shape sh;
+    sh.waves = 4;
+    sh.rows_per_wave = 32;
+    if (!causal) {
+        const int64_t wg256 = (int64_t)B * H * ((N + 255) / 256);
+        if (wg256 >= 256) sh.waves = 8;
+    }
+    sh.block_m = sh.waves * sh.rows_per_wave;
+    sh.threads = 64 * sh.waves;
+    return sh;
+}
+
+int block_n(int) { return 64; }
+int lds_bytes(int d) { return 4 * 64 * d * 2; }
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                       int H, int N, int d, bool causal, float scale, bool bf16,
                       hipStream_t stream)
 {
     const int BH = B * H;
-#define FA_DISPATCH(T, D)                                                                      \
-    return causal ? launch_one<T, D, true>(q, k, v, o, lse, BH, N, scale, stream)              \
-                  : launch_one<T, D, false>(q, k, v, o, lse, BH, N, scale, stream)
+    const Shape sh = pick_shape(B, H, N, d, causal);
+#define FA_DISPATCH(T, D)                                                                        \
+    return causal ? launch_shape<T, D, true>(sh, q, k, v, o, lse, BH, N, scale, stream)          \
+                  : launch_shape<T, D, false>(sh, q, k, v, o, lse, BH, N, scale, stream)
     if (bf16) {
         if (d == 64) FA_DISPATCH(__bf16, 64);
         FA_DISPATCH(__bf16, 128);

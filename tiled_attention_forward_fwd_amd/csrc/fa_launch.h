@@ -6,9 +6,17 @@
 
 namespace fa {
 
-int block_m();
+// Workgroup shape chosen for a problem: waves per workgroup, query rows per
+// wave, and the resulting rows per workgroup and threads.
+struct Shape {
+    int waves;
+    int rows_per_wave;
+    int block_m;
+    int threads;
+};
+
+Shape pick_shape(int B, int H, int N, int d, bool causal);
 int block_n(int d);
-int threads_per_block();
 int lds_bytes(int d);
 
 // Enqueues the forward kernel; arguments were validated by the caller.
