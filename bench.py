@@ -96,6 +96,42 @@ def warm(fn, min_calls, min_seconds):
     torch.cuda.synchronize()
 
 
+def power_and_clock(step, seconds=2.0):
+    """Socket power (W) and mean graphics clock (MHz) read once with amd-smi
+    while `step` runs back to back; outside the timed region. None if amd-smi
+    is unavailable. Under sustained attention load the MI355X runs at its
+    board power limit, and the clock it holds sets the MFMA rate reached."""
+    import subprocess
+    import threading
+    import torch
+    result = {}
+
+    def sample():
+        time.sleep(seconds / 2)
+        try:
+            r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "--json"],
+                               capture_output=True, text=True, timeout=30)
+            j = json.loads(r.stdout)
+            g = j["gpu_data"][0] if isinstance(j, dict) else j[0]
+            clks = [c["clk"]["value"] for name, c in g["clock"].items()
+                    if name.startswith("gfx_") and isinstance(c, dict)
+                    and isinstance(c.get("clk"), dict) and isinstance(c["clk"].get("value"), (int, float))]
+            result["socket_power_w"] = g["power"]["socket_power"]["value"]
+            result["gfx_clock_mhz"] = round(sum(clks) / len(clks)) if clks else None
+        except Exception as e:  # telemetry is context only
+            result["error"] = str(e)[:200]
+
+    th = threading.Thread(target=sample)
+    t0 = time.perf_counter()
+    th.start()
+    while th.is_alive() or time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+    th.join()
+    return result if "socket_power_w" in result else None
+
+
 def cpu_baseline(cfg, q, k, v, stride):
     """The fp64 oracle on a bounded row sample of the workload (host cores)."""
     import oracle
@@ -207,6 +243,7 @@ def headline(args):
                      "algorithmic_bytes_per_launch": plan_nc["algo_bytes"],
                      "hbm_gbs_compulsory": plan_nc["algo_bytes"] / (k_nc["avg_ms"] * 1e-3) / 1e9},
         "peak_mem_bytes": peak_mem,
+        "telemetry_during_step_loop": power_and_clock(step) if args.telemetry else None,
         "wall_s_timed": wall,
         "kernel_source_sha256_16": kernel_hash(),
         "device": torch.cuda.get_device_name(dev),
@@ -291,6 +328,8 @@ def main():
     ap.add_argument("--cpu-stride", type=int, default=2,
                     help="oracle baseline evaluates every Nth query row")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-telemetry", dest="telemetry", action="store_false",
+                    help="skip the amd-smi power/clock sample (taken outside the timed region)")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
