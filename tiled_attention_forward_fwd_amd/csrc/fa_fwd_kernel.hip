@@ -51,9 +51,11 @@
 //     (Round 4, "Causal tile-skipping"). Masked scores are -inf; the running
 //     max starts at a finite very negative value so a row with no visible key
 //     in a tile never forms -inf - (-inf).
-//   * Workgroup ids are remapped so that all query tiles of one (b, h) run on
-//     the same XCD (workgroups are dealt round-robin over the 8 XCDs, each with
-//     its own L2), which keeps that head's K and V in one L2.
+//   * Workgroup ids are remapped. Non-causal: all query tiles of one (b, h)
+//     run on the same XCD (workgroups are dealt round-robin over the 8 XCDs,
+//     each with its own L2), which keeps that head's K and V in one L2.
+//     Causal: longest tiles of every head first, which balances the uneven
+//     causal work over the XCDs.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -402,16 +404,28 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     typedef typename Mma<T>::vec8 vec8;
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * C::TILE];
 
-    // blockIdx -> (b*H + h, query tile), XCD-aware: hardware id i runs on XCD
-    // i % 8; give each XCD a contiguous range of logical ids.
+    // blockIdx -> (b*H + h, query tile). Hardware id i runs on XCD i % 8 and
+    // the ids are dealt in order.
+    //  * Non-causal (equal tiles): each XCD gets a contiguous range of
+    //    head-major ids, so a head's query tiles share one L2.
+    //  * Causal (a tile's work grows with its index): tile-major, longest
+    //    tiles of all heads first, id i -> head i % BH. Greedy dispatch of
+    //    longest-first work then keeps every XCD busy to the end, and when BH
+    //    is a multiple of 8 every tile of a head still lands on one XCD.
     const uint32_t nwg = gridDim.x, hw = blockIdx.x;
-    const uint32_t xcd = hw % kXcds, slot = hw / kXcds;
-    const uint32_t per = nwg / kXcds, extra = nwg % kXcds;
-    const uint32_t logical = xcd < extra ? xcd * (per + 1) + slot
-                                         : extra * (per + 1) + (xcd - extra) * per + slot;
-    const uint32_t bh = logical / (uint32_t)n_qt;
-    uint32_t qt = logical % (uint32_t)n_qt;
-    if (CAUSAL) qt = (uint32_t)n_qt - 1 - qt;  // longest causal tiles first
+    uint32_t bh, qt;
+    if (CAUSAL) {
+        const uint32_t n_bh = nwg / (uint32_t)n_qt;
+        bh = hw % n_bh;
+        qt = (uint32_t)n_qt - 1 - hw / n_bh;
+    } else {
+        const uint32_t xcd = hw % kXcds, slot = hw / kXcds;
+        const uint32_t per = nwg / kXcds, extra = nwg % kXcds;
+        const uint32_t logical = xcd < extra ? xcd * (per + 1) + slot
+                                             : extra * (per + 1) + (xcd - extra) * per + slot;
+        bh = logical / (uint32_t)n_qt;
+        qt = logical % (uint32_t)n_qt;
+    }
     const int q0 = (int)qt * C::BM;
 
     const int tid = threadIdx.x;
