@@ -107,9 +107,7 @@ typedef struct {
     int64_t workgroups;     /* grid size */
     int64_t pairs_visited;  /* visited (query tile, key tile) pairs, all heads */
     double mfma_flops;      /* FLOPs the matrix cores execute: 4*d per (row, key)
-                               of every visited tile pair, masked ones included,
-                               plus one surplus score tile (2*d per row and key)
-                               per query tile from the software pipeline */
+                               of every visited tile pair, masked ones included */
     double algo_flops;      /* 4*B*H*N*N*d, halved for causal (the pages' convention) */
     double algo_bytes;      /* compulsory HBM bytes: q, k, v read and o written
                                once (8*B*H*N*d for 2-byte types) plus lse */

@@ -129,11 +129,11 @@ def test_plan_flops_match_printed_counts(lib):
     assert abs(nc["algo_flops"] - g["value"]) <= g["printed_digits"]
     g = GOLDEN["flops_causal_needed_B4_H8_N4096_D64"]
     assert abs(c["algo_flops"] - g["value"]) <= g["printed_digits"]
-    # non-causal with tile-divisible N: the matrix cores execute the algorithm's FLOPs
-    # plus one surplus 64-key score tile per 128-row query tile (pipeline tail)
-    tail = 2 * 64 * nc["block_m"] * 64 * nc["workgroups"]
-    assert nc["mfma_flops"] == nc["algo_flops"] + tail
-    assert c["mfma_flops"] > c["algo_flops"] + tail
+    # non-causal with tile-divisible N: the matrix cores execute exactly the
+    # algorithm's FLOPs; causal adds the masked part of the diagonal tiles
+    assert nc["mfma_flops"] == nc["algo_flops"]
+    assert c["mfma_flops"] > c["algo_flops"]
+    assert c["mfma_flops"] == 4 * 64 * c["block_m"] * c["block_n"] * c["pairs_visited"]
 
 
 def test_plan_flop_convention_matches_t4_table(lib):

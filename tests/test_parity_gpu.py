@@ -122,6 +122,21 @@ def test_heavy_tail_small(dtype):
         check(q, k, v, causal, label=f"q*4 N1000 d128 {dtype}")
 
 
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "fp16")])
+@pytest.mark.parametrize("direction", ["growing", "shrinking"])
+def test_scores_that_drift_along_the_keys(d, dtype, direction):
+    # key norms that grow (or shrink) along the sequence move the row max by
+    # tens of log2 units from tile to tile, so the running max is raised, and
+    # O and l rescaled, many times within a row (or never after the first tile)
+    q, k, v = make_qkv(2, 3, 1500, d, dtype, 52)
+    ramp = 1.0 + 6.0 * torch.arange(1500, dtype=torch.float32) / 1500
+    if direction == "shrinking":
+        ramp = ramp.flip(0)
+    k = (k.float() * ramp[None, None, :, None]).to(k.dtype)
+    for causal in (False, True):
+        check(q, k, v, causal, label=f"{direction} keys d{d} {dtype}")
+
+
 def test_custom_scale():
     q, k, v = make_qkv(1, 2, 333, 64, "fp16", 42)
     for causal in (False, True):

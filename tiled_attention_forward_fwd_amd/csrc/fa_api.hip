@@ -103,10 +103,8 @@ int fa_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t* plan)
     plan->lds_bytes = fa::lds_bytes(d);
     plan->workgroups = bh * ((N + bm - 1) / bm);
     plan->pairs_visited = bh * counts[1];
-    // every visited pair costs S = Q K^T and P V; the pipeline also computes
-    // one surplus score tile per query tile past the last key tile
-    plan->mfma_flops = 4.0 * d * (double)bm * bn * (double)plan->pairs_visited +
-                       2.0 * d * (double)bm * bn * (double)plan->workgroups;
+    // every visited pair costs S = Q K^T and P V, masked pairs included
+    plan->mfma_flops = 4.0 * d * (double)bm * bn * (double)plan->pairs_visited;
     const double nn = (double)N * (double)N;
     plan->algo_flops = 4.0 * (double)bh * nn * d * (causal ? 0.5 : 1.0);
     plan->algo_bytes = 8.0 * (double)bh * N * d + 4.0 * (double)bh * N;

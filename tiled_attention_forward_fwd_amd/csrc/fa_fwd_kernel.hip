@@ -18,7 +18,9 @@
 //     32x32 accumulator each lane holds 16 keys of ONE query, and the other 16
 //     keys of that query sit in lane ^ 32. The row max and row sum are
 //     in-lane plus one v_permlane32_swap, and the rescale of O by alpha is one
-//     scalar per lane.
+//     scalar per lane. Consecutive score MFMAs share their Q operand (the
+//     32-key blocks of a tile run interleaved), which lowers operand toggling
+//     and with it the energy per MFMA on this power-limited part.
 //   * O^T += V^T P^T takes P^T straight from the score registers as the B
 //     operand: the accumulator hands lane half h, element e the key
 //     16t + 8(e/4) + 4h + (e%4), and the V^T operand is read in that key
@@ -35,15 +37,18 @@
 //     4e + j/4, so 16 lanes addressing 4 keys x 4 dim-quads receive 4 keys of
 //     one dim each: a transposed read of the row-major tile.
 //   * Software pipeline over key tiles, two K and two V buffers in LDS:
-//     iteration j computes the scores of tile j+1 on the matrix cores while
-//     the vector units reduce the row max of tile j, then runs the exp2 work
-//     and P_j V_j; the copies of K_{j+2} and V_{j+1} are in flight meanwhile;
-//     one barrier per tile. The copies go through a buffer descriptor bounded
-//     to the head, so the rows of a ragged last tile past N arrive as zeros
-//     (and are masked).
+//     iteration j computes the scores of tile j+1 on the matrix cores, then
+//     the exp2 work and P_j V_j of tile j; the copies of K_{j+2} and V_{j+1}
+//     are in flight meanwhile; one barrier per tile. The last tile runs
+//     without a successor, so no score MFMA is wasted. The copies go through
+//     a buffer descriptor bounded to the head, so the rows of a ragged last
+//     tile past N arrive as zeros (and are masked).
 //   * exp2 with the softmax scale and log2(e) folded into one constant
-//     (Round 4, "exp2"); the running max is kept in log2 units; the row max is
-//     taken on the scaled scores so the maximal term is 2^0 = 1.
+//     (Round 4, "exp2"); the running max is kept in log2 units. The max is
+//     updated lazily: a tile's P is taken against the running max and the
+//     tile's own row max is reduced only when a partial row sum shows that P
+//     grew past 2^12 (always on the first tile); O and l carry the same
+//     factor, so O / l is unchanged.
 //   * P is rounded to the input type after l has been summed from fp32 P
 //     (Round 4, "The P cast").
 //   * Causal attention visits no key tile above the diagonal and masks only
@@ -222,13 +227,6 @@ __device__ __forceinline__ __bf16 to_elem<__bf16>(float x) { return (__bf16)x; }
 template <>
 __device__ __forceinline__ _Float16 to_elem<_Float16>(float x) { return (_Float16)x; }
 
-// Largest growth of the row max, in log2 units, that the running state may
-// absorb without rescaling O and l: P then reaches at most 2^8, far inside the
-// fp16/bf16 range, and the final O / l is unchanged (both carry the same
-// factor). Rescaling only when some row of the wave passes this keeps the
-// O * alpha multiplies off the common path.
-constexpr float kRescaleSlack = 8.0f;
-
 // S^T = K Q^T for one key tile: s[qb][kb] holds keys 32*kb + (accumulator
 // rows) of this lane's query in block qb. Each K operand read feeds QB MFMAs.
 template <typename T, int D, int QB, int KB, int DS>
@@ -237,14 +235,16 @@ __device__ __forceinline__ void scores(f32x16 (&s)[QB][KB], const uint16_t* __re
 {
     typedef typename Mma<T>::vec8 vec8;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] = (f32x16){};
-        const int row = kb * 32 + l32;
-        const uint16_t* krow = ks + row * D;
-        const int sw = swz<D>(row);
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
+    for (int ds = 0; ds < DS; ++ds) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int row = kb * 32 + l32;
+            const uint16_t* krow = ks + row * D;
+            const int sw = swz<D>(row);
             vec8 a = as_vec8<vec8>(*(const u32x4*)(krow + (((2 * ds + hh) ^ sw) * 8)));
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) s[qb][kb] = Mma<T>::run(a, qf[qb][ds], s[qb][kb]);
@@ -280,56 +280,75 @@ __device__ __forceinline__ float row_max_log2(const f32x16 (&s)[KB], float c_log
     return swap_halves_max(mx) * c_log2;
 }
 
-// Online-softmax rescale: when some row of the wave grew past the slack, every
-// row of the wave moves to its true running max (wave-uniform branch).
-template <int DB, int QB>
-__device__ __forceinline__ void rescale_if_needed(const float (&mx)[QB], f32x16 (&o)[QB][DB],
-                                                  float (&m_run)[QB], float (&l_run)[QB])
+// P = 2^(s * c - m) of one tile, rounded to the input type after the fp32
+// value has been added to the lane's partial row sum (Round 4, "The P cast").
+template <typename T, int QB, int KB, int KT>
+__device__ __forceinline__ void exp_tile(const f32x16 (&s)[QB][KB], const float (&m_run)[QB], float c_log2,
+                                         typename Mma<T>::vec8 (&p)[QB][KT], float (&rs)[QB])
 {
-    bool grew = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) grew = grew || (mx[qb] > m_run[qb] + kRescaleSlack);
-    if (__builtin_amdgcn_ballot_w64(grew)) {
+    for (int qb = 0; qb < QB; ++qb) {
+        float acc = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r], c_log2, -m_run[qb]));
+                acc += e;
+                p[qb][kb * 2 + (r >> 3)][r & 7] = to_elem<T>(e);
+            }
+        }
+        rs[qb] = acc;
+    }
+}
+
+// Online softmax with a lazily updated max. The exponentials of a tile are
+// taken against the running max m of the earlier tiles; the row max of the
+// tile itself is only needed when that makes some P large. The test is on the
+// lane's partial row sum (32 of the tile's 64 keys), which bounds every P of
+// the lane: while it stays <= 2^12 the tile is accepted as it is. P <= 2^12
+// is far inside the fp16/bf16 range, the accumulators cannot overflow, and
+// O / l and m + log2(l) are unchanged because O and l carry the same factor.
+// Otherwise (always on the first tile, where m is still the initial -1e30,
+// and when the scores grew by more than about 2^12 over m) the wave takes the
+// true row max, rescales O and l by alpha = 2^(m_old - m_new) and recomputes
+// the tile's P (the update of "Programming an attention kernel in Triton",
+// online softmax). The branch is wave-uniform.
+constexpr float kLaneSumBound = 4096.0f;
+
+// Then O^T += V^T P^T. V^T operand, lane l = 16g + i: dim 32*db + (l % 32);
+// elements 0..3 are keys 16t + 4h + [0,4), elements 4..7 keys
+// 16t + 8 + 4h + [0,4) (h = g/2), the key order of P^T. Each of the two
+// transposed reads has lane i address key (base + i/4), dims 4*(i%4) + [0,4)
+// of the group's 16 dims. Each V operand feeds QB MFMAs; the t-major order
+// consumes P in the order it is produced.
+template <typename T, int D, int QB, int KB, int DB, int KT>
+__device__ __forceinline__ void softmax_pv(const f32x16 (&s)[QB][KB], const uint16_t* __restrict__ vts,
+                                           f32x16 (&o)[QB][DB], float (&m_run)[QB],
+                                           float (&l_run)[QB], float c_log2, int lane, int hh)
+{
+    typedef typename Mma<T>::vec8 vec8;
+    vec8 p[QB][KT];
+    float rs[QB];
+    exp_tile<T, QB, KB, KT>(s, m_run, c_log2, p, rs);
+    bool bad = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) bad = bad || !(rs[qb] <= kLaneSumBound);
+    if (__builtin_amdgcn_ballot_w64(bad)) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const float m_new = fmaxf(m_run[qb], mx[qb]);
+            const float mx = row_max_log2<KB>(s[qb], c_log2);
+            const float m_new = fmaxf(m_run[qb], mx);
             const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
             m_run[qb] = m_new;
             l_run[qb] *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
         }
+        exp_tile<T, QB, KB, KT>(s, m_run, c_log2, p, rs);
     }
-}
-
-// P = 2^(s * c - m) rounded to the input type (l summed from fp32 P first,
-// Round 4 "The P cast"), then O^T += V^T P^T. V^T operand, lane l = 16g + i:
-// dim 32*db + (l % 32); elements 0..3 are keys 16t + 4h + [0,4), elements
-// 4..7 keys 16t + 8 + 4h + [0,4) (h = g/2), the key order of P^T. Each of the
-// two transposed reads has lane i address key (base + i/4), dims
-// 4*(i%4) + [0,4) of the group's 16 dims. Each V operand feeds QB MFMAs; the
-// t-major order consumes P in the order it is produced.
-template <typename T, int D, int QB, int KB, int DB, int KT>
-__device__ __forceinline__ void softmax_pv(const f32x16 (&s)[QB][KB], const uint16_t* __restrict__ vts,
-                                           f32x16 (&o)[QB][DB], const float (&m_run)[QB],
-                                           float (&l_run)[QB], float c_log2, int lane, int hh)
-{
-    typedef typename Mma<T>::vec8 vec8;
-    vec8 p[QB][KT];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r], c_log2, -m_run[qb]));
-                rs += e;
-                p[qb][kb * 2 + (r >> 3)][r & 7] = to_elem<T>(e);
-            }
-        }
-        l_run[qb] += rs;
-    }
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
 
     const int gi = lane & 15, g1 = (lane >> 4) & 1;
     const int half = (gi & 1) * 4;
@@ -357,11 +376,10 @@ __device__ __forceinline__ void softmax_pv(const f32x16 (&s)[QB][KB], const uint
 }
 
 // Instruction order of a pipelined tile. The scores of the next tile are
-// issued first (MFMAs that need only K and Q) so the matrix cores work while
-// the row max of this tile is reduced; the score MFMAs keep their K operand
-// reads a few MFMAs ahead. After the (rare) rescale branch, the P.V MFMAs
-// follow their exp2/convert work with their transposed V reads issued ahead.
-// Vector instructions are left to the scheduler.
+// issued first (MFMAs that need only K and Q), keeping their K operand reads
+// a few MFMAs ahead; then the P.V MFMAs follow their exp2/convert work with
+// their transposed V reads issued ahead. Vector instructions are left to the
+// scheduler.
 template <int D, int WAVES, int QB>
 __device__ __forceinline__ void order_scores_block()
 {
@@ -481,22 +499,17 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     scores<T, D, QB, C::KB, C::DS>(sa, kbuf(0), qf, l32, hh);
     stage_barrier();  // K_0's buffer is refilled in the first iteration
 
-    // One tile: sc holds the scores of tile j; sn receives those of tile j+1
-    // (past the last tile it reads a stale buffer and is never used).
+    // One tile that has a successor: sc holds the scores of tile j; sn
+    // receives those of tile j+1.
     auto step = [&](auto masked, int j, f32x16 (&sc)[QB][C::KB], f32x16 (&sn)[QB][C::KB]) {
         if (j + 2 < n_tiles)
             issue_tile<D, WAVES, QB>(kbuf(j), krs, (j + 2) * C::BN, wave, lane_off);
-        if (j + 1 < n_tiles)
-            issue_tile<D, WAVES, QB>(vbuf(j + 1), vrs, (j + 1) * C::BN, wave, lane_off);
+        issue_tile<D, WAVES, QB>(vbuf(j + 1), vrs, (j + 1) * C::BN, wave, lane_off);
         scores<T, D, QB, C::KB, C::DS>(sn, kbuf(j + 1), qf, l32, hh);
-        float mx[QB];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
+        for (int qb = 0; qb < QB; ++qb)
             if (decltype(masked)::value) mask_scores<C::KB, CAUSAL>(sc[qb], j * C::BN, qrow[qb], N, hh);
-            mx[qb] = row_max_log2<C::KB>(sc[qb], c_log2);
-        }
         order_scores_block<D, WAVES, QB>();
-        rescale_if_needed<C::DB, QB>(mx, oacc, m_run, l_run);
         softmax_pv<T, D, QB, C::KB, C::DB, C::KT>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
         order_pv_block<D, WAVES, QB>();
         stage_barrier();
@@ -504,26 +517,48 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     typedef std::integral_constant<bool, false> unmasked_t;
     typedef std::integral_constant<bool, true> masked_t;
 
-    // tiles [0, n_unmasked) need no mask, [n_unmasked, n_tiles) get it; the
-    // loops are unrolled by two so the score registers alternate
-    int j = 0;
-    for (; j + 2 <= n_unmasked; j += 2) {
-        step(unmasked_t(), j, sa, sb);
-        step(unmasked_t(), j + 1, sb, sa);
-    }
-    if (j < n_unmasked) {
-        step(unmasked_t(), j, sa, sb);
-        ++j;
+    // The last tile has no successor whose scores would be computed, so it
+    // runs a step of its own. Before it: tiles [0, n_unmasked) need no mask,
+    // the rest get it; the loops are unrolled by two so the score registers
+    // alternate.
+    auto last_step = [&](auto masked, int j, f32x16 (&sc)[QB][C::KB]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            if (decltype(masked)::value) mask_scores<C::KB, CAUSAL>(sc[qb], j * C::BN, qrow[qb], N, hh);
+        softmax_pv<T, D, QB, C::KB, C::DB, C::KT>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
+        order_pv_block<D, WAVES, QB>();
+    };
+    auto shift_scores = [&]() {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int kb = 0; kb < C::KB; ++kb) sa[qb][kb] = sb[qb][kb];
+    };
+    const int n_lead = n_tiles - 1;
+    const int n_u = n_unmasked < n_lead ? n_unmasked : n_lead;
+    int j = 0;
+    for (; j + 2 <= n_u; j += 2) {
+        step(unmasked_t(), j, sa, sb);
+        step(unmasked_t(), j + 1, sb, sa);
     }
-    for (; j + 2 <= n_tiles; j += 2) {
+    if (j < n_u) {
+        step(unmasked_t(), j, sa, sb);
+        ++j;
+        shift_scores();
+    }
+    for (; j + 2 <= n_lead; j += 2) {
         step(masked_t(), j, sa, sb);
         step(masked_t(), j + 1, sb, sa);
     }
-    if (j < n_tiles) step(masked_t(), j, sa, sb);
+    if (j < n_lead) {
+        step(masked_t(), j, sa, sb);
+        ++j;
+        shift_scores();
+    }
+    if (j < n_unmasked)
+        last_step(unmasked_t(), j, sa);
+    else
+        last_step(masked_t(), j, sa);
 
     // Epilogue: O = O_acc / l in the input type, lse = (m + log2 l) * ln 2.
 #pragma unroll
