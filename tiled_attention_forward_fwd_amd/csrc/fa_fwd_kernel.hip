@@ -316,19 +316,11 @@ __device__ __forceinline__ void exp_tile(const f32x16 (&s)[QB][KB], const float 
 // online softmax). The branch is wave-uniform.
 constexpr float kLaneSumBound = 4096.0f;
 
-// Then O^T += V^T P^T. V^T operand, lane l = 16g + i: dim 32*db + (l % 32);
-// elements 0..3 are keys 16t + 4h + [0,4), elements 4..7 keys
-// 16t + 8 + 4h + [0,4) (h = g/2), the key order of P^T. Each of the two
-// transposed reads has lane i address key (base + i/4), dims 4*(i%4) + [0,4)
-// of the group's 16 dims. Each V operand feeds QB MFMAs; the t-major order
-// consumes P in the order it is produced.
-template <typename T, int D, int QB, int KB, int DB, int KT>
-__device__ __forceinline__ void softmax_pv(const f32x16 (&s)[QB][KB], const uint16_t* __restrict__ vts,
-                                           f32x16 (&o)[QB][DB], float (&m_run)[QB],
-                                           float (&l_run)[QB], float c_log2, int lane, int hh)
+template <typename T, int QB, int KB, int DB, int KT>
+__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[QB][KB], f32x16 (&o)[QB][DB],
+                                             float (&m_run)[QB], float (&l_run)[QB], float c_log2,
+                                             typename Mma<T>::vec8 (&p)[QB][KT])
 {
-    typedef typename Mma<T>::vec8 vec8;
-    vec8 p[QB][KT];
     float rs[QB];
     exp_tile<T, QB, KB, KT>(s, m_run, c_log2, p, rs);
     bool bad = false;
@@ -349,7 +341,20 @@ __device__ __forceinline__ void softmax_pv(const f32x16 (&s)[QB][KB], const uint
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
+}
 
+// O^T += V^T P^T. V^T operand, lane l = 16g + i: dim 32*db + (l % 32);
+// elements 0..3 are keys 16t + 4h + [0,4), elements 4..7 keys
+// 16t + 8 + 4h + [0,4) (h = g/2), the key order of P^T. Each of the two
+// transposed reads has lane i address key (base + i/4), dims 4*(i%4) + [0,4)
+// of the group's 16 dims. Each V operand feeds QB MFMAs; the t-major order
+// consumes P in the order it is produced.
+template <typename T, int D, int QB, int DB, int KT>
+__device__ __forceinline__ void pv_tile(const typename Mma<T>::vec8 (&p)[QB][KT],
+                                        const uint16_t* __restrict__ vts, f32x16 (&o)[QB][DB], int lane,
+                                        int hh)
+{
+    typedef typename Mma<T>::vec8 vec8;
     const int gi = lane & 15, g1 = (lane >> 4) & 1;
     const int half = (gi & 1) * 4;
 #pragma unroll
@@ -373,6 +378,16 @@ __device__ __forceinline__ void softmax_pv(const f32x16 (&s)[QB][KB], const uint
             for (int qb = 0; qb < QB; ++qb) o[qb][db] = Mma<T>::run(a, p[qb][t], o[qb][db]);
         }
     }
+}
+
+template <typename T, int D, int QB, int KB, int DB, int KT>
+__device__ __forceinline__ void softmax_pv(const f32x16 (&s)[QB][KB], const uint16_t* __restrict__ vts,
+                                           f32x16 (&o)[QB][DB], float (&m_run)[QB],
+                                           float (&l_run)[QB], float c_log2, int lane, int hh)
+{
+    typename Mma<T>::vec8 p[QB][KT];
+    softmax_tile<T, QB, KB, DB, KT>(s, o, m_run, l_run, c_log2, p);
+    pv_tile<T, D, QB, DB, KT>(p, vts, o, lane, hh);
 }
 
 // Instruction order of a pipelined tile. The scores of the next tile are
@@ -412,26 +427,18 @@ __device__ __forceinline__ void order_pv_block()
     for (int i = 0; i < lead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
 }
 
-template <typename T, int D, bool CAUSAL, int WAVES, int QB>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
-                          amdgpu_waves_per_eu(2 / QB, 2 / QB)))
-void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                   T* __restrict__ o, float* __restrict__ lse, int N, int n_qt, float c_log2)
+// blockIdx -> (b*H + h, query tile). Hardware id i runs on XCD i % 8 and
+// the ids are dealt in order.
+//  * Non-causal (equal tiles): each XCD gets a contiguous range of
+//    head-major ids, so a head's query tiles share one L2.
+//  * Causal (a tile's work grows with its index): tile-major, longest tiles
+//    of all heads first, id i -> head i % BH. Greedy dispatch of
+//    longest-first work then keeps every XCD busy to the end, and when BH is
+//    a multiple of 8 every tile of a head still lands on one XCD.
+template <bool CAUSAL>
+__device__ __forceinline__ void workgroup_tile(int n_qt, uint32_t& bh, uint32_t& qt)
 {
-    typedef Cfg<D, WAVES, QB> C;
-    typedef typename Mma<T>::vec8 vec8;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * C::TILE];
-
-    // blockIdx -> (b*H + h, query tile). Hardware id i runs on XCD i % 8 and
-    // the ids are dealt in order.
-    //  * Non-causal (equal tiles): each XCD gets a contiguous range of
-    //    head-major ids, so a head's query tiles share one L2.
-    //  * Causal (a tile's work grows with its index): tile-major, longest
-    //    tiles of all heads first, id i -> head i % BH. Greedy dispatch of
-    //    longest-first work then keeps every XCD busy to the end, and when BH
-    //    is a multiple of 8 every tile of a head still lands on one XCD.
     const uint32_t nwg = gridDim.x, hw = blockIdx.x;
-    uint32_t bh, qt;
     if (CAUSAL) {
         const uint32_t n_bh = nwg / (uint32_t)n_qt;
         bh = hw % n_bh;
@@ -444,30 +451,80 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
         bh = logical / (uint32_t)n_qt;
         qt = logical % (uint32_t)n_qt;
     }
+}
+
+// Q fragments: B operand of S^T = K Q^T, query qrow[qb] = row0 + 32*qb +
+// (lane % 32), dims 16*ds + 8*hh + [0, 8). Rows past N are zero (their
+// outputs are not stored).
+template <typename T, int D, int QB, int DS>
+__device__ __forceinline__ void load_q(const T* __restrict__ qh, int row0, int N, int l32, int hh,
+                                       int (&qrow)[QB], typename Mma<T>::vec8 (&qf)[QB][DS])
+{
+    typedef typename Mma<T>::vec8 vec8;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        qrow[qb] = row0 + qb * 32 + l32;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (qrow[qb] < N) x = *(const u32x4*)(qh + (int64_t)qrow[qb] * D + ds * 16 + hh * 8);
+            qf[qb][ds] = as_vec8<vec8>(x);
+        }
+    }
+}
+
+// Epilogue: O = O_acc / l in the input type, lse = (m + log2 l) * ln 2.
+template <typename T, int D, int QB, int DB>
+__device__ __forceinline__ void store_outputs(const f32x16 (&oacc)[QB][DB], const float (&m_run)[QB],
+                                              const float (&l_run)[QB], const int (&qrow)[QB], int N,
+                                              T* __restrict__ oh, float* __restrict__ lseh, int hh)
+{
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const float l_tot = swap_halves_sum(l_run[qb]);
+        if (qrow[qb] < N) {
+            const float inv = 1.0f / l_tot;
+            T* orow = oh + (int64_t)qrow[qb] * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    T vals[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) vals[t] = to_elem<T>(oacc[qb][db][4 * g + t] * inv);
+                    u32x2 packed = __builtin_bit_cast(u32x2, vals);
+                    *(u32x2*)(orow + db * 32 + 8 * g + 4 * hh) = packed;
+                }
+            }
+            if (hh == 0) lseh[qrow[qb]] = (m_run[qb] + log2f(l_tot)) * 0.69314718055994531f;
+        }
+    }
+}
+
+template <typename T, int D, bool CAUSAL, int WAVES, int QB>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
+                          amdgpu_waves_per_eu(2 / QB, 2 / QB)))
+void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                   T* __restrict__ o, float* __restrict__ lse, int N, int n_qt, float c_log2)
+{
+    typedef Cfg<D, WAVES, QB> C;
+    typedef typename Mma<T>::vec8 vec8;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * C::TILE];
+
+    uint32_t bh, qt;
+    workgroup_tile<CAUSAL>(n_qt, bh, qt);
     const int q0 = (int)qt * C::BM;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
     const int64_t head_off = (int64_t)bh * N * D;
-    const T* qh = q + head_off;
     const T* kh = k + head_off;
     const T* vh = v + head_off;
 
-    // Q fragments: B operand of S^T = K Q^T, query qrow[qb], dims
-    // 16*ds + 8*hh + [0, 8). Rows past N are zero (their outputs are not stored).
     int qrow[QB];
     vec8 qf[QB][C::DS];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        qrow[qb] = q0 + (wave * QB + qb) * 32 + l32;
-#pragma unroll
-        for (int ds = 0; ds < C::DS; ++ds) {
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (qrow[qb] < N) x = *(const u32x4*)(qh + (int64_t)qrow[qb] * D + ds * 16 + hh * 8);
-            qf[qb][ds] = as_vec8<vec8>(x);
-        }
-    }
+    load_q<T, D, QB, C::DS>(q + head_off, q0 + wave * QB * 32, N, l32, hh, qrow, qf);
 
     const TileSpan span = tile_span(q0, C::BM, C::BN, N, CAUSAL);
     const int n_unmasked = (int)span.unmasked, n_tiles = (int)span.total;
@@ -501,17 +558,26 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 
     // One tile that has a successor: sc holds the scores of tile j; sn
     // receives those of tile j+1.
+    // Causal: the key tiles this wave's rows can see form the prefix
+    // [0, n_wave); in the diagonal tiles past it the wave only helps with the
+    // copies and the barriers.
+    const int n_wave = CAUSAL ? min(n_tiles, (q0 + (wave + 1) * QB * 32 - 1) / C::BN + 1) : n_tiles;
     auto step = [&](auto masked, int j, f32x16 (&sc)[QB][C::KB], f32x16 (&sn)[QB][C::KB]) {
+        constexpr bool M = decltype(masked)::value;
         if (j + 2 < n_tiles)
             issue_tile<D, WAVES, QB>(kbuf(j), krs, (j + 2) * C::BN, wave, lane_off);
         issue_tile<D, WAVES, QB>(vbuf(j + 1), vrs, (j + 1) * C::BN, wave, lane_off);
-        scores<T, D, QB, C::KB, C::DS>(sn, kbuf(j + 1), qf, l32, hh);
+        if (!M || j + 1 < n_wave) {
+            scores<T, D, QB, C::KB, C::DS>(sn, kbuf(j + 1), qf, l32, hh);
+            order_scores_block<D, WAVES, QB>();
+        }
+        if (!M || j < n_wave) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-            if (decltype(masked)::value) mask_scores<C::KB, CAUSAL>(sc[qb], j * C::BN, qrow[qb], N, hh);
-        order_scores_block<D, WAVES, QB>();
-        softmax_pv<T, D, QB, C::KB, C::DB, C::KT>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
-        order_pv_block<D, WAVES, QB>();
+            for (int qb = 0; qb < QB; ++qb)
+                if (M) mask_scores<C::KB, CAUSAL>(sc[qb], j * C::BN, qrow[qb], N, hh);
+            softmax_pv<T, D, QB, C::KB, C::DB, C::KT>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
+            order_pv_block<D, WAVES, QB>();
+        }
         stage_barrier();
     };
     typedef std::integral_constant<bool, false> unmasked_t;
@@ -522,11 +588,14 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     // the rest get it; the loops are unrolled by two so the score registers
     // alternate.
     auto last_step = [&](auto masked, int j, f32x16 (&sc)[QB][C::KB]) {
+        constexpr bool M = decltype(masked)::value;
+        if (!M || j < n_wave) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-            if (decltype(masked)::value) mask_scores<C::KB, CAUSAL>(sc[qb], j * C::BN, qrow[qb], N, hh);
-        softmax_pv<T, D, QB, C::KB, C::DB, C::KT>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
-        order_pv_block<D, WAVES, QB>();
+            for (int qb = 0; qb < QB; ++qb)
+                if (M) mask_scores<C::KB, CAUSAL>(sc[qb], j * C::BN, qrow[qb], N, hh);
+            softmax_pv<T, D, QB, C::KB, C::DB, C::KT>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
+            order_pv_block<D, WAVES, QB>();
+        }
     };
     auto shift_scores = [&]() {
 #pragma unroll
@@ -560,28 +629,7 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     else
         last_step(masked_t(), j, sa);
 
-    // Epilogue: O = O_acc / l in the input type, lse = (m + log2 l) * ln 2.
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float l_tot = swap_halves_sum(l_run[qb]);
-        if (qrow[qb] < N) {
-            const float inv = 1.0f / l_tot;
-            T* orow = o + head_off + (int64_t)qrow[qb] * D;
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    T vals[4];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) vals[t] = to_elem<T>(oacc[qb][db][4 * g + t] * inv);
-                    u32x2 packed = __builtin_bit_cast(u32x2, vals);
-                    *(u32x2*)(orow + db * 32 + 8 * g + 4 * hh) = packed;
-                }
-            }
-            if (hh == 0)
-                lse[(int64_t)bh * N + qrow[qb]] = (m_run[qb] + log2f(l_tot)) * 0.69314718055994531f;
-        }
-    }
+    store_outputs<T, D, QB, C::DB>(oacc, m_run, l_run, qrow, N, o + head_off, lse + (int64_t)bh * N, hh);
 }
 
 template <typename T, int D, bool CAUSAL, int WAVES, int QB>
