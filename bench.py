@@ -14,6 +14,10 @@ around the K timed steps). Per-kernel durations come from HIP events recorded
 around every launch on the launch stream; the roofline entry uses the
 non-causal kernel's average duration.
 
+After the timed region (never inside it) the default run also samples board power and clock
+with amd-smi while the step loops, times a plain hipBLASLt bf16 GEMM on random operands as
+context for the roofline, and times the fp64 oracle on the host (cpu_baseline).
+
 Other modes (used to collect counters; each runs a few launches only):
     --profile-kernels   a few launches of each headline kernel, nothing else
     --copy-calibration  a plain device-to-device copy of a known size
@@ -132,6 +136,31 @@ def power_and_clock(step, seconds=2.0):
     return result if "socket_power_w" in result else None
 
 
+def gemm_ceiling(seconds=1.0):
+    """Context for the roofline: TFLOP/s of a plain 8192^3 bf16 GEMM (hipBLASLt through
+    torch.matmul) on seeded N(0,1) operands, run back to back after the timed region. The
+    dense peak assumes 2.4 GHz; under sustained random-operand MFMA load the board power limit
+    holds the clock lower, and this measures what a vendor GEMM reaches under the same limit."""
+    import torch
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(11)
+    a = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+    ts = timed_launches(lambda: torch.matmul(a, b, out=c), 20, torch.cuda.current_stream())
+    med = statistics.median(ts)
+    return {"value": 2.0 * n ** 3 / (med * 1e-3) / 1e12, "unit": "TFLOP/s",
+            "what": "bf16 8192x8192x8192 GEMM, torch.matmul (hipBLASLt), N(0,1) operands, median of 20"}
+
+
 def cpu_baseline(cfg, q, k, v, stride):
     """The fp64 oracle on a bounded row sample of the workload (host cores)."""
     import oracle
@@ -150,8 +179,9 @@ def cpu_baseline(cfg, q, k, v, stride):
     # the same convention as the GPU: the causal pass counts half of the full rows' keys
     conv = 4.0 * cfg["B"] * cfg["H"] * len(rows) * N * cfg["d"] * 1.5
     return {"value": conv / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": (f"B={cfg['B']} H={cfg['H']} N={N} d={cfg['d']} {cfg['dtype']}: every "
-                       f"{stride}th query row ({len(rows)} rows per head, all heads), one "
+            "sample": (f"B={cfg['B']} H={cfg['H']} N={N} d={cfg['d']} {cfg['dtype']}: "
+                       + ("all query rows" if stride == 1 else f"every {stride}th query row")
+                       + f" ({len(rows)} rows per head, all heads), one "
                        f"non-causal and one causal pass, fp64 two-pass; {dt:.1f} s wall; FLOPs "
                        f"counted like the GPU step (causal = half the rows' full key count); "
                        f"exact visited-key FLOPs {flops / 1e9:.1f} G"),
@@ -325,11 +355,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--cpu-stride", type=int, default=2,
+    ap.add_argument("--cpu-stride", type=int, default=1,
                     help="oracle baseline evaluates every Nth query row")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-telemetry", dest="telemetry", action="store_false",
                     help="skip the amd-smi power/clock sample (taken outside the timed region)")
+    ap.add_argument("--no-gemm-ceiling", dest="gemm_ceiling", action="store_false",
+                    help="skip the hipBLASLt GEMM reference run (context for the roofline)")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -354,6 +386,10 @@ def main():
         return copy_calibration(args)
 
     out, (q, k, v) = headline(args)
+    if args.gemm_ceiling:
+        ceil = gemm_ceiling()
+        ceil["attention_noncausal_fraction"] = out["roofline"]["achieved"] / ceil["value"]
+        out["gemm_ceiling"] = ceil
     if args.sweep:
         out["sweep"] = sweep(args)
     if not args.no_cpu_baseline:
