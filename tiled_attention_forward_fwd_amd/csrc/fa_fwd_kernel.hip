@@ -37,8 +37,10 @@
 //     4e + j/4, so 16 lanes addressing 4 keys x 4 dim-quads receive 4 keys of
 //     one dim each: a transposed read of the row-major tile.
 //   * Software pipeline over key tiles, two K and two V buffers in LDS:
-//     iteration j computes the scores of tile j+1 on the matrix cores, then
-//     the exp2 work and P_j V_j of tile j; the copies of K_{j+2} and V_{j+1}
+//     iteration j computes the scores of tile j+1 on the matrix cores with
+//     the exp2 work of tile j interleaved between those MFMAs in program
+//     order (the two are independent, so the vector units run while the
+//     matrix core does), then P_j V_j; the copies of K_{j+2} and V_{j+1}
 //     are in flight meanwhile; one barrier per tile. The last tile runs
 //     without a successor, so no score MFMA is wasted. The copies go through
 //     a buffer descriptor bounded to the head, so the rows of a ragged last
@@ -252,6 +254,42 @@ __device__ __forceinline__ void scores(f32x16 (&s)[QB][KB], const uint16_t* __re
     }
 }
 
+// The scores of the next tile fused with the exp2 work of this one: after
+// each score MFMA come the exp2 / row-sum / convert of a few elements of the
+// current tile, so the vector units work while the matrix core runs instead
+// of after it (the two streams are independent). One 32-row block (QB = 1).
+template <typename T, int D, int KB, int DS, int KT>
+__device__ __forceinline__ void scores_with_exp(f32x16 (&sn)[1][KB], const uint16_t* __restrict__ ks,
+                                                const typename Mma<T>::vec8 (&qf)[1][DS], int l32, int hh,
+                                                const f32x16 (&sc)[1][KB], float m, float c_log2,
+                                                typename Mma<T>::vec8 (&p)[1][KT], float (&rs)[1])
+{
+    typedef typename Mma<T>::vec8 vec8;
+    constexpr int n_mfma = KB * DS, n_el = KB * 16, per = n_el / n_mfma;
+    static_assert(per * n_mfma == n_el && per % 2 == 0, "exp work per MFMA");
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sn[0][kb] = (f32x16){};
+    float acc = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int row = kb * 32 + l32;
+            const vec8 a = as_vec8<vec8>(*(const u32x4*)(ks + row * D + (((2 * ds + hh) ^ swz<D>(row)) * 8)));
+            sn[0][kb] = Mma<T>::run(a, qf[0][ds], sn[0][kb]);
+            const int i = ds * KB + kb;
+#pragma unroll
+            for (int e = i * per; e < (i + 1) * per; ++e) {
+                const int eb = e >> 4, r = e & 15;
+                const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][eb][r], c_log2, -m));
+                acc += x;
+                p[0][eb * 2 + (r >> 3)][r & 7] = to_elem<T>(x);
+            }
+        }
+    }
+    rs[0] = acc;
+}
+
 // Diagonal / ragged tiles: keys past N, and for causal attention keys after
 // the lane's query, get score -inf.
 template <int KB, bool CAUSAL>
@@ -317,12 +355,10 @@ __device__ __forceinline__ void exp_tile(const f32x16 (&s)[QB][KB], const float 
 constexpr float kLaneSumBound = 4096.0f;
 
 template <typename T, int QB, int KB, int DB, int KT>
-__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[QB][KB], f32x16 (&o)[QB][DB],
-                                             float (&m_run)[QB], float (&l_run)[QB], float c_log2,
-                                             typename Mma<T>::vec8 (&p)[QB][KT])
+__device__ __forceinline__ void softmax_finish(const f32x16 (&s)[QB][KB], f32x16 (&o)[QB][DB],
+                                               float (&m_run)[QB], float (&l_run)[QB], float c_log2,
+                                               typename Mma<T>::vec8 (&p)[QB][KT], float (&rs)[QB])
 {
-    float rs[QB];
-    exp_tile<T, QB, KB, KT>(s, m_run, c_log2, p, rs);
     bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) bad = bad || !(rs[qb] <= kLaneSumBound);
@@ -341,6 +377,16 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[QB][KB], f32x16 (
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
+}
+
+template <typename T, int QB, int KB, int DB, int KT>
+__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[QB][KB], f32x16 (&o)[QB][DB],
+                                             float (&m_run)[QB], float (&l_run)[QB], float c_log2,
+                                             typename Mma<T>::vec8 (&p)[QB][KT])
+{
+    float rs[QB];
+    exp_tile<T, QB, KB, KT>(s, m_run, c_log2, p, rs);
+    softmax_finish<T, QB, KB, DB, KT>(s, o, m_run, l_run, c_log2, p, rs);
 }
 
 // O^T += V^T P^T. V^T operand, lane l = 16g + i: dim 32*db + (l % 32);
@@ -392,9 +438,9 @@ __device__ __forceinline__ void softmax_pv(const f32x16 (&s)[QB][KB], const uint
 
 // Instruction order of a pipelined tile. The scores of the next tile are
 // issued first (MFMAs that need only K and Q), keeping their K operand reads
-// a few MFMAs ahead; then the P.V MFMAs follow their exp2/convert work with
-// their transposed V reads issued ahead. Vector instructions are left to the
-// scheduler.
+// a few MFMAs ahead; then the P.V MFMAs follow with their transposed V reads
+// issued ahead. Vector instructions keep their program order between the
+// MFMAs (scores_with_exp places them).
 template <int D, int WAVES, int QB>
 __device__ __forceinline__ void order_scores_block()
 {
@@ -558,6 +604,10 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 
     // One tile that has a successor: sc holds the scores of tile j; sn
     // receives those of tile j+1.
+    // The exp2 work of tile j is interleaved with the score MFMAs of tile j+1
+    // (scores_with_exp). The 4-wave d=128 shape keeps them apart: with its
+    // four copies per thread and tile it runs out of registers when fused.
+    constexpr bool kFuseExp = QB == 1 && !(D == 128 && WAVES == 4);
     // Causal: the key tiles this wave's rows can see form the prefix
     // [0, n_wave); in the diagonal tiles past it the wave only helps with the
     // copies and the barriers.
@@ -567,16 +617,34 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
         if (j + 2 < n_tiles)
             issue_tile<D, WAVES, QB>(kbuf(j), krs, (j + 2) * C::BN, wave, lane_off);
         issue_tile<D, WAVES, QB>(vbuf(j + 1), vrs, (j + 1) * C::BN, wave, lane_off);
-        if (!M || j + 1 < n_wave) {
-            scores<T, D, QB, C::KB, C::DS>(sn, kbuf(j + 1), qf, l32, hh);
-            order_scores_block<D, WAVES, QB>();
-        }
-        if (!M || j < n_wave) {
+        if (kFuseExp) {
+            if (!M || j < n_wave) {
+                if (M) mask_scores<C::KB, CAUSAL>(sc[0], j * C::BN, qrow[0], N, hh);
+                vec8 p[QB][C::KT];
+                float rs[QB];
+                if (!M || j + 1 < n_wave) {
+                    scores_with_exp<T, D, C::KB, C::DS, C::KT>(sn, kbuf(j + 1), qf, l32, hh, sc, m_run[0],
+                                                               c_log2, p, rs);
+                    order_scores_block<D, WAVES, QB>();
+                } else {
+                    exp_tile<T, QB, C::KB, C::KT>(sc, m_run, c_log2, p, rs);
+                }
+                softmax_finish<T, QB, C::KB, C::DB, C::KT>(sc, oacc, m_run, l_run, c_log2, p, rs);
+                pv_tile<T, D, QB, C::DB, C::KT>(p, vbuf(j), oacc, lane, hh);
+                order_pv_block<D, WAVES, QB>();
+            }
+        } else {
+            if (!M || j + 1 < n_wave) {
+                scores<T, D, QB, C::KB, C::DS>(sn, kbuf(j + 1), qf, l32, hh);
+                order_scores_block<D, WAVES, QB>();
+            }
+            if (!M || j < n_wave) {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-                if (M) mask_scores<C::KB, CAUSAL>(sc[qb], j * C::BN, qrow[qb], N, hh);
-            softmax_pv<T, D, QB, C::KB, C::DB, C::KT>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
-            order_pv_block<D, WAVES, QB>();
+                for (int qb = 0; qb < QB; ++qb)
+                    if (M) mask_scores<C::KB, CAUSAL>(sc[qb], j * C::BN, qrow[qb], N, hh);
+                softmax_pv<T, D, QB, C::KB, C::DB, C::KT>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
+                order_pv_block<D, WAVES, QB>();
+            }
         }
         stage_barrier();
     };
