@@ -31,9 +31,9 @@ def build(src=_SRC, out=_LIB, extra_flags=()):
 
 
 def _bind(lib):
-    fn = lib.fa_oracle_fwd
+    fn = lib.fa_oracle_fwd_qk
     fn.restype = ctypes.c_int
-    fn.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 4 + [
+    fn.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 5 + [
         ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     return lib
@@ -73,17 +73,20 @@ def _as_f32(x):
 def attention_fwd(q, k, v, causal, scale, rows=None, tile_n=0, nthreads=None, lib=None):
     """fp64 attention forward on the CPU.
 
-    q, k, v : ``[B, H, N, d]`` (torch or numpy; values already in the storage
-              dtype). ``scale`` is applied to Q.K^T before the softmax.
+    q       : ``[B, H, Nq, d]``; k, v: ``[B, H, Nk, d]`` (torch or numpy; values
+              already in the storage dtype). ``scale`` is applied to Q.K^T
+              before the softmax. A causal row i sees keys j <= i (top-left
+              alignment when Nq != Nk).
     rows    : optional sorted list of query rows to evaluate (all by default).
     tile_n  : 0 for the two-pass definition, > 0 for the online order.
     Returns ``(o, lse)`` as float64 numpy arrays of shape ``[B, H, R, d]`` and
-    ``[B, H, R]``, where ``R`` is ``len(rows)`` or ``N``; lse is natural-log.
+    ``[B, H, R]``, where ``R`` is ``len(rows)`` or ``Nq``; lse is natural-log.
     """
     lib = lib or load()
     qf, kf, vf = _as_f32(q), _as_f32(k), _as_f32(v)
     B, H, N, d = qf.shape
-    assert kf.shape == qf.shape and vf.shape == qf.shape
+    Nk = kf.shape[2]
+    assert kf.shape == (B, H, Nk, d) and vf.shape == kf.shape
     if rows is None:
         R, rows_arr, rows_ptr = N, None, None
     else:
@@ -91,7 +94,7 @@ def attention_fwd(q, k, v, causal, scale, rows=None, tile_n=0, nthreads=None, li
         R, rows_ptr = rows_arr.size, rows_arr.ctypes.data
     o = np.empty((B, H, R, d), dtype=np.float64)
     lse = np.empty((B, H, R), dtype=np.float64)
-    rc = lib.fa_oracle_fwd(qf.ctypes.data, kf.ctypes.data, vf.ctypes.data, B, H, N, d,
+    rc = lib.fa_oracle_fwd_qk(qf.ctypes.data, kf.ctypes.data, vf.ctypes.data, B, H, N, Nk, d,
                            1 if causal else 0, float(scale), rows_ptr,
                            0 if rows_arr is None else R, int(tile_n), o.ctypes.data,
                            lse.ctypes.data, int(nthreads or default_threads()))

@@ -5,7 +5,8 @@
  * bench's CPU-baseline leg may load this library. The GPU path never calls
  * it, includes it or shares code with it.
  *
- * What it computes, per batch b, head h and query row i (all independent):
+ * What it computes, per batch b, head h and query row i (all independent),
+ * for Nq query rows attending to Nk keys (Nq = Nk for self-attention):
  *
  *   s_j   = scale * sum_c q[b,h,i,c] * k[b,h,j,c]      for visible keys j
  *   O_i   = sum_j softmax(s)_j * v[b,h,j,:]
@@ -15,9 +16,14 @@
  * softmax is the one in "Programming an attention kernel in Triton",
  * section "Kernel 4: bringing it together, a self-attention kernel"; the
  * max subtraction before the exponential is from the same page, "Kernel 3:
- * fused softmax". A causal row i sees keys j <= i (the keep test of the
- * causal mask in "How to optimise a Triton FlashAttention-2 kernel step by
- * step with a profiler", Round 4, "Causal tile-skipping"). The per-row
+ * fused softmax". Every row sees keys 0..Nk-1, and a causal row i sees keys
+ * j <= i among them: the keep test of the causal mask in "How to optimise a
+ * Triton FlashAttention-2 kernel step by step with a profiler", Round 4,
+ * "Causal tile-skipping", compares absolute key and query positions and
+ * bounds keys by the key count, so with Nq != Nk the diagonal starts at the
+ * top-left corner (row i >= Nk sees every key). Mismatched query and key
+ * lengths are the shapes "Programming an attention kernel in Triton"
+ * validates in "Kernel 4". The per-row
  * logsumexp is stored in natural-log units (same page, Round 4, "exp2": the
  * kernel converts its base-2 state back because its tests compare against a
  * natural-log logsumexp).
@@ -47,7 +53,7 @@
 
 typedef struct {
     const float *q, *k, *v;
-    int64_t B, H, N, d;
+    int64_t B, H, Nq, Nk, d;
     int causal;
     double scale;
     const int64_t *rows; /* NULL: all rows 0..N-1 */
@@ -69,10 +75,11 @@ static double score(const float *qi, const float *kj, int64_t d, double scale)
     return scale * acc;
 }
 
-/* Number of keys row i may attend to: all N, or keys 0..i when causal. */
-static int64_t visible_keys(int64_t i, int64_t N, int causal)
+/* Number of keys row i may attend to: all Nk, or keys 0..min(i, Nk-1) when
+ * causal. */
+static int64_t visible_keys(int64_t i, int64_t Nk, int causal)
 {
-    return causal ? i + 1 : N;
+    return causal ? (i + 1 < Nk ? i + 1 : Nk) : Nk;
 }
 
 /* The plain definition, evaluated in two passes over the scores. */
@@ -145,8 +152,8 @@ static void row_online(const float *qi, const float *kh, const float *vh,
 static void *worker(void *arg)
 {
     job_t *job = (job_t *)arg;
-    const int64_t d = job->d, N = job->N;
-    int64_t scratch_n = job->tile_n > 0 ? job->tile_n : N;
+    const int64_t d = job->d, Nq = job->Nq, Nk = job->Nk;
+    int64_t scratch_n = job->tile_n > 0 ? job->tile_n : Nk;
     double *s = (double *)malloc(sizeof(double) * (size_t)scratch_n);
     if (!s) {
         pthread_mutex_lock(&job->lock);
@@ -164,12 +171,12 @@ static void *worker(void *arg)
         int64_t bh = item / chunks;
         int64_t r0 = (item % chunks) * ROWS_PER_ITEM;
         int64_t r1 = r0 + ROWS_PER_ITEM < job->n_rows ? r0 + ROWS_PER_ITEM : job->n_rows;
-        const float *qh = job->q + bh * N * d;
-        const float *kh = job->k + bh * N * d;
-        const float *vh = job->v + bh * N * d;
+        const float *qh = job->q + bh * Nq * d;
+        const float *kh = job->k + bh * Nk * d;
+        const float *vh = job->v + bh * Nk * d;
         for (int64_t r = r0; r < r1; ++r) {
             int64_t i = job->rows ? job->rows[r] : r;
-            int64_t nvis = visible_keys(i, N, job->causal);
+            int64_t nvis = visible_keys(i, Nk, job->causal);
             double *o_row = job->o + (bh * job->n_rows + r) * d;
             double *lse_out = job->lse + bh * job->n_rows + r;
             if (job->tile_n > 0)
@@ -184,28 +191,31 @@ static void *worker(void *arg)
 }
 
 /*
- * fa_oracle_fwd: O and lse for the rows listed in `rows` (NULL = every row)
- * of every (b, h).
- *   q, k, v : fp32, [B, H, N, d] contiguous (dtype-rounded values).
- *   o       : double, [B, H, R, d] with R = n_rows (or N when rows is NULL).
+ * fa_oracle_fwd_qk: O and lse for the query rows listed in `rows` (NULL =
+ * every row) of every (b, h).
+ *   q       : fp32, [B, H, Nq, d] contiguous (dtype-rounded values).
+ *   k, v    : fp32, [B, H, Nk, d] contiguous.
+ *   o       : double, [B, H, R, d] with R = n_rows (or Nq when rows is NULL).
  *   lse     : double, [B, H, R], natural log.
  *   tile_n  : 0 for the two-pass definition, > 0 for the online order.
  * Returns 0 on success, -1 on a bad argument, -2 when memory runs out.
  */
-int fa_oracle_fwd(const float *q, const float *k, const float *v, int64_t B, int64_t H,
-                  int64_t N, int64_t d, int causal, double scale, const int64_t *rows,
-                  int64_t n_rows, int64_t tile_n, double *o, double *lse, int nthreads)
+int fa_oracle_fwd_qk(const float *q, const float *k, const float *v, int64_t B, int64_t H,
+                     int64_t Nq, int64_t Nk, int64_t d, int causal, double scale,
+                     const int64_t *rows, int64_t n_rows, int64_t tile_n, double *o, double *lse,
+                     int nthreads)
 {
-    if (!q || !k || !v || !o || !lse || B < 1 || H < 1 || N < 1 || d < 1 || tile_n < 0)
+    if (!q || !k || !v || !o || !lse || B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1 ||
+        tile_n < 0)
         return -1;
     if (rows) {
         if (n_rows < 1)
             return -1;
         for (int64_t r = 0; r < n_rows; ++r)
-            if (rows[r] < 0 || rows[r] >= N)
+            if (rows[r] < 0 || rows[r] >= Nq)
                 return -1;
     } else {
-        n_rows = N;
+        n_rows = Nq;
     }
     if (nthreads < 1)
         nthreads = 1;
@@ -216,7 +226,8 @@ int fa_oracle_fwd(const float *q, const float *k, const float *v, int64_t B, int
     job.v = v;
     job.B = B;
     job.H = H;
-    job.N = N;
+    job.Nq = Nq;
+    job.Nk = Nk;
     job.d = d;
     job.causal = causal ? 1 : 0;
     job.scale = scale;
@@ -246,4 +257,13 @@ int fa_oracle_fwd(const float *q, const float *k, const float *v, int64_t B, int
     free(tids);
     pthread_mutex_destroy(&job.lock);
     return job.status;
+}
+
+/* fa_oracle_fwd: the self-attention case, Nq = Nk = N. */
+int fa_oracle_fwd(const float *q, const float *k, const float *v, int64_t B, int64_t H,
+                  int64_t N, int64_t d, int causal, double scale, const int64_t *rows,
+                  int64_t n_rows, int64_t tile_n, double *o, double *lse, int nthreads)
+{
+    return fa_oracle_fwd_qk(q, k, v, B, H, N, N, d, causal, scale, rows, n_rows, tile_n, o, lse,
+                            nthreads);
 }

@@ -23,6 +23,15 @@ What pins what:
   shift                adding a vector to every key shifts each row's scores
                        by a constant: O unchanged, lse shifted (also needs the
                        max subtraction at scores of several thousand)
+  qk_decimal_bruteforce  Nq != Nk: the definition at 50 digits, including the
+                       shapes "Programming an attention kernel in Triton"
+                       validates in "Kernel 4" (5 x 15 and 1 x 10 keys)
+  qk_torch_sdpa        Nq != Nk against the library routine, whose causal mask
+                       is also aligned at the top-left corner
+  qk_square_prefix     causal Nq < Nk: rows equal the first Nq rows of the
+                       square problem (the diagonal starts at the top left)
+  qk_rows_past_keys    causal Nq > Nk: every row i >= Nk - 1 sees all keys and
+                       equals the non-causal row
 """
 
 from decimal import Decimal, getcontext
@@ -48,9 +57,11 @@ def _close(a, b, rtol, what):
 
 
 def _decimal_attention(q, k, v, causal, scale):
-    """Attention of one head, [N, d] float inputs, evaluated in 50-digit decimal."""
+    """Attention of one head, q [Nq, d] and k, v [Nk, d] float inputs, evaluated in
+    50-digit decimal. A causal row i sees keys j <= i."""
     getcontext().prec = 50
     N, d = q.shape
+    Nk = k.shape[0]
     Q = [[Decimal(float(x)) for x in row] for row in q]
     K = [[Decimal(float(x)) for x in row] for row in k]
     V = [[Decimal(float(x)) for x in row] for row in v]
@@ -58,7 +69,7 @@ def _decimal_attention(q, k, v, causal, scale):
     o = np.zeros((N, d))
     lse = np.zeros(N)
     for i in range(N):
-        J = range(i + 1) if causal else range(N)
+        J = range(min(i + 1, Nk)) if causal else range(Nk)
         s = [sc * sum(Q[i][c] * K[j][c] for c in range(d)) for j in J]
         e = [x.exp() for x in s]
         den = sum(e)
@@ -236,6 +247,62 @@ def shift(fwd):
             _close(lse_s, lse + qu, 1e-12, f"shifted keys shift lse (|u|~{mag}) causal={causal}")
 
 
+def _qk_inputs(B, H, Nq, Nk, d, dtype, seed, q_scale=1.0):
+    q = make_qkv(B, H, Nq, d, dtype, seed, q_scale=q_scale)[0]
+    _, k, v = make_qkv(B, H, Nk, d, dtype, seed + 1)
+    return q, k, v
+
+
+def qk_decimal_bruteforce(fwd):
+    shapes = [(1, 1, 5, 15, 32), (1, 1, 1, 10, 64), (2, 1, 9, 4, 3), (1, 2, 3, 8, 4)]
+    for seed, (B, H, Nq, Nk, d) in enumerate(shapes):
+        q, k, v = _qk_inputs(B, H, Nq, Nk, d, "bf16", 300 + 2 * seed)
+        scale = float(np.float32(1.0 / np.sqrt(d)))
+        for causal in (False, True):
+            o, lse = fwd(q, k, v, causal, scale)
+            for b in range(B):
+                for h in range(H):
+                    od, ld = _decimal_attention(_f(q[b, h]), _f(k[b, h]), _f(v[b, h]), causal, scale)
+                    _close(o[b, h], od, 1e-14, f"decimal O Nq={Nq} Nk={Nk} causal={causal}")
+                    _close(lse[b, h], ld, 1e-14, f"decimal lse Nq={Nq} Nk={Nk} causal={causal}")
+
+
+def qk_torch_sdpa(fwd):
+    for B, H, Nq, Nk, d in [(2, 3, 37, 130, 16), (1, 2, 200, 70, 64), (3, 1, 1, 257, 32)]:
+        q, k, v = _qk_inputs(B, H, Nq, Nk, d, "fp16", 400 + Nq)
+        scale = float(np.float32(1.0 / np.sqrt(d)))
+        q64, k64, v64 = (t.to(torch.float64) for t in (q, k, v))
+        s = torch.matmul(q64, k64.transpose(-1, -2).contiguous()) * scale
+        for causal in (False, True):
+            o, lse = fwd(q, k, v, causal, scale)
+            ot = torch.nn.functional.scaled_dot_product_attention(q64, k64, v64, is_causal=causal,
+                                                                  scale=scale)
+            sm = s.masked_fill(torch.ones(Nq, Nk, dtype=torch.bool).triu(1), float("-inf")) if causal else s
+            _close(o, ot.numpy(), 1e-12, f"sdpa O Nq={Nq} Nk={Nk} causal={causal}")
+            _close(lse, torch.logsumexp(sm, dim=-1).numpy(), 1e-12, f"sdpa lse Nq={Nq} Nk={Nk} causal={causal}")
+
+
+def qk_square_prefix(fwd):
+    B, H, Nq, Nk, d = 2, 2, 50, 180, 32
+    q_sq, k, v = make_qkv(B, H, Nk, d, "bf16", 500)
+    q = q_sq[:, :, :Nq].contiguous()
+    o, lse = fwd(q, k, v, True, 0.2)
+    o_sq, lse_sq = fwd(q_sq, k, v, True, 0.2)
+    assert np.array_equal(o, o_sq[:, :, :Nq]) and np.array_equal(lse, lse_sq[:, :, :Nq]), \
+        "causal Nq < Nk differs from the first Nq rows of the square problem"
+
+
+def qk_rows_past_keys(fwd):
+    B, H, Nq, Nk, d = 1, 3, 120, 45, 64
+    q, k, v = _qk_inputs(B, H, Nq, Nk, d, "fp16", 600)
+    o_c, lse_c = fwd(q, k, v, True, 0.125)
+    o_n, lse_n = fwd(q, k, v, False, 0.125)
+    assert np.array_equal(o_c[:, :, Nk - 1:], o_n[:, :, Nk - 1:]), "causal rows >= Nk-1 differ from non-causal"
+    assert np.array_equal(lse_c[:, :, Nk - 1:], lse_n[:, :, Nk - 1:])
+    assert not np.array_equal(o_c[:, :, :Nk - 1], o_n[:, :, :Nk - 1])
+
+
 ALL_PINS = [decimal_bruteforce, torch_sdpa, keys_zero, causal_row0, causal_last_row,
             prefix_truncation, v_ones, v_identity, online_equals_twopass, linearity,
-            permutation, single_key, shift]
+            permutation, single_key, shift, qk_decimal_bruteforce, qk_torch_sdpa,
+            qk_square_prefix, qk_rows_past_keys]

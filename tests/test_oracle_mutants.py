@@ -16,9 +16,15 @@ MUTANTS = [
     ("score_sign", [("acc += (double)qi[c] * (double)kj[c];", "acc -= (double)qi[c] * (double)kj[c];")]),
     ("feature_index_reversed", [("(double)kj[c]", "(double)kj[d - 1 - c]")]),
     ("accumulate_in_float", [("double acc = 0.0;", "float acc = 0.0f;")]),
-    ("causal_excludes_diagonal", [("return causal ? i + 1 : N;", "return causal ? (i > 0 ? i : 1) : N;")]),
-    ("causal_sees_next_key", [("return causal ? i + 1 : N;", "return causal ? (i + 2 < N ? i + 2 : N) : N;")]),
-    ("causal_ignored", [("return causal ? i + 1 : N;", "return N;")]),
+    ("causal_excludes_diagonal", [("return causal ? (i + 1 < Nk ? i + 1 : Nk) : Nk;",
+                                   "return causal ? (i > 0 ? (i < Nk ? i : Nk) : 1) : Nk;")]),
+    ("causal_sees_next_key", [("return causal ? (i + 1 < Nk ? i + 1 : Nk) : Nk;",
+                               "return causal ? (i + 2 < Nk ? i + 2 : Nk) : Nk;")]),
+    ("causal_ignored", [("return causal ? (i + 1 < Nk ? i + 1 : Nk) : Nk;", "return Nk;")]),
+    ("causal_bottom_right", [("int64_t nvis = visible_keys(i, Nk, job->causal);",
+                              "int64_t nvis = visible_keys(i + (Nk > Nq ? Nk - Nq : 0), Nk, job->causal);")]),
+    ("keys_strided_by_query_length", [("const float *kh = job->k + bh * Nk * d;",
+                                       "const float *kh = job->k + bh * Nq * d;")]),
     ("lse_base2", [("*lse_out = m + log(l);", "*lse_out = m + log2(l);")]),
     ("lse_drops_max", [("*lse_out = m + log(l);", "*lse_out = log(l);")]),
     ("no_max_subtraction", [("s[j] = exp(s[j] - m);", "s[j] = exp(s[j]);"),
