@@ -14,11 +14,17 @@
  * registers (online softmax); O and lse are written once.
  *
  * Conventions shared by every entry point:
- *   - Tensors are dense, row-major [B, H, N, d] (q, k, v, o) and [B, H, N]
- *     (lse); the same N for queries and keys. No strides are taken.
+ *   - Tensors are dense, row-major: q and o [B, H, Nq, d], k and v
+ *     [B, H, Nk, d], lse [B, H, Nq]. The *_qk entry points take Nq and Nk
+ *     separately; the others are the self-attention case Nq = Nk = N. No
+ *     strides are taken.
  *   - Device pointers are HIP device memory owned by the caller; libfa
  *     allocates nothing, frees nothing and keeps no pointer after a call.
- *   - A causal query row i attends to keys j <= i.
+ *   - A causal query row i attends to keys j <= i (absolute positions, as the
+ *     keep test of "How to optimise a Triton FlashAttention-2 kernel step by
+ *     step with a profiler", Round 4, "Causal tile-skipping": with Nq != Nk
+ *     the diagonal starts at the top-left corner, and rows i >= Nk see every
+ *     key).
  *   - Functions return an fa_status; nothing is thrown across the ABI.
  *     Argument errors are reported before any HIP call is made.
  */
@@ -72,6 +78,22 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
            int N, int d, int causal, float scale, int dtype, void *stream);
 
 /*
+ * fa_fwd_qk -- attention forward pass with Nq query rows and Nk keys per head
+ * ("Programming an attention kernel in Triton", Kernel 4, validates such
+ * mismatched lengths, down to a single query).
+ *
+ *   q, o    : device, [B, H, Nq, d] contiguous, element type `dtype`, 16-byte
+ *             aligned (o is written, as in fa_fwd).
+ *   k, v    : device, [B, H, Nk, d] contiguous, element type `dtype`, 16-byte
+ *             aligned.
+ *   lse     : device, [B, H, Nq] fp32, 4-byte aligned (written).
+ *   Nq, Nk  : >= 1, with Nk*d*2 < 2^32 and Nq*d*2 < 2^32.
+ * Everything else as fa_fwd, which is fa_fwd_qk with Nq = Nk = N.
+ */
+int fa_fwd_qk(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+              int Nq, int Nk, int d, int causal, float scale, int dtype, void *stream);
+
+/*
  * fa_status_string -- human-readable text for a status code. For FA_ERR_HIP
  * and FA_ERR_INVALID_ARG it names the HIP error or the failed check of the
  * last failing call on the calling thread. The returned pointer stays valid
@@ -98,6 +120,12 @@ const char *fa_status_string(int status);
  */
 int fa_tile_counts(int64_t N, int block_m, int block_n, int causal, int64_t counts[4]);
 
+/* fa_tile_counts_qk -- the same for Nq query rows against Nk keys:
+ * counts[0] = ceil(Nq/block_m) * ceil(Nk/block_n); fa_tile_counts is the
+ * case Nq = Nk = N. */
+int fa_tile_counts_qk(int64_t Nq, int64_t Nk, int block_m, int block_n, int causal,
+                      int64_t counts[4]);
+
 /* Launch plan of fa_fwd for a problem (host only, no HIP call). */
 typedef struct {
     int block_m;            /* query rows per workgroup */
@@ -108,9 +136,13 @@ typedef struct {
     int64_t pairs_visited;  /* visited (query tile, key tile) pairs, all heads */
     double mfma_flops;      /* FLOPs the matrix cores execute: 4*d per (row, key)
                                of every visited tile pair, masked ones included */
-    double algo_flops;      /* 4*B*H*N*N*d, halved for causal (the pages' convention) */
+    double algo_flops;      /* 4*d per (query, key) pair of the visible region:
+                               4*B*H*Nq*Nk*d non-causal; causal counts the area
+                               below the diagonal, Nq*Nq/2 for Nq <= Nk and
+                               Nk*Nk/2 + (Nq-Nk)*Nk otherwise, so that Nq = Nk
+                               gives the pages' halved 4*B*H*N*N*d */
     double algo_bytes;      /* compulsory HBM bytes: q, k, v read and o written
-                               once (8*B*H*N*d for 2-byte types) plus lse */
+                               once (2 bytes each: 4*B*H*(Nq+Nk)*d) plus lse */
 } fa_plan_t;
 
 /*
@@ -119,6 +151,9 @@ typedef struct {
  * FA_ERR_UNSUPPORTED.
  */
 int fa_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t *plan);
+
+/* fa_plan_qk -- the plan of fa_fwd_qk; fa_plan is the case Nq = Nk = N. */
+int fa_plan_qk(int B, int H, int Nq, int Nk, int d, int causal, int dtype, fa_plan_t *plan);
 
 #ifdef __cplusplus
 }

@@ -160,3 +160,64 @@ def test_plan_picks_workgroup_shape(lib):
     assert (causal["block_m"], causal["threads"], causal["workgroups"]) == (128, 256, 2048)
     small = fa.fa_plan(2, 4, 1000, 64, 0, fa.FA_DTYPE_F16)
     assert (small["block_m"], small["threads"], small["workgroups"]) == (128, 256, 64)
+
+
+# ---- Nq != Nk (fa_fwd_qk, fa_tile_counts_qk, fa_plan_qk)
+
+def call_qk(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, Nq=16, Nk=48, d=64, causal=0,
+             scale=0.125, dtype=fa.FA_DTYPE_BF16, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_qk(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                        a["Nk"], a["d"], a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=-5), fa.FA_ERR_INVALID_ARG),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nk=1 << 24, d=128), fa.FA_ERR_INVALID_ARG),   # one key head >= 4 GiB
+    (dict(Nq=1 << 24, d=128), fa.FA_ERR_INVALID_ARG),   # one query head >= 4 GiB
+    (dict(o=P[1] + 32 * 64 * 2), fa.FA_ERR_INVALID_ARG),  # o inside k's 48 rows (not q's 16)
+    (dict(lse=P[3] + 16 * 64 * 2 - 4), fa.FA_ERR_INVALID_ARG),  # lse overlaps o's tail
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+])
+def test_fa_fwd_qk_rejects_before_any_hip_call(lib, kw, status):
+    assert call_qk(**kw) == status
+
+
+@pytest.mark.parametrize("Nq,Nk,bm,bn", [(5, 15, 128, 64), (1, 10, 128, 64), (1000, 300, 128, 64),
+                                         (300, 1000, 128, 64), (257, 64, 256, 64), (64, 4097, 128, 64),
+                                         (1, 16384, 128, 64), (700, 129, 64, 128)])
+def test_tile_counts_qk_cover_every_visible_key(lib, Nq, Nk, bm, bn):
+    n_qt, n_kt = -(-Nq // bm), -(-Nk // bn)
+    total, visited, unmasked, masked = fa.fa_tile_counts_qk(Nq, Nk, bm, bn, 0)
+    assert total == n_qt * n_kt and visited == total and masked == (n_qt if Nk % bn else 0)
+    # causal (top-left): a query tile needs key tiles up to min(last query, Nk - 1)
+    need = sum(min(min(Nq, (i + 1) * bm) - 1, Nk - 1) // bn + 1 for i in range(n_qt))
+    total, visited, unmasked, masked = fa.fa_tile_counts_qk(Nq, Nk, bm, bn, 1)
+    assert visited == need
+    # an unmasked pair is fully visible: inside [0, Nk) and at or below the tile's first query
+    fully_visible = sum(1 for i in range(n_qt) for j in range(n_kt)
+                        if (j + 1) * bn <= Nk and (j + 1) * bn - 1 <= i * bm)
+    assert unmasked <= fully_visible and unmasked + masked == visited
+
+
+def test_tile_counts_qk_square_case_is_fa_tile_counts(lib):
+    for N in (1, 100, 4096):
+        for causal in (0, 1):
+            assert fa.fa_tile_counts_qk(N, N, 128, 64, causal) == fa.fa_tile_counts(N, 128, 64, causal)
+
+
+def test_plan_qk_flops_and_bytes(lib):
+    B, H, d = 2, 3, 64
+    for Nq, Nk in [(100, 300), (300, 100), (4096, 4096), (1, 16384)]:
+        nc = fa.fa_plan_qk(B, H, Nq, Nk, d, 0, fa.FA_DTYPE_F16)
+        c = fa.fa_plan_qk(B, H, Nq, Nk, d, 1, fa.FA_DTYPE_F16)
+        assert nc["algo_flops"] == 4 * B * H * Nq * Nk * d
+        area = Nq * Nq / 2 if Nq <= Nk else Nk * Nk / 2 + (Nq - Nk) * Nk
+        assert c["algo_flops"] == 4 * B * H * area * d
+        assert nc["algo_bytes"] == 2 * B * H * d * (2 * Nq + 2 * Nk) + 4 * B * H * Nq
+        assert nc["workgroups"] == B * H * -(-Nq // nc["block_m"])
+    assert fa.fa_plan_qk(4, 8, 4096, 4096, 64, 1, 1) == fa.fa_plan(4, 8, 4096, 64, 1, 1)

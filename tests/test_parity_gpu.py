@@ -137,6 +137,49 @@ def test_scores_that_drift_along_the_keys(d, dtype, direction):
         check(q, k, v, causal, label=f"{direction} keys d{d} {dtype}")
 
 
+def qk_inputs(B, H, Nq, Nk, d, dtype, seed, q_scale=1.0):
+    q = make_qkv(B, H, Nq, d, dtype, seed, q_scale=q_scale)[0]
+    _, k, v = make_qkv(B, H, Nk, d, dtype, seed + 1)
+    return q, k, v
+
+
+# (B, H, Nq, Nk, d, dtype): the page's Kernel 4 shapes (5 x 15 keys at the
+# nearest supported head dim, and a single query against 10 keys), ragged
+# Nq < Nk and Nq > Nk, grids large enough for the 256-row workgroups, and a
+# decode-like single query against a long key sequence
+QK_CASES = [
+    (1, 1, 5, 15, 64, "fp16"), (1, 1, 1, 10, 64, "bf16"), (2, 3, 300, 1000, 128, "bf16"),
+    (2, 3, 1000, 300, 64, "fp16"), (8, 16, 1000, 2000, 128, "bf16"), (8, 16, 1100, 333, 64, "bf16"),
+    (1, 4, 1, 16384, 128, "bf16"), (3, 2, 129, 64, 128, "fp16"), (2, 2, 64, 4097, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", QK_CASES, ids=[f"B{c[0]}H{c[1]}q{c[2]}k{c[3]}d{c[4]}{c[5]}" for c in QK_CASES])
+def test_query_and_key_lengths_differ(case):
+    B, H, Nq, Nk, d, dtype = case
+    print(f"[case] Nq={Nq} Nk={Nk} d={d} {dtype}", flush=True)
+    q, k, v = qk_inputs(B, H, Nq, Nk, d, dtype, 60 + Nq % 50)
+    for causal in (False, True):
+        check(q, k, v, causal, label=f"Nq={Nq} Nk={Nk} d={d} {dtype}")
+
+
+def test_long_keys_sampled_rows():
+    # long-context shape with more keys than queries, in the launch the bench
+    # times for that grid; sampled rows against the oracle
+    q, k, v = qk_inputs(1, 32, 4096, 16384, 128, "bf16", 70)
+    rows = sample_rows(4096)
+    for causal in (False, True):
+        check(q, k, v, causal, rows=rows, label="Nq=4096 Nk=16384")
+
+
+def test_fewer_queries_equal_the_square_prefix_bitwise():
+    # causal rows of a query prefix attend exactly as in the square problem
+    q, k, v = make_qkv(2, 4, 1500, 128, "bf16", 71)
+    o_sq, l_sq = run(q, k, v, True)
+    o_pre, l_pre = run(q[:, :, :700].contiguous(), k, v, True)
+    assert torch.equal(o_pre, o_sq[:, :, :700]) and torch.equal(l_pre, l_sq[:, :, :700])
+
+
 def test_custom_scale():
     q, k, v = make_qkv(1, 2, 333, 64, "fp16", 42)
     for causal in (False, True):

@@ -7,9 +7,11 @@ functions here raise.
 
     o, lse = fwd(q, k, v, causal=False, scale=None)
 
-The C entry points are exposed under their own names (``fa_fwd``,
-``fa_status_string``, ``fa_tile_counts``, ``fa_plan``) for callers that
-manage their own buffers.
+q is ``[B, H, Nq, d]`` and k, v are ``[B, H, Nk, d]``; Nq may differ from Nk
+(a causal row i sees keys j <= i). The C entry points are exposed under
+their own names (``fa_fwd``, ``fa_fwd_qk``, ``fa_status_string``,
+``fa_tile_counts``, ``fa_tile_counts_qk``, ``fa_plan``, ``fa_plan_qk``) for
+callers that manage their own buffers.
 """
 
 import ctypes
@@ -23,7 +25,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1
 
 # Entry points declared in include/fa.h.
-EXPORTED = ("fa_fwd", "fa_status_string", "fa_tile_counts", "fa_plan")
+EXPORTED = ("fa_fwd", "fa_fwd_qk", "fa_status_string", "fa_tile_counts", "fa_tile_counts_qk",
+            "fa_plan", "fa_plan_qk")
 
 
 class FaPlan(ctypes.Structure):
@@ -58,13 +61,21 @@ def load_library(path=LIB_PATH):
     lib.fa_fwd.restype = ctypes.c_int
     lib.fa_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_fwd_qk.restype = ctypes.c_int
+    lib.fa_fwd_qk.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [ctypes.c_int]
     lib.fa_tile_counts.restype = ctypes.c_int
     lib.fa_tile_counts.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.POINTER(ctypes.c_int64)]
+    lib.fa_tile_counts_qk.restype = ctypes.c_int
+    lib.fa_tile_counts_qk.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]
     lib.fa_plan.restype = ctypes.c_int
     lib.fa_plan.argtypes = [ctypes.c_int] * 6 + [ctypes.POINTER(FaPlan)]
+    lib.fa_plan_qk.restype = ctypes.c_int
+    lib.fa_plan_qk.argtypes = [ctypes.c_int] * 7 + [ctypes.POINTER(FaPlan)]
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -83,6 +94,27 @@ def fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, stream):
     """Direct call of the C entry point with raw pointers (ints); returns the status."""
     return load_library().fa_fwd(q, k, v, o, lse, int(B), int(H), int(N), int(d), int(causal),
                                  float(scale), int(dtype), stream)
+
+
+def fa_fwd_qk(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, stream):
+    """Direct call of the C entry point with raw pointers (ints); returns the status."""
+    return load_library().fa_fwd_qk(q, k, v, o, lse, int(B), int(H), int(Nq), int(Nk), int(d),
+                                    int(causal), float(scale), int(dtype), stream)
+
+
+def fa_tile_counts_qk(Nq, Nk, block_m, block_n, causal):
+    """fa_tile_counts for Nq query rows against Nk keys."""
+    out = (ctypes.c_int64 * 4)()
+    _check(load_library().fa_tile_counts_qk(int(Nq), int(Nk), int(block_m), int(block_n),
+                                            int(causal), out))
+    return tuple(out)
+
+
+def fa_plan_qk(B, H, Nq, Nk, d, causal, dtype):
+    plan = FaPlan()
+    _check(load_library().fa_plan_qk(int(B), int(H), int(Nq), int(Nk), int(d), int(causal),
+                                     int(dtype), ctypes.byref(plan)))
+    return plan.as_dict()
 
 
 def fa_tile_counts(N, block_m, block_n, causal):
@@ -117,11 +149,12 @@ def default_scale(d):
 def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
     """Attention forward on the GPU: returns ``(o, lse)``.
 
-    q, k, v : CUDA (HIP) tensors ``[B, H, N, d]``, contiguous, float16 or
-              bfloat16, all the same shape and dtype.
+    q       : CUDA (HIP) tensor ``[B, H, Nq, d]``; k, v: ``[B, H, Nk, d]``;
+              contiguous, float16 or bfloat16, all the same dtype. A causal
+              row i sees keys j <= i.
     scale   : defaults to 1/sqrt(d) in fp32.
-    out/lse : optional preallocated outputs (``[B, H, N, d]`` dtype and
-              ``[B, H, N]`` float32).
+    out/lse : optional preallocated outputs (``[B, H, Nq, d]`` dtype and
+              ``[B, H, Nq]`` float32).
     The kernel is enqueued on ``stream`` (default: torch's current stream).
     """
     import torch
@@ -132,11 +165,12 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
             raise ValueError(f"{name} must be contiguous")
         if t.dim() != 4:
             raise ValueError(f"{name} must be [B, H, N, d]")
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k and v must have the same shape")
+    if k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3] or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k and v must have the same dtype")
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     code = dtype_code(q.dtype)
     if scale is None:
         scale = default_scale(d)
@@ -152,7 +186,7 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     with torch.cuda.device(q.device):
-        rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                    B, H, N, d, causal, scale, code, handle)
+        rc = fa_fwd_qk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                       B, H, N, Nk, d, causal, scale, code, handle)
     _check(rc)
     return out, lse

@@ -32,23 +32,31 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb)
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// Shape/dtype/scale checks shared by fa_fwd and fa_plan.
-int check_problem(int B, int H, int N, int d, int causal, int dtype)
+// Shape/dtype checks shared by the forward entry points and the plans.
+int check_problem(int B, int H, int Nq, int Nk, int d, int causal, int dtype)
 {
-    if (B < 1 || H < 1 || N < 1) return fail(FA_ERR_INVALID_ARG, "B, H and N must be >= 1");
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1)
+        return fail(FA_ERR_INVALID_ARG, "B, H and the sequence lengths must be >= 1");
     if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
     if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
         return fail(FA_ERR_INVALID_ARG, "dtype must be FA_DTYPE_F16 or FA_DTYPE_BF16");
     if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
     const int64_t bh = (int64_t)B * H;
-    const int64_t n_qt = ((int64_t)N + 127) / 128;  // the smallest workgroup tile
+    const int64_t n_qt = ((int64_t)Nq + 127) / 128;  // the smallest workgroup tile
     if (bh > INT32_MAX || bh * n_qt > (int64_t)UINT32_MAX)
-        return fail(FA_ERR_INVALID_ARG, "B*H*ceil(N/128) exceeds the grid limit");
-    const int64_t elems = bh * (int64_t)N * d;
-    if (elems > INT64_MAX / 4) return fail(FA_ERR_INVALID_ARG, "B*H*N*d too large");
-    if ((int64_t)N * d * 2 > (int64_t)UINT32_MAX)
+        return fail(FA_ERR_INVALID_ARG, "B*H*ceil(Nq/128) exceeds the grid limit");
+    const int64_t n_max = Nq > Nk ? Nq : Nk;
+    if (bh * n_max * d > INT64_MAX / 4) return fail(FA_ERR_INVALID_ARG, "B*H*N*d too large");
+    if ((int64_t)n_max * d * 2 > (int64_t)UINT32_MAX)
         return fail(FA_ERR_INVALID_ARG, "one head (N*d*2 bytes) must be below 4 GiB");
     return FA_OK;
+}
+
+// Causal visible area below the diagonal in the pages' convention (N*N/2
+// for a square problem).
+double causal_area(double Nq, double Nk)
+{
+    return Nq <= Nk ? 0.5 * Nq * Nq : 0.5 * Nk * Nk + (Nq - Nk) * Nk;
 }
 
 }  // namespace
@@ -69,14 +77,16 @@ const char* fa_status_string(int status)
     }
 }
 
-int fa_tile_counts(int64_t N, int block_m, int block_n, int causal, int64_t counts[4])
+int fa_tile_counts_qk(int64_t Nq, int64_t Nk, int block_m, int block_n, int causal,
+                      int64_t counts[4])
 {
-    if (!counts || N < 1 || block_m < 1 || block_n < 1)
-        return fail(FA_ERR_INVALID_ARG, "fa_tile_counts: N, block sizes must be >= 1, counts non-NULL");
-    const int64_t n_qt = (N + block_m - 1) / block_m, n_kt = (N + block_n - 1) / block_n;
+    if (!counts || Nq < 1 || Nk < 1 || block_m < 1 || block_n < 1)
+        return fail(FA_ERR_INVALID_ARG,
+                    "fa_tile_counts: lengths and block sizes must be >= 1, counts non-NULL");
+    const int64_t n_qt = (Nq + block_m - 1) / block_m, n_kt = (Nk + block_n - 1) / block_n;
     int64_t visited = 0, unmasked = 0;
     for (int64_t i = 0; i < n_qt; ++i) {
-        const fa::TileSpan s = fa::tile_span(i * block_m, block_m, block_n, N, causal != 0);
+        const fa::TileSpan s = fa::tile_span(i * block_m, block_m, block_n, Nq, Nk, causal != 0);
         visited += s.total;
         unmasked += s.unmasked;
     }
@@ -87,55 +97,72 @@ int fa_tile_counts(int64_t N, int block_m, int block_n, int causal, int64_t coun
     return FA_OK;
 }
 
-int fa_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t* plan)
+int fa_tile_counts(int64_t N, int block_m, int block_n, int causal, int64_t counts[4])
+{
+    return fa_tile_counts_qk(N, N, block_m, block_n, causal, counts);
+}
+
+int fa_plan_qk(int B, int H, int Nq, int Nk, int d, int causal, int dtype, fa_plan_t* plan)
 {
     if (!plan) return fail(FA_ERR_INVALID_ARG, "plan is NULL");
-    const int rc = check_problem(B, H, N, d, causal, dtype);
+    const int rc = check_problem(B, H, Nq, Nk, d, causal, dtype);
     if (rc != FA_OK) return rc;
-    const fa::Shape sh = fa::pick_shape(B, H, N, d, causal != 0);
+    const fa::Shape sh = fa::pick_shape(B, H, Nq, d, causal != 0);
     const int bm = sh.block_m, bn = fa::block_n(d);
     int64_t counts[4];
-    fa_tile_counts(N, bm, bn, causal, counts);
+    fa_tile_counts_qk(Nq, Nk, bm, bn, causal, counts);
     const int64_t bh = (int64_t)B * H;
     plan->block_m = bm;
     plan->block_n = bn;
     plan->threads = sh.threads;
     plan->lds_bytes = fa::lds_bytes(d);
-    plan->workgroups = bh * ((N + bm - 1) / bm);
+    plan->workgroups = bh * ((Nq + bm - 1) / bm);
     plan->pairs_visited = bh * counts[1];
     // every visited pair costs S = Q K^T and P V, masked pairs included
     plan->mfma_flops = 4.0 * d * (double)bm * bn * (double)plan->pairs_visited;
-    const double nn = (double)N * (double)N;
-    plan->algo_flops = 4.0 * (double)bh * nn * d * (causal ? 0.5 : 1.0);
-    plan->algo_bytes = 8.0 * (double)bh * N * d + 4.0 * (double)bh * N;
+    const double pairs = causal ? causal_area(Nq, Nk) : (double)Nq * (double)Nk;
+    plan->algo_flops = 4.0 * (double)bh * pairs * d;
+    plan->algo_bytes = 4.0 * (double)bh * ((double)Nq + Nk) * d + 4.0 * (double)bh * Nq;
     return FA_OK;
 }
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-           int d, int causal, float scale, int dtype, void* stream)
+int fa_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t* plan)
+{
+    return fa_plan_qk(B, H, N, N, d, causal, dtype, plan);
+}
+
+int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int Nq, int Nk, int d, int causal, float scale, int dtype, void* stream)
 {
     g_msg[0] = 0;
     if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "NULL tensor pointer");
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
         return fail(FA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
     if (!aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-    const int rc = check_problem(B, H, N, d, causal, dtype);
+    const int rc = check_problem(B, H, Nq, Nk, d, causal, dtype);
     if (rc != FA_OK) return rc;
     if (!(scale > 0.f) || !isfinite(scale))
         return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
-    const size_t tb = (size_t)B * H * N * d * 2, lb = (size_t)B * H * N * 4;
-    if (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb))
+    const size_t qb = (size_t)B * H * Nq * d * 2, kb = (size_t)B * H * Nk * d * 2;
+    const size_t lb = (size_t)B * H * Nq * 4;
+    if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb))
         return fail(FA_ERR_INVALID_ARG, "o overlaps q, k or v");
-    if (overlap(lse, lb, q, tb) || overlap(lse, lb, k, tb) || overlap(lse, lb, v, tb) ||
-        overlap(lse, lb, o, tb))
+    if (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) ||
+        overlap(lse, lb, o, qb))
         return fail(FA_ERR_INVALID_ARG, "lse overlaps q, k, v or o");
-    const hipError_t e = fa::launch_fwd(q, k, v, o, lse, B, H, N, d, causal != 0, scale,
+    const hipError_t e = fa::launch_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, scale,
                                         dtype == FA_DTYPE_BF16, (hipStream_t)stream);
     if (e != hipSuccess) {
         snprintf(g_msg, sizeof g_msg, "HIP error %d: %s", (int)e, hipGetErrorString(e));
         return FA_ERR_HIP;
     }
     return FA_OK;
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, int causal, float scale, int dtype, void* stream)
+{
+    return fa_fwd_qk(q, k, v, o, lse, B, H, N, N, d, causal, scale, dtype, stream);
 }
 
 }  // extern "C"

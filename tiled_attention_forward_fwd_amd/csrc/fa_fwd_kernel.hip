@@ -293,14 +293,14 @@ __device__ __forceinline__ void scores_with_exp(f32x16 (&sn)[1][KB], const uint1
 // Diagonal / ragged tiles: keys past N, and for causal attention keys after
 // the lane's query, get score -inf.
 template <int KB, bool CAUSAL>
-__device__ __forceinline__ void mask_scores(f32x16 (&s)[KB], int k0, int qrow, int N, int hh)
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[KB], int k0, int qrow, int n_keys, int hh)
 {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool hide = key >= N || (CAUSAL && key > qrow);
+            const bool hide = key >= n_keys || (CAUSAL && key > qrow);
             if (hide) s[kb][r] = -INFINITY;
         }
     }
@@ -503,7 +503,7 @@ __device__ __forceinline__ void workgroup_tile(int n_qt, uint32_t& bh, uint32_t&
 // (lane % 32), dims 16*ds + 8*hh + [0, 8). Rows past N are zero (their
 // outputs are not stored).
 template <typename T, int D, int QB, int DS>
-__device__ __forceinline__ void load_q(const T* __restrict__ qh, int row0, int N, int l32, int hh,
+__device__ __forceinline__ void load_q(const T* __restrict__ qh, int row0, int n_rows, int l32, int hh,
                                        int (&qrow)[QB], typename Mma<T>::vec8 (&qf)[QB][DS])
 {
     typedef typename Mma<T>::vec8 vec8;
@@ -513,7 +513,7 @@ __device__ __forceinline__ void load_q(const T* __restrict__ qh, int row0, int N
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
             u32x4 x = {0u, 0u, 0u, 0u};
-            if (qrow[qb] < N) x = *(const u32x4*)(qh + (int64_t)qrow[qb] * D + ds * 16 + hh * 8);
+            if (qrow[qb] < n_rows) x = *(const u32x4*)(qh + (int64_t)qrow[qb] * D + ds * 16 + hh * 8);
             qf[qb][ds] = as_vec8<vec8>(x);
         }
     }
@@ -522,13 +522,13 @@ __device__ __forceinline__ void load_q(const T* __restrict__ qh, int row0, int N
 // Epilogue: O = O_acc / l in the input type, lse = (m + log2 l) * ln 2.
 template <typename T, int D, int QB, int DB>
 __device__ __forceinline__ void store_outputs(const f32x16 (&oacc)[QB][DB], const float (&m_run)[QB],
-                                              const float (&l_run)[QB], const int (&qrow)[QB], int N,
+                                              const float (&l_run)[QB], const int (&qrow)[QB], int n_rows,
                                               T* __restrict__ oh, float* __restrict__ lseh, int hh)
 {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float l_tot = swap_halves_sum(l_run[qb]);
-        if (qrow[qb] < N) {
+        if (qrow[qb] < n_rows) {
             const float inv = 1.0f / l_tot;
             T* orow = oh + (int64_t)qrow[qb] * D;
 #pragma unroll
@@ -551,7 +551,7 @@ template <typename T, int D, bool CAUSAL, int WAVES, int QB>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
                           amdgpu_waves_per_eu(2 / QB, 2 / QB)))
 void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                   T* __restrict__ o, float* __restrict__ lse, int N, int n_qt, float c_log2)
+                   T* __restrict__ o, float* __restrict__ lse, int Nq, int Nk, int n_qt, float c_log2)
 {
     typedef Cfg<D, WAVES, QB> C;
     typedef typename Mma<T>::vec8 vec8;
@@ -564,15 +564,15 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
-    const int64_t head_off = (int64_t)bh * N * D;
-    const T* kh = k + head_off;
-    const T* vh = v + head_off;
+    const int64_t q_off = (int64_t)bh * Nq * D, kv_off = (int64_t)bh * Nk * D;
+    const T* kh = k + kv_off;
+    const T* vh = v + kv_off;
 
     int qrow[QB];
     vec8 qf[QB][C::DS];
-    load_q<T, D, QB, C::DS>(q + head_off, q0 + wave * QB * 32, N, l32, hh, qrow, qf);
+    load_q<T, D, QB, C::DS>(q + q_off, q0 + wave * QB * 32, Nq, l32, hh, qrow, qf);
 
-    const TileSpan span = tile_span(q0, C::BM, C::BN, N, CAUSAL);
+    const TileSpan span = tile_span(q0, C::BM, C::BN, Nq, Nk, CAUSAL);
     const int n_unmasked = (int)span.unmasked, n_tiles = (int)span.total;
 
     f32x16 oacc[QB][C::DB];
@@ -591,7 +591,7 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     auto kbuf = [&](int i) { return smem + (i & 1) * C::TILE; };
     auto vbuf = [&](int i) { return smem + (2 + (i & 1)) * C::TILE; };
 
-    const uint32_t head_bytes = (uint32_t)N * (D * 2);
+    const uint32_t head_bytes = (uint32_t)Nk * (D * 2);
     const rsrc_t krs = head_rsrc(kh, head_bytes), vrs = head_rsrc(vh, head_bytes);
     const uint32_t lane_off = tile_lane_offset<D>(wave, lane);
     issue_tile<D, WAVES, QB>(kbuf(0), krs, 0, wave, lane_off);
@@ -619,7 +619,7 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
         issue_tile<D, WAVES, QB>(vbuf(j + 1), vrs, (j + 1) * C::BN, wave, lane_off);
         if (kFuseExp) {
             if (!M || j < n_wave) {
-                if (M) mask_scores<C::KB, CAUSAL>(sc[0], j * C::BN, qrow[0], N, hh);
+                if (M) mask_scores<C::KB, CAUSAL>(sc[0], j * C::BN, qrow[0], Nk, hh);
                 vec8 p[QB][C::KT];
                 float rs[QB];
                 if (!M || j + 1 < n_wave) {
@@ -641,7 +641,7 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
             if (!M || j < n_wave) {
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
-                    if (M) mask_scores<C::KB, CAUSAL>(sc[qb], j * C::BN, qrow[qb], N, hh);
+                    if (M) mask_scores<C::KB, CAUSAL>(sc[qb], j * C::BN, qrow[qb], Nk, hh);
                 softmax_pv<T, D, QB, C::KB, C::DB, C::KT>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
                 order_pv_block<D, WAVES, QB>();
             }
@@ -660,7 +660,7 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
         if (!M || j < n_wave) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
-                if (M) mask_scores<C::KB, CAUSAL>(sc[qb], j * C::BN, qrow[qb], N, hh);
+                if (M) mask_scores<C::KB, CAUSAL>(sc[qb], j * C::BN, qrow[qb], Nk, hh);
             softmax_pv<T, D, QB, C::KB, C::DB, C::KT>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
             order_pv_block<D, WAVES, QB>();
         }
@@ -697,28 +697,28 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     else
         last_step(masked_t(), j, sa);
 
-    store_outputs<T, D, QB, C::DB>(oacc, m_run, l_run, qrow, N, o + head_off, lse + (int64_t)bh * N, hh);
+    store_outputs<T, D, QB, C::DB>(oacc, m_run, l_run, qrow, Nq, o + q_off, lse + (int64_t)bh * Nq, hh);
 }
 
 template <typename T, int D, bool CAUSAL, int WAVES, int QB>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                      int N, float scale, hipStream_t stream)
+                      int Nq, int Nk, float scale, hipStream_t stream)
 {
     typedef Cfg<D, WAVES, QB> C;
-    const int n_qt = (N + C::BM - 1) / C::BM;
+    const int n_qt = (Nq + C::BM - 1) / C::BM;
     const float c_log2 = scale * 1.4426950408889634f;
     dim3 grid((unsigned)((int64_t)n_qt * BH)), block(C::THREADS);
     hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, WAVES, QB>), grid, block, 0, stream, (const T*)q,
-                       (const T*)k, (const T*)v, (T*)o, lse, N, n_qt, c_log2);
+                       (const T*)k, (const T*)v, (T*)o, lse, Nq, Nk, n_qt, c_log2);
     return hipGetLastError();
 }
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_shape(const Shape& sh, const void* q, const void* k, const void* v, void* o,
-                        float* lse, int BH, int N, float scale, hipStream_t stream)
+                        float* lse, int BH, int Nq, int Nk, float scale, hipStream_t stream)
 {
-    if (sh.waves == 8) return launch_one<T, D, CAUSAL, 8, 1>(q, k, v, o, lse, BH, N, scale, stream);
-    return launch_one<T, D, CAUSAL, 4, 1>(q, k, v, o, lse, BH, N, scale, stream);
+    if (sh.waves == 8) return launch_one<T, D, CAUSAL, 8, 1>(q, k, v, o, lse, BH, Nq, Nk, scale, stream);
+    return launch_one<T, D, CAUSAL, 4, 1>(q, k, v, o, lse, BH, Nq, Nk, scale, stream);
 }
 
 }  // namespace
@@ -729,14 +729,14 @@ hipError_t launch_shape(const Shape& sh, const void* q, const void* k, const voi
 // holds; they are used for non-causal problems whose grid still gives every
 // CU a workgroup. Causal problems keep 128-row workgroups (less work above
 // the diagonal), as do small grids.
-Shape pick_shape(int B, int H, int N, int d, bool causal)
+Shape pick_shape(int B, int H, int n_queries, int d, bool causal)
 {
     (void)d;
     Shape sh;
     sh.waves = 4;
     sh.rows_per_wave = 32;
     if (!causal) {
-        const int64_t wg256 = (int64_t)B * H * ((N + 255) / 256);
+        const int64_t wg256 = (int64_t)B * H * ((n_queries + 255) / 256);
         if (wg256 >= 256) sh.waves = 8;
     }
     sh.block_m = sh.waves * sh.rows_per_wave;
@@ -748,14 +748,14 @@ int block_n(int) { return 64; }
 int lds_bytes(int d) { return 4 * 64 * d * 2; }
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                      int H, int N, int d, bool causal, float scale, bool bf16,
+                      int H, int Nq, int Nk, int d, bool causal, float scale, bool bf16,
                       hipStream_t stream)
 {
     const int BH = B * H;
-    const Shape sh = pick_shape(B, H, N, d, causal);
+    const Shape sh = pick_shape(B, H, Nq, d, causal);
 #define FA_DISPATCH(T, D)                                                                        \
-    return causal ? launch_shape<T, D, true>(sh, q, k, v, o, lse, BH, N, scale, stream)          \
-                  : launch_shape<T, D, false>(sh, q, k, v, o, lse, BH, N, scale, stream)
+    return causal ? launch_shape<T, D, true>(sh, q, k, v, o, lse, BH, Nq, Nk, scale, stream)     \
+                  : launch_shape<T, D, false>(sh, q, k, v, o, lse, BH, Nq, Nk, scale, stream)
     if (bf16) {
         if (d == 64) FA_DISPATCH(__bf16, 64);
         FA_DISPATCH(__bf16, 128);

@@ -15,13 +15,14 @@ struct Shape {
     int threads;
 };
 
-Shape pick_shape(int B, int H, int N, int d, bool causal);
+Shape pick_shape(int B, int H, int n_queries, int d, bool causal);
 int block_n(int d);
 int lds_bytes(int d);
 
-// Enqueues the forward kernel; arguments were validated by the caller.
+// Enqueues the forward kernel for Nq query rows against Nk keys per head;
+// arguments were validated by the caller.
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                      int H, int N, int d, bool causal, float scale, bool bf16,
+                      int H, int Nq, int Nk, int d, bool causal, float scale, bool bf16,
                       hipStream_t stream);
 
 }  // namespace fa
