@@ -94,6 +94,40 @@ int fa_fwd_qk(const void *q, const void *k, const void *v, void *o, float *lse, 
               int Nq, int Nk, int d, int causal, float scale, int dtype, void *stream);
 
 /*
+ * Split-key forward, for problems with too few query tiles to fill the GPU
+ * (KV-cache decode: a handful of query rows against a long key sequence).
+ * The key tiles each 128-row query tile visits are divided into n_splits
+ * contiguous chunks, one workgroup each; every chunk's normalised partial
+ * output (fp32) and logsumexp go to a caller-owned workspace, and a second
+ * kernel merges them exactly: lse = ln sum_s e^{lse_s},
+ * O = sum_s e^{lse_s - lse} O_s. That merge is the running-max and
+ * running-sum correction of the online softmax ("Programming an attention
+ * kernel in Triton", "The wall, named honestly") applied once per chunk.
+ * The profiler page names KV-cache decode as the next step ("Getting the
+ * kernel correct, then benchmarking it honestly", closing paragraph).
+ *
+ * fa_split_count -- a suggested n_splits (>= 1): enough workgroups to fill
+ *   the GPU about twice, at least 4 key tiles of 64 per chunk. Returns 0 on
+ *   invalid arguments.
+ * fa_split_workspace_bytes -- bytes of workspace fa_fwd_split_qk needs:
+ *   n_splits * B*H*Nq * (d + 1) * 4. Returns 0 on invalid arguments.
+ * fa_fwd_split_qk -- arguments as fa_fwd_qk, plus:
+ *   n_splits        : 1 .. ceil(Nk / 64).
+ *   workspace       : device, >= fa_split_workspace_bytes(...) bytes,
+ *                     16-byte aligned, owned by the caller, overlapping no
+ *                     tensor argument. Its contents on entry do not matter;
+ *                     on return it holds the partial results.
+ *   workspace_bytes : its size.
+ * Two kernels are enqueued on `stream`; calls that share a workspace must be
+ * ordered on one stream. O and lse equal those of fa_fwd_qk up to rounding.
+ */
+int fa_split_count(int B, int H, int Nq, int Nk, int d, int causal);
+int64_t fa_split_workspace_bytes(int B, int H, int Nq, int d, int n_splits);
+int fa_fwd_split_qk(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                    int H, int Nq, int Nk, int d, int causal, float scale, int dtype, int n_splits,
+                    void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * fa_status_string -- human-readable text for a status code. For FA_ERR_HIP
  * and FA_ERR_INVALID_ARG it names the HIP error or the failed check of the
  * last failing call on the calling thread. The returned pointer stays valid

@@ -180,6 +180,51 @@ def test_fewer_queries_equal_the_square_prefix_bitwise():
     assert torch.equal(o_pre, o_sq[:, :, :700]) and torch.equal(l_pre, l_sq[:, :, :700])
 
 
+def run_split(q, k, v, causal, splits, scale=None):
+    o, lse = fa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale, splits=splits)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+# (B, H, Nq, Nk, d, dtype, splits): KV-cache decode shapes and a small grid;
+# the largest split counts leave the early causal query tiles with empty chunks
+SPLIT_CASES = [
+    (1, 32, 1, 16384, 128, "bf16", None), (4, 8, 7, 4096, 64, "fp16", None),
+    (2, 2, 300, 1000, 128, "bf16", 2), (2, 2, 300, 1000, 128, "bf16", 3),
+    (2, 2, 300, 1000, 128, "bf16", 16), (1, 3, 33, 130, 64, "fp16", 3), (1, 1, 1, 1, 128, "bf16", 1),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[f"q{c[2]}k{c[3]}d{c[4]}s{c[6]}" for c in SPLIT_CASES])
+def test_split_keys_match_oracle(case):
+    B, H, Nq, Nk, d, dtype, splits = case
+    q, k, v = qk_inputs(B, H, Nq, Nk, d, dtype, 80 + Nq % 30)
+    if splits is None:
+        splits = fa.fa_split_count(B, H, Nq, Nk, d, 0)
+        assert splits > 1
+    print(f"[case] split Nq={Nq} Nk={Nk} d={d} splits={splits}", flush=True)
+    scale = fa.default_scale(d)
+    for causal in (False, True):
+        o, lse = run_split(q, k, v, causal, splits)
+        o64, l64 = oracle.attention_fwd(q, k, v, causal, scale)
+        err_o, err_l = errors(o, lse, o64, l64)
+        print(f"[parity] split {case} causal={causal} max|dO|={err_o:.3e} max rel dlse={err_l:.3e}", flush=True)
+        assert err_o <= TOL_O[q.dtype] and err_l <= TOL_LSE
+        if causal:
+            assert torch.equal(o[:, :, 0], v[:, :, 0])
+
+
+def test_split_rejects_a_small_workspace():
+    q, k, v = (t.cuda() for t in qk_inputs(1, 2, 4, 1024, 64, "bf16", 90))
+    need = fa.fa_split_workspace_bytes(1, 2, 4, 64, 4)
+    assert need == 4 * 1 * 2 * 4 * 65 * 4
+    small = torch.empty(need // 4 - 1, device="cuda", dtype=torch.float32)
+    with pytest.raises(ValueError):
+        fa.fwd(q, k, v, splits=4, workspace=small)
+    with pytest.raises(fa.FaError):
+        fa.fwd(q, k, v, splits=17)  # more chunks than the 16 key tiles
+
+
 def test_custom_scale():
     q, k, v = make_qkv(1, 2, 333, 64, "fp16", 42)
     for causal in (False, True):

@@ -25,8 +25,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1
 
 # Entry points declared in include/fa.h.
-EXPORTED = ("fa_fwd", "fa_fwd_qk", "fa_status_string", "fa_tile_counts", "fa_tile_counts_qk",
-            "fa_plan", "fa_plan_qk")
+EXPORTED = ("fa_fwd", "fa_fwd_qk", "fa_fwd_split_qk", "fa_split_count", "fa_split_workspace_bytes",
+            "fa_status_string", "fa_tile_counts", "fa_tile_counts_qk", "fa_plan", "fa_plan_qk")
 
 
 class FaPlan(ctypes.Structure):
@@ -64,6 +64,13 @@ def load_library(path=LIB_PATH):
     lib.fa_fwd_qk.restype = ctypes.c_int
     lib.fa_fwd_qk.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_fwd_split_qk.restype = ctypes.c_int
+    lib.fa_fwd_split_qk.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.fa_split_count.restype = ctypes.c_int
+    lib.fa_split_count.argtypes = [ctypes.c_int] * 6
+    lib.fa_split_workspace_bytes.restype = ctypes.c_int64
+    lib.fa_split_workspace_bytes.argtypes = [ctypes.c_int] * 5
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [ctypes.c_int]
     lib.fa_tile_counts.restype = ctypes.c_int
@@ -100,6 +107,22 @@ def fa_fwd_qk(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, stream):
     """Direct call of the C entry point with raw pointers (ints); returns the status."""
     return load_library().fa_fwd_qk(q, k, v, o, lse, int(B), int(H), int(Nq), int(Nk), int(d),
                                     int(causal), float(scale), int(dtype), stream)
+
+
+def fa_fwd_split_qk(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, n_splits, workspace,
+                    workspace_bytes, stream):
+    """Direct call of the C entry point with raw pointers (ints); returns the status."""
+    return load_library().fa_fwd_split_qk(q, k, v, o, lse, int(B), int(H), int(Nq), int(Nk), int(d),
+                                          int(causal), float(scale), int(dtype), int(n_splits),
+                                          workspace, int(workspace_bytes), stream)
+
+
+def fa_split_count(B, H, Nq, Nk, d, causal):
+    return int(load_library().fa_split_count(int(B), int(H), int(Nq), int(Nk), int(d), int(causal)))
+
+
+def fa_split_workspace_bytes(B, H, Nq, d, n_splits):
+    return int(load_library().fa_split_workspace_bytes(int(B), int(H), int(Nq), int(d), int(n_splits)))
 
 
 def fa_tile_counts_qk(Nq, Nk, block_m, block_n, causal):
@@ -146,7 +169,8 @@ def default_scale(d):
     return float(np.float32(1.0 / math.sqrt(d)))
 
 
-def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
+def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None, splits=None,
+        workspace=None):
     """Attention forward on the GPU: returns ``(o, lse)``.
 
     q       : CUDA (HIP) tensor ``[B, H, Nq, d]``; k, v: ``[B, H, Nk, d]``;
@@ -155,7 +179,11 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
     scale   : defaults to 1/sqrt(d) in fp32.
     out/lse : optional preallocated outputs (``[B, H, Nq, d]`` dtype and
               ``[B, H, Nq]`` float32).
-    The kernel is enqueued on ``stream`` (default: torch's current stream).
+    splits  : key chunks of the split-key path (``fa_fwd_split_qk``). None
+              takes ``fa_split_count``'s suggestion, which is 1 (the direct
+              path) unless the grid is too small to fill the GPU; the
+              workspace is then allocated with torch unless given.
+    The kernels are enqueued on ``stream`` (default: torch's current stream).
     """
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -185,8 +213,21 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if splits is None:
+        splits = fa_split_count(B, H, N, Nk, d, causal) or 1
     with torch.cuda.device(q.device):
-        rc = fa_fwd_qk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                       B, H, N, Nk, d, causal, scale, code, handle)
+        if splits == 1:
+            rc = fa_fwd_qk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                           B, H, N, Nk, d, causal, scale, code, handle)
+        else:
+            need = fa_split_workspace_bytes(B, H, N, d, splits)
+            if workspace is None:
+                workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
+            if workspace.numel() * workspace.element_size() < need or not workspace.is_contiguous():
+                raise ValueError(f"workspace must be a contiguous tensor of at least {need} bytes")
+            rc = fa_fwd_split_qk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr(), B, H, N, Nk, d, causal, scale, code, splits,
+                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                 handle)
     _check(rc)
     return out, lse

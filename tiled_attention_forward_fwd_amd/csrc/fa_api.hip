@@ -159,6 +159,67 @@ int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, 
     return FA_OK;
 }
 
+int fa_split_count(int B, int H, int Nq, int Nk, int d, int causal)
+{
+    if (check_problem(B, H, Nq, Nk, d, causal, FA_DTYPE_BF16) != FA_OK) return 0;
+    const int64_t rows = fa::split_rows_per_tile();
+    const int64_t wgs = (int64_t)B * H * (((int64_t)Nq + rows - 1) / rows);
+    const int64_t n_kt = ((int64_t)Nk + 63) / 64;
+    const int64_t target = 1024;  // two 4-wave workgroups per CU, twice over
+    int64_t s = (target + wgs - 1) / wgs;
+    const int64_t cap = n_kt / 4 > 1 ? n_kt / 4 : 1;
+    if (s > cap) s = cap;
+    return (int)(s < 1 ? 1 : s);
+}
+
+int64_t fa_split_workspace_bytes(int B, int H, int Nq, int d, int n_splits)
+{
+    if (B < 1 || H < 1 || Nq < 1 || (d != 64 && d != 128) || n_splits < 1) return 0;
+    return (int64_t)n_splits * B * H * Nq * (d + 1) * 4;
+}
+
+int fa_fwd_split_qk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                    int Nq, int Nk, int d, int causal, float scale, int dtype, int n_splits,
+                    void* workspace, int64_t workspace_bytes, void* stream)
+{
+    g_msg[0] = 0;
+    if (!q || !k || !v || !o || !lse || !workspace)
+        return fail(FA_ERR_INVALID_ARG, "NULL tensor or workspace pointer");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(workspace, 16))
+        return fail(FA_ERR_INVALID_ARG, "q, k, v, o and the workspace must be 16-byte aligned");
+    if (!aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    const int rc = check_problem(B, H, Nq, Nk, d, causal, dtype);
+    if (rc != FA_OK) return rc;
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (n_splits < 1 || n_splits > (Nk + 63) / 64)
+        return fail(FA_ERR_INVALID_ARG, "n_splits must be between 1 and ceil(Nk / 64)");
+    const int64_t need = fa_split_workspace_bytes(B, H, Nq, d, n_splits);
+    if ((int64_t)B * H * ((Nq + 127) / 128) * n_splits > (int64_t)UINT32_MAX)
+        return fail(FA_ERR_INVALID_ARG, "B*H*ceil(Nq/128)*n_splits exceeds the grid limit");
+    if (workspace_bytes < need) return fail(FA_ERR_INVALID_ARG, "workspace too small");
+    const size_t qb = (size_t)B * H * Nq * d * 2, kb = (size_t)B * H * Nk * d * 2;
+    const size_t lb = (size_t)B * H * Nq * 4, wb = (size_t)need;
+    if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb))
+        return fail(FA_ERR_INVALID_ARG, "o overlaps q, k or v");
+    if (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) ||
+        overlap(lse, lb, o, qb))
+        return fail(FA_ERR_INVALID_ARG, "lse overlaps q, k, v or o");
+    if (overlap(workspace, wb, q, qb) || overlap(workspace, wb, k, kb) ||
+        overlap(workspace, wb, v, kb) || overlap(workspace, wb, o, qb) ||
+        overlap(workspace, wb, lse, lb))
+        return fail(FA_ERR_INVALID_ARG, "the workspace overlaps a tensor argument");
+    const hipError_t e = fa::launch_fwd_split(q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, scale,
+                                              dtype == FA_DTYPE_BF16, n_splits, (float*)workspace,
+                                              (hipStream_t)stream);
+    if (e != hipSuccess) {
+        snprintf(g_msg, sizeof g_msg, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+        return FA_ERR_HIP;
+    }
+    return FA_OK;
+}
+
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
            int d, int causal, float scale, int dtype, void* stream)
 {

@@ -547,18 +547,98 @@ __device__ __forceinline__ void store_outputs(const f32x16 (&oacc)[QB][DB], cons
     }
 }
 
-template <typename T, int D, bool CAUSAL, int WAVES, int QB>
+// SPLIT: the key tiles of a query tile are divided into n_splits contiguous
+// chunks, one workgroup each, and every workgroup writes the normalised
+// partial output of its chunk (fp32) and the chunk's logsumexp to a
+// workspace instead of O and lse; fa_merge_kernel combines them. This is for
+// problems with too few query tiles to fill the GPU (KV-cache decode). A
+// chunk's partial result is exact for its keys, and the merge is the online
+// softmax identity applied once per chunk.
+// Partial result of a key chunk: O_chunk = O_acc / l in fp32 and the chunk's
+// logsumexp (natural log). A row that sees no key of the chunk gets O = 0
+// and lse = -inf, which gives it weight zero in the merge.
+template <int D, int QB, int DB>
+__device__ __forceinline__ void store_partials(const f32x16 (&oacc)[QB][DB], const float (&m_run)[QB],
+                                               const float (&l_run)[QB], const int (&qrow)[QB], int n_rows,
+                                               float* __restrict__ ws_o, float* __restrict__ ws_lse, int hh)
+{
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const float l_tot = swap_halves_sum(l_run[qb]);
+        if (qrow[qb] < n_rows) {
+            const bool seen = l_tot > 0.f;
+            const float inv = seen ? 1.0f / l_tot : 0.f;
+            float* orow = ws_o + (int64_t)qrow[qb] * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    typedef float f32x4 __attribute__((ext_vector_type(4)));
+                    f32x4 vals;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) vals[t] = oacc[qb][db][4 * g + t] * inv;
+                    *(f32x4*)(orow + db * 32 + 8 * g + 4 * hh) = vals;
+                }
+            }
+            if (hh == 0) ws_lse[qrow[qb]] = seen ? (m_run[qb] + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+        }
+    }
+}
+
+// Merge of the key chunks of a split launch, per query row:
+// lse = ln sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s. Each thread
+// owns 8 consecutive dims of one row; rows are [B*H*Nq] in order.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__ ws_o,
+                                                       const float* __restrict__ ws_lse, T* __restrict__ o,
+                                                       float* __restrict__ lse, int64_t n_rows, int n_splits)
+{
+    constexpr int TPR = D / 8;  // threads per row
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = t / TPR;
+    const int c0 = (int)(t % TPR) * 8;
+    if (row >= n_rows) return;
+    float mx = -INFINITY;
+    for (int sp = 0; sp < n_splits; ++sp) mx = fmaxf(mx, ws_lse[(int64_t)sp * n_rows + row]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (mx > -INFINITY) {
+        for (int sp = 0; sp < n_splits; ++sp) {
+            const float w = expf(ws_lse[(int64_t)sp * n_rows + row] - mx);
+            const float* src = ws_o + ((int64_t)sp * n_rows + row) * D + c0;
+            wsum += w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += w * src[e];
+        }
+    }
+    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+    T vals[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vals[e] = to_elem<T>(acc[e] * inv);
+    *(u32x4*)(o + row * D + c0) = __builtin_bit_cast(u32x4, vals);
+    if (c0 == 0) lse[row] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
+}
+
+template <typename T, int D, bool CAUSAL, int WAVES, int QB, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
                           amdgpu_waves_per_eu(2 / QB, 2 / QB)))
 void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                   T* __restrict__ o, float* __restrict__ lse, int Nq, int Nk, int n_qt, float c_log2)
+                   T* __restrict__ o, float* __restrict__ lse, int Nq, int Nk, int n_qt, float c_log2,
+                   int n_splits, float* __restrict__ ws_o, float* __restrict__ ws_lse)
 {
     typedef Cfg<D, WAVES, QB> C;
     typedef typename Mma<T>::vec8 vec8;
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * C::TILE];
 
-    uint32_t bh, qt;
-    workgroup_tile<CAUSAL>(n_qt, bh, qt);
+    uint32_t bh, qt, split = 0;
+    if (SPLIT) {
+        const uint32_t rest = blockIdx.x / (uint32_t)n_splits;
+        split = blockIdx.x % (uint32_t)n_splits;
+        bh = rest / (uint32_t)n_qt;
+        qt = rest % (uint32_t)n_qt;
+    } else {
+        workgroup_tile<CAUSAL>(n_qt, bh, qt);
+    }
     const int q0 = (int)qt * C::BM;
 
     const int tid = threadIdx.x;
@@ -574,6 +654,13 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 
     const TileSpan span = tile_span(q0, C::BM, C::BN, Nq, Nk, CAUSAL);
     const int n_unmasked = (int)span.unmasked, n_tiles = (int)span.total;
+    // key tiles [jb, je) of this workgroup: all of them, or one chunk
+    int jb = 0, je = n_tiles;
+    if (SPLIT) {
+        const int per = (n_tiles + n_splits - 1) / n_splits;
+        jb = min(n_tiles, (int)split * per);
+        je = min(n_tiles, jb + per);
+    }
 
     f32x16 oacc[QB][C::DB];
     float m_run[QB], l_run[QB];
@@ -594,13 +681,28 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     const uint32_t head_bytes = (uint32_t)Nk * (D * 2);
     const rsrc_t krs = head_rsrc(kh, head_bytes), vrs = head_rsrc(vh, head_bytes);
     const uint32_t lane_off = tile_lane_offset<D>(wave, lane);
-    issue_tile<D, WAVES, QB>(kbuf(0), krs, 0, wave, lane_off);
-    issue_tile<D, WAVES, QB>(vbuf(0), vrs, 0, wave, lane_off);
-    if (n_tiles > 1) issue_tile<D, WAVES, QB>(kbuf(1), krs, C::BN, wave, lane_off);
-    stage_barrier();
+    // Causal: the key tiles this wave's rows can see form the prefix
+    // [0, n_wave); in the diagonal tiles past it the wave only helps with the
+    // copies and the barriers. In a split launch a wave whose rows all lie
+    // past Nq computes nothing either.
+    int n_wave = CAUSAL ? min(je, (q0 + (wave + 1) * QB * 32 - 1) / C::BN + 1) : je;
+    if (SPLIT && q0 + wave * QB * 32 >= Nq) n_wave = jb;
+
     f32x16 sa[QB][C::KB], sb[QB][C::KB];
-    scores<T, D, QB, C::KB, C::DS>(sa, kbuf(0), qf, l32, hh);
-    stage_barrier();  // K_0's buffer is refilled in the first iteration
+    if (SPLIT && jb == je) {
+        // an empty chunk: no key of this query tile falls in it
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < C::KB; ++kb) sa[qb][kb] = (f32x16){};
+    } else {
+        issue_tile<D, WAVES, QB>(kbuf(jb), krs, jb * C::BN, wave, lane_off);
+        issue_tile<D, WAVES, QB>(vbuf(jb), vrs, jb * C::BN, wave, lane_off);
+        if (jb + 1 < je) issue_tile<D, WAVES, QB>(kbuf(jb + 1), krs, (jb + 1) * C::BN, wave, lane_off);
+        stage_barrier();
+        if (!SPLIT || jb < n_wave) scores<T, D, QB, C::KB, C::DS>(sa, kbuf(jb), qf, l32, hh);
+        stage_barrier();  // K_jb's buffer is refilled in the first iteration
+    }
 
     // One tile that has a successor: sc holds the scores of tile j; sn
     // receives those of tile j+1.
@@ -608,21 +710,19 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     // (scores_with_exp). The 4-wave d=128 shape keeps them apart: with its
     // four copies per thread and tile it runs out of registers when fused.
     constexpr bool kFuseExp = QB == 1 && !(D == 128 && WAVES == 4);
-    // Causal: the key tiles this wave's rows can see form the prefix
-    // [0, n_wave); in the diagonal tiles past it the wave only helps with the
-    // copies and the barriers.
-    const int n_wave = CAUSAL ? min(n_tiles, (q0 + (wave + 1) * QB * 32 - 1) / C::BN + 1) : n_tiles;
     auto step = [&](auto masked, int j, f32x16 (&sc)[QB][C::KB], f32x16 (&sn)[QB][C::KB]) {
-        constexpr bool M = decltype(masked)::value;
-        if (j + 2 < n_tiles)
+        // M: the tile gets the mask; G: per-wave limits apply (masked tiles,
+        // and every tile of a split launch)
+        constexpr bool M = decltype(masked)::value, G = M || SPLIT;
+        if (j + 2 < je)
             issue_tile<D, WAVES, QB>(kbuf(j), krs, (j + 2) * C::BN, wave, lane_off);
         issue_tile<D, WAVES, QB>(vbuf(j + 1), vrs, (j + 1) * C::BN, wave, lane_off);
         if (kFuseExp) {
-            if (!M || j < n_wave) {
+            if (!G || j < n_wave) {
                 if (M) mask_scores<C::KB, CAUSAL>(sc[0], j * C::BN, qrow[0], Nk, hh);
                 vec8 p[QB][C::KT];
                 float rs[QB];
-                if (!M || j + 1 < n_wave) {
+                if (!G || j + 1 < n_wave) {
                     scores_with_exp<T, D, C::KB, C::DS, C::KT>(sn, kbuf(j + 1), qf, l32, hh, sc, m_run[0],
                                                                c_log2, p, rs);
                     order_scores_block<D, WAVES, QB>();
@@ -634,11 +734,11 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
                 order_pv_block<D, WAVES, QB>();
             }
         } else {
-            if (!M || j + 1 < n_wave) {
+            if (!G || j + 1 < n_wave) {
                 scores<T, D, QB, C::KB, C::DS>(sn, kbuf(j + 1), qf, l32, hh);
                 order_scores_block<D, WAVES, QB>();
             }
-            if (!M || j < n_wave) {
+            if (!G || j < n_wave) {
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
                     if (M) mask_scores<C::KB, CAUSAL>(sc[qb], j * C::BN, qrow[qb], Nk, hh);
@@ -656,8 +756,8 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     // the rest get it; the loops are unrolled by two so the score registers
     // alternate.
     auto last_step = [&](auto masked, int j, f32x16 (&sc)[QB][C::KB]) {
-        constexpr bool M = decltype(masked)::value;
-        if (!M || j < n_wave) {
+        constexpr bool M = decltype(masked)::value, G = M || SPLIT;
+        if (!G || j < n_wave) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
                 if (M) mask_scores<C::KB, CAUSAL>(sc[qb], j * C::BN, qrow[qb], Nk, hh);
@@ -671,9 +771,9 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 #pragma unroll
             for (int kb = 0; kb < C::KB; ++kb) sa[qb][kb] = sb[qb][kb];
     };
-    const int n_lead = n_tiles - 1;
+    const int n_lead = je - 1;
     const int n_u = n_unmasked < n_lead ? n_unmasked : n_lead;
-    int j = 0;
+    int j = jb;
     for (; j + 2 <= n_u; j += 2) {
         step(unmasked_t(), j, sa, sb);
         step(unmasked_t(), j + 1, sb, sa);
@@ -692,12 +792,19 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
         ++j;
         shift_scores();
     }
-    if (j < n_unmasked)
-        last_step(unmasked_t(), j, sa);
-    else
-        last_step(masked_t(), j, sa);
+    if (j < je) {
+        if (j < n_unmasked)
+            last_step(unmasked_t(), j, sa);
+        else
+            last_step(masked_t(), j, sa);
+    }
 
-    store_outputs<T, D, QB, C::DB>(oacc, m_run, l_run, qrow, Nq, o + q_off, lse + (int64_t)bh * Nq, hh);
+    if (SPLIT) {
+        const int64_t slot = ((int64_t)split * (gridDim.x / ((uint32_t)n_splits * (uint32_t)n_qt)) + bh) * Nq;
+        store_partials<D, QB, C::DB>(oacc, m_run, l_run, qrow, Nq, ws_o + slot * D, ws_lse + slot, hh);
+    } else {
+        store_outputs<T, D, QB, C::DB>(oacc, m_run, l_run, qrow, Nq, o + q_off, lse + (int64_t)bh * Nq, hh);
+    }
 }
 
 template <typename T, int D, bool CAUSAL, int WAVES, int QB>
@@ -708,8 +815,35 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o, floa
     const int n_qt = (Nq + C::BM - 1) / C::BM;
     const float c_log2 = scale * 1.4426950408889634f;
     dim3 grid((unsigned)((int64_t)n_qt * BH)), block(C::THREADS);
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, WAVES, QB>), grid, block, 0, stream, (const T*)q,
-                       (const T*)k, (const T*)v, (T*)o, lse, Nq, Nk, n_qt, c_log2);
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, WAVES, QB, false>), grid, block, 0, stream,
+                       (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, Nq, Nk, n_qt, c_log2, 1,
+                       (float*)nullptr, (float*)nullptr);
+    return hipGetLastError();
+}
+
+// Split launch (4-wave, 128-row workgroups) followed by the merge; the
+// workspace holds n_splits * B*H*Nq partial rows of D floats and then as many
+// logsumexps.
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_split(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
+                        int Nq, int Nk, float scale, int n_splits, float* ws, hipStream_t stream)
+{
+    typedef Cfg<D, 4, 1> C;
+    const int n_qt = (Nq + C::BM - 1) / C::BM;
+    const float c_log2 = scale * 1.4426950408889634f;
+    const int64_t n_rows = (int64_t)BH * Nq;
+    float* ws_o = ws;
+    float* ws_lse = ws + (int64_t)n_splits * n_rows * D;
+    dim3 grid((unsigned)((int64_t)n_qt * BH * n_splits)), block(C::THREADS);
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, 4, 1, true>), grid, block, 0, stream, (const T*)q,
+                       (const T*)k, (const T*)v, (T*)o, lse, Nq, Nk, n_qt, c_log2, n_splits, ws_o,
+                       ws_lse);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t threads = n_rows * (D / 8);
+    dim3 mgrid((unsigned)((threads + 255) / 256)), mblock(256);
+    hipLaunchKernelGGL((fa_merge_kernel<T, D>), mgrid, mblock, 0, stream, (const float*)ws_o,
+                       (const float*)ws_lse, (T*)o, lse, n_rows, n_splits);
     return hipGetLastError();
 }
 
@@ -746,6 +880,27 @@ Shape pick_shape(int B, int H, int n_queries, int d, bool causal)
 
 int block_n(int) { return 64; }
 int lds_bytes(int d) { return 4 * 64 * d * 2; }
+
+hipError_t launch_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                            int H, int Nq, int Nk, int d, bool causal, float scale, bool bf16,
+                            int n_splits, float* workspace, hipStream_t stream)
+{
+    const int BH = B * H;
+#define FA_DISPATCH(T, D)                                                                         \
+    return causal ? launch_split<T, D, true>(q, k, v, o, lse, BH, Nq, Nk, scale, n_splits, workspace, \
+                                             stream)                                              \
+                  : launch_split<T, D, false>(q, k, v, o, lse, BH, Nq, Nk, scale, n_splits, workspace, \
+                                              stream)
+    if (bf16) {
+        if (d == 64) FA_DISPATCH(__bf16, 64);
+        FA_DISPATCH(__bf16, 128);
+    }
+    if (d == 64) FA_DISPATCH(_Float16, 64);
+    FA_DISPATCH(_Float16, 128);
+#undef FA_DISPATCH
+}
+
+int split_rows_per_tile() { return 128; }
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                       int H, int Nq, int Nk, int d, bool causal, float scale, bool bf16,

@@ -25,4 +25,13 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
                       int H, int Nq, int Nk, int d, bool causal, float scale, bool bf16,
                       hipStream_t stream);
 
+// Split launch for few query tiles (KV-cache decode): the key tiles of each
+// 128-row query tile are divided into n_splits chunks whose partial results
+// go to `workspace` (n_splits * B*H*Nq * (d + 1) floats) and are then merged
+// into o and lse; arguments were validated by the caller.
+hipError_t launch_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                            int H, int Nq, int Nk, int d, bool causal, float scale, bool bf16,
+                            int n_splits, float* workspace, hipStream_t stream);
+int split_rows_per_tile();
+
 }  // namespace fa
