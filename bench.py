@@ -298,24 +298,39 @@ def sweep(args):
         dict(B=4, H=16, N=4096, d=128, dtype="bf16", seed=7, flags=(0, 1)),
         dict(B=1, H=32, N=16384, d=128, dtype="bf16", seed=8, flags=(1,)),
         dict(B=1, H=32, N=16384, d=128, dtype="bf16", seed=9, q_scale=4.0, flags=(1,)),
+        # fewer queries than keys: KV-cache decode (split-key path) and a long-key prefill
+        dict(B=1, H=32, Nq=1, N=16384, d=128, dtype="bf16", seed=10, flags=(0,)),
+        dict(B=4, H=32, Nq=1, N=16384, d=128, dtype="bf16", seed=11, flags=(0,)),
+        dict(B=1, H=32, Nq=4096, N=16384, d=128, dtype="bf16", seed=12, flags=(1,)),
     ]
     for cfg in configs:
         _, _, _, qd, kd, vd = make_inputs(cfg, dev)
+        B, H, Nk, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+        Nq = cfg.get("Nq", Nk)
+        qd = qd[:, :, :Nq].contiguous()
+        code = fa.FA_DTYPE_BF16 if cfg["dtype"] == "bf16" else fa.FA_DTYPE_F16
         for causal in cfg["flags"]:
-            fn = lambda: fa.fwd(qd, kd, vd, causal=bool(causal))  # noqa: E731
+            splits = fa.fa_split_count(B, H, Nq, Nk, d, causal)
+            out = torch.empty_like(qd)
+            lse = torch.empty((B, H, Nq), device=dev, dtype=torch.float32)
+            ws = (torch.empty(fa.fa_split_workspace_bytes(B, H, Nq, d, splits) // 4, device=dev,
+                              dtype=torch.float32) if splits > 1 else None)
+
+            def fn(causal=causal, splits=splits, out=out, lse=lse, ws=ws):
+                fa.fwd(qd, kd, vd, causal=bool(causal), out=out, lse=lse, splits=splits, workspace=ws)
             warm(fn, 20, 0.5)
             torch.cuda.reset_peak_memory_stats(dev)
             ts = timed_launches(fn, 50, torch.cuda.current_stream(dev))
-            plan = fa.fa_plan(cfg["B"], cfg["H"], cfg["N"], cfg["d"], causal,
-                              fa.FA_DTYPE_BF16 if cfg["dtype"] == "bf16" else fa.FA_DTYPE_F16)
+            plan = fa.fa_plan_qk(B, H, Nq, Nk, d, causal, code)
             med = statistics.median(ts)
-            rows.append({"B": cfg["B"], "H": cfg["H"], "N": cfg["N"], "d": cfg["d"],
+            rows.append({"B": B, "H": H, "Nq": Nq, "N": Nk, "d": d,
                          "dtype": cfg["dtype"], "q_scale": cfg.get("q_scale", 1.0),
-                         "causal": bool(causal), "median_ms": med, "min_ms": min(ts),
-                         "max_ms": max(ts),
+                         "causal": bool(causal), "splits": splits, "median_ms": med,
+                         "min_ms": min(ts), "max_ms": max(ts),
                          "tflops": plan["algo_flops"] / (med * 1e-3) / 1e12,
                          "frac_peak": plan["algo_flops"] / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                          "hbm_gbs_compulsory": plan["algo_bytes"] / (med * 1e-3) / 1e9,
+                         "frac_hbm": plan["algo_bytes"] / (med * 1e-3) / 1e9 / PEAK_HBM_GBS,
                          "peak_mem_bytes": torch.cuda.max_memory_allocated(dev)})
             print(json.dumps({"sweep_row": rows[-1]}), flush=True)
         del qd, kd, vd

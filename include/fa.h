@@ -106,9 +106,9 @@ int fa_fwd_qk(const void *q, const void *k, const void *v, void *o, float *lse, 
  * The profiler page names KV-cache decode as the next step ("Getting the
  * kernel correct, then benchmarking it honestly", closing paragraph).
  *
- * fa_split_count -- a suggested n_splits (>= 1): enough workgroups to fill
- *   the GPU about twice, at least 4 key tiles of 64 per chunk. Returns 0 on
- *   invalid arguments.
+ * fa_split_count -- a suggested n_splits (>= 1): about 256 to 1024
+ *   workgroups in all and at least 16 key tiles of 64 per chunk (1, the
+ *   direct path, for short key sequences). Returns 0 on invalid arguments.
  * fa_split_workspace_bytes -- bytes of workspace fa_fwd_split_qk needs:
  *   n_splits * B*H*Nq * (d + 1) * 4. Returns 0 on invalid arguments.
  * fa_fwd_split_qk -- arguments as fa_fwd_qk, plus:
