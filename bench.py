@@ -21,6 +21,7 @@ context for the roofline, and times the fp64 oracle on the host (cpu_baseline).
 Other modes (used to collect counters; each runs a few launches only):
     --profile-kernels   a few launches of each headline kernel, nothing else
     --copy-calibration  a plain device-to-device copy of a known size
+    --profile-decode    the split-key decode path (one query x 16384 keys, B=1 H=32)
     --sweep             medians of 50 for every configuration of the workload
                         list, with peak memory (one extra JSON object)
 """
@@ -351,6 +352,45 @@ def profile_kernels(args):
     print(json.dumps({"profiled": "fa_fwd bf16 d=128 N=4096 B=4 H=16", "launches_each": args.steps}))
 
 
+DECODE = dict(B=1, H=32, Nq=1, N=16384, d=128, dtype="bf16", seed=10)
+
+
+def profile_decode(args):
+    """KV-cache decode (one query row per head against 16384 keys, B=1 H=32 d=128 bf16, non-causal)
+    on the split-key path: `steps` calls back to back after 20 untimed ones, then one JSON line with
+    the event-timed average per call and its compulsory HBM rate (for rocprofv3 passes)."""
+    import torch
+    import tiled_attention_forward_fwd_amd as fa
+    dev = torch.device("cuda:0")
+    cfg = DECODE
+    _, _, _, qd, kd, vd = make_inputs(cfg, dev)
+    B, H, Nq, Nk, d = cfg["B"], cfg["H"], cfg["Nq"], cfg["N"], cfg["d"]
+    qd = qd[:, :, :Nq].contiguous()
+    splits = fa.fa_split_count(B, H, Nq, Nk, d, 0)
+    out = torch.empty_like(qd)
+    lse = torch.empty((B, H, Nq), device=dev, dtype=torch.float32)
+    ws = torch.empty(fa.fa_split_workspace_bytes(B, H, Nq, d, splits) // 4, device=dev,
+                     dtype=torch.float32)
+
+    def call():
+        fa.fwd(qd, kd, vd, out=out, lse=lse, splits=splits, workspace=ws)
+    for _ in range(20):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    plan = fa.fa_plan_qk(B, H, Nq, Nk, d, 0, fa.FA_DTYPE_BF16)
+    print(json.dumps({"profiled": f"decode B={B} H={H} Nq={Nq} Nk={Nk} d={d} bf16, {splits} key chunks",
+                      "calls": args.steps, "avg_ms_per_call_back_to_back": ms,
+                      "algorithmic_bytes": plan["algo_bytes"],
+                      "hbm_gbs_compulsory": plan["algo_bytes"] / (ms * 1e-3) / 1e9}))
+
+
 def copy_calibration(args):
     """A plain copy of a known size, to scale the HBM byte counters."""
     import torch
@@ -380,6 +420,8 @@ def main():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--profile-decode", action="store_true",
+                    help="split-key decode calls only (one query x 16384 keys), for rocprofv3")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -399,6 +441,8 @@ def main():
         return profile_kernels(args)
     if args.copy_calibration:
         return copy_calibration(args)
+    if args.profile_decode:
+        return profile_decode(args)
 
     out, (q, k, v) = headline(args)
     if args.gemm_ceiling:
