@@ -587,34 +587,63 @@ __device__ __forceinline__ void store_partials(const f32x16 (&oacc)[QB][DB], con
 
 // Merge of the key chunks of a split launch, per query row:
 // lse = ln sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s. Each thread
-// owns 8 consecutive dims of one row; rows are [B*H*Nq] in order.
+// owns 8 consecutive dims of one row; rows are [B*H*Nq] in order. Chunks go
+// in groups of 16 whose loads are all issued before any is used, so a call
+// with up to 16 chunks makes two rounds of memory reads (the logsumexps, then
+// the partial outputs) instead of one per chunk.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__ ws_o,
                                                        const float* __restrict__ ws_lse, T* __restrict__ o,
                                                        float* __restrict__ lse, int64_t n_rows, int n_splits)
 {
-    constexpr int TPR = D / 8;  // threads per row
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int TPR = D / 8, G = 16;  // threads per row, chunks per group
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t row = t / TPR;
     const int c0 = (int)(t % TPR) * 8;
     if (row >= n_rows) return;
     float mx = -INFINITY;
-    for (int sp = 0; sp < n_splits; ++sp) mx = fmaxf(mx, ws_lse[(int64_t)sp * n_rows + row]);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < n_splits; s0 += G) {
+        float l[G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) l[i] = s0 + i < n_splits ? ws_lse[(int64_t)(s0 + i) * n_rows + row] : -INFINITY;
+#pragma unroll
+        for (int i = 0; i < G; ++i) mx = fmaxf(mx, l[i]);
+    }
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     if (mx > -INFINITY) {
-        for (int sp = 0; sp < n_splits; ++sp) {
-            const float w = expf(ws_lse[(int64_t)sp * n_rows + row] - mx);
-            const float* src = ws_o + ((int64_t)sp * n_rows + row) * D + c0;
-            wsum += w;
+        for (int s0 = 0; s0 < n_splits; s0 += G) {
+            float l[G];
+            f32x4 a[G], b[G];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += w * src[e];
+            for (int i = 0; i < G; ++i) {
+                if (s0 + i < n_splits) {
+                    const float* src = ws_o + ((int64_t)(s0 + i) * n_rows + row) * D + c0;
+                    l[i] = ws_lse[(int64_t)(s0 + i) * n_rows + row];
+                    a[i] = *(const f32x4*)src;
+                    b[i] = *(const f32x4*)(src + 4);
+                } else {
+                    l[i] = -INFINITY;
+                    a[i] = b[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                const float w = expf(l[i] - mx);  // exp(-inf) = 0 for absent or empty chunks
+                wsum += w;
+                acc0 += w * a[i];
+                acc1 += w * b[i];
+            }
         }
     }
     const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
     T vals[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) vals[e] = to_elem<T>(acc[e] * inv);
+    for (int e = 0; e < 4; ++e) {
+        vals[e] = to_elem<T>(acc0[e] * inv);
+        vals[4 + e] = to_elem<T>(acc1[e] * inv);
+    }
     *(u32x4*)(o + row * D + c0) = __builtin_bit_cast(u32x4, vals);
     if (c0 == 0) lse[row] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
