@@ -17,17 +17,30 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fa_oracle.c")
+_SRC_BWD = os.path.join(_HERE, "fa_oracle_bwd.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+_LIB_BWD = os.path.join(_HERE, "liboracle_bwd.so")
 _lib = None
+_lib_bwd = None
 
 
 def build(src=_SRC, out=_LIB, extra_flags=()):
-    """Compile the oracle (or a variant of its source) into a shared library."""
+    """Compile the forward oracle (or a variant of its source) into a shared library."""
     cmd = ["gcc", "-O2", "-std=c11", "-shared", "-fPIC", "-pthread", *extra_flags,
            src, "-o", out + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
     return out
+
+
+def build_bwd(src=_SRC_BWD, out=_LIB_BWD, extra_flags=()):
+    """Compile the backward oracle (or a variant of its source) into a shared library."""
+    return build(src, out, extra_flags)
+
+
+def build_all():
+    build()
+    build_bwd()
 
 
 def _bind(lib):
@@ -101,3 +114,46 @@ def attention_fwd(q, k, v, causal, scale, rows=None, tile_n=0, nthreads=None, li
     if rc != 0:
         raise RuntimeError(f"fa_oracle_fwd failed with status {rc}")
     return o, lse
+
+
+def _bind_bwd(lib):
+    fn = lib.fa_oracle_bwd
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 5 + [
+        ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    return lib
+
+
+def load_bwd(path=None):
+    """Load the built backward oracle, building it first if it is missing."""
+    global _lib_bwd
+    if path is not None:
+        return _bind_bwd(ctypes.CDLL(path))
+    if _lib_bwd is None:
+        if not os.path.exists(_LIB_BWD):
+            build_bwd()
+        _lib_bwd = _bind_bwd(ctypes.CDLL(_LIB_BWD))
+    return _lib_bwd
+
+
+def attention_bwd(q, k, v, dout, causal, scale, nthreads=None, lib=None):
+    """fp64 gradients of sum(dout * O) for O = attention(q, k, v) on the CPU.
+
+    q, dout : ``[B, H, Nq, d]``; k, v: ``[B, H, Nk, d]`` (values in the storage
+              dtype). Returns ``(dq, dk, dv)`` as float64 numpy arrays. See the
+              header of ``fa_oracle_bwd.c`` for the definition.
+    """
+    lib = lib or load_bwd()
+    qf, kf, vf, df = _as_f32(q), _as_f32(k), _as_f32(v), _as_f32(dout)
+    B, H, Nq, d = qf.shape
+    Nk = kf.shape[2]
+    assert kf.shape == (B, H, Nk, d) and vf.shape == kf.shape and df.shape == qf.shape
+    dq = np.empty((B, H, Nq, d), dtype=np.float64)
+    dk = np.empty((B, H, Nk, d), dtype=np.float64)
+    dv = np.empty((B, H, Nk, d), dtype=np.float64)
+    rc = lib.fa_oracle_bwd(qf.ctypes.data, kf.ctypes.data, vf.ctypes.data, df.ctypes.data, B, H,
+                           Nq, Nk, d, 1 if causal else 0, float(scale), dq.ctypes.data,
+                           dk.ctypes.data, dv.ctypes.data, int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"fa_oracle_bwd failed with status {rc}")
+    return dq, dk, dv
