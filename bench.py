@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk/CU x 2.4 GHz, dense (no sparsity)
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_forward_fwd_amd", "csrc", f)
-                  for f in ("fa_fwd_kernel.hip", "fa_tiles.h")]
+                  for f in ("fa_fwd_kernel.hip", "fa_device.h", "fa_tiles.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_bf16_d128_N4096.txt")
 
 HEADLINE = dict(B=4, H=16, N=4096, d=128, dtype="bf16", seed=7)

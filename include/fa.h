@@ -128,6 +128,32 @@ int fa_fwd_split_qk(const void *q, const void *k, const void *v, void *o, float 
                     void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * fa_bwd -- attention backward pass: the gradients of sum(dO * O) with respect
+ * to q, k and v, where O = fa_fwd(q, k, v) with the same causal flag and
+ * scale. "How to optimise a Triton FlashAttention-2 kernel step by step with
+ * a profiler" names this pass as its next kernel (closing list): it consumes
+ * the logsumexp the forward writes and accumulates in two directions. With
+ * P_ij = exp(scale <q_i, k_j> - lse_i) over the visible keys:
+ *   D_i = <dO_i, O_i>,  dS_ij = P_ij (<dO_i, v_j> - D_i),
+ *   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i,
+ *   dQ_i = scale sum_j dS_ij k_j.
+ *
+ *   q, k, v, o, dout : device, [B, H, N, d] contiguous, element type `dtype`,
+ *                      16-byte aligned; o and lse as written by fa_fwd.
+ *   lse              : device, [B, H, N] fp32, 4-byte aligned.
+ *   dq, dk, dv       : device, [B, H, N, d], `dtype`, 16-byte aligned,
+ *                      overwritten; no overlap with any other argument.
+ *   delta            : device, [B, H, N] fp32, 16-byte aligned, owned by the
+ *                      caller: scratch that receives D (libfa allocates
+ *                      nothing).
+ * Other arguments as fa_fwd. Three kernels are enqueued on `stream`; nothing
+ * uses atomics, so results are deterministic.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+           const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H, int N, int d,
+           int causal, float scale, int dtype, void *stream);
+
+/*
  * fa_status_string -- human-readable text for a status code. For FA_ERR_HIP
  * and FA_ERR_INVALID_ARG it names the HIP error or the failed check of the
  * last failing call on the calling thread. The returned pointer stays valid

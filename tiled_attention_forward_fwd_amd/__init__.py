@@ -26,7 +26,8 @@ FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1
 
 # Entry points declared in include/fa.h.
 EXPORTED = ("fa_fwd", "fa_fwd_qk", "fa_fwd_split_qk", "fa_split_count", "fa_split_workspace_bytes",
-            "fa_status_string", "fa_tile_counts", "fa_tile_counts_qk", "fa_plan", "fa_plan_qk")
+            "fa_bwd", "fa_status_string", "fa_tile_counts", "fa_tile_counts_qk", "fa_plan",
+            "fa_plan_qk")
 
 
 class FaPlan(ctypes.Structure):
@@ -71,6 +72,9 @@ def load_library(path=LIB_PATH):
     lib.fa_split_count.argtypes = [ctypes.c_int] * 6
     lib.fa_split_workspace_bytes.restype = ctypes.c_int64
     lib.fa_split_workspace_bytes.argtypes = [ctypes.c_int] * 5
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [ctypes.c_int]
     lib.fa_tile_counts.restype = ctypes.c_int
@@ -123,6 +127,47 @@ def fa_split_count(B, H, Nq, Nk, d, causal):
 
 def fa_split_workspace_bytes(B, H, Nq, d, n_splits):
     return int(load_library().fa_split_workspace_bytes(int(B), int(H), int(Nq), int(d), int(n_splits)))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, causal, scale, dtype, stream):
+    """Direct call of the C entry point with raw pointers (ints); returns the status."""
+    return load_library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, int(B), int(H), int(N),
+                                 int(d), int(causal), float(scale), int(dtype), stream)
+
+
+def bwd(q, k, v, o, lse, dout, causal=False, scale=None, stream=None):
+    """Attention backward on the GPU: returns ``(dq, dk, dv)``.
+
+    q, k, v, o, dout : CUDA (HIP) tensors ``[B, H, N, d]``, contiguous, one of
+                       float16/bfloat16; ``o`` and ``lse`` (``[B, H, N]``
+                       float32) from ``fwd`` with the same causal flag and
+                       scale. The D = rowsum(dO * O) scratch is allocated with
+                       torch.
+    """
+    import torch
+    ts = (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout))
+    for name, t in ts:
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous [B, H, N, d] GPU tensor")
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    code = dtype_code(q.dtype)
+    if scale is None:
+        scale = default_scale(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                    B, H, N, d, causal, scale, code, handle)
+    _check(rc)
+    return dq, dk, dv
 
 
 def fa_tile_counts_qk(Nq, Nk, block_m, block_n, causal):

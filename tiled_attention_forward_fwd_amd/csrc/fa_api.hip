@@ -224,6 +224,44 @@ int fa_fwd_split_qk(const void* q, const void* k, const void* v, void* o, float*
     return FA_OK;
 }
 
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d,
+           int causal, float scale, int dtype, void* stream)
+{
+    g_msg[0] = 0;
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta)
+        return fail(FA_ERR_INVALID_ARG, "NULL tensor pointer");
+    const void* a16[] = {q, k, v, o, dout, dq, dk, dv, delta};
+    for (const void* p : a16)
+        if (!aligned(p, 16)) return fail(FA_ERR_INVALID_ARG, "tensors and delta must be 16-byte aligned");
+    if (!aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    const int rc = check_problem(B, H, N, N, d, causal, dtype);
+    if (rc != FA_OK) return rc;
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    const size_t tb = (size_t)B * H * N * d * 2, lb = (size_t)B * H * N * 4;
+    const void* outs[] = {dq, dk, dv};
+    const void* ins[] = {q, k, v, o, dout};
+    for (const void* w : outs) {
+        for (const void* r : ins)
+            if (overlap(w, tb, r, tb)) return fail(FA_ERR_INVALID_ARG, "a gradient overlaps an input");
+        if (overlap(w, tb, lse, lb) || overlap(w, tb, delta, lb))
+            return fail(FA_ERR_INVALID_ARG, "a gradient overlaps lse or delta");
+    }
+    if (overlap(dq, tb, dk, tb) || overlap(dq, tb, dv, tb) || overlap(dk, tb, dv, tb))
+        return fail(FA_ERR_INVALID_ARG, "dq, dk and dv overlap");
+    for (const void* r : ins)
+        if (overlap(delta, lb, r, tb)) return fail(FA_ERR_INVALID_ARG, "delta overlaps an input");
+    if (overlap(delta, lb, lse, lb)) return fail(FA_ERR_INVALID_ARG, "delta overlaps lse");
+    const hipError_t e = fa::launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d,
+                                        causal != 0, scale, dtype == FA_DTYPE_BF16, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        snprintf(g_msg, sizeof g_msg, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+        return FA_ERR_HIP;
+    }
+    return FA_OK;
+}
+
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
            int d, int causal, float scale, int dtype, void* stream)
 {

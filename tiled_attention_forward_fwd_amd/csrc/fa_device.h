@@ -1,0 +1,435 @@
+// fa_device.h -- device building blocks shared by the attention kernels
+// (forward and backward): MFMA wrappers, the LDS tile layout and its copies,
+// the score and transposed-operand MFMA loops and their ordering hints. The
+// layouts are described where they are defined and in the forward kernel's
+// header comment. Included by the kernel sources only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace fa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<__bf16> {
+    typedef bf16x8 vec8;
+    static __device__ __forceinline__ f32x16 run(vec8 a, vec8 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mma<_Float16> {
+    typedef f16x8 vec8;
+    static __device__ __forceinline__ f32x16 run(vec8 a, vec8 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+constexpr int kXcds = 8;  // XCDs of an MI355X
+
+// Tile shape: head dim D, WAVES waves per workgroup, QB 32-row query blocks
+// per wave, BN = 64 keys per K/V tile.
+template <int D, int WAVES, int QB>
+struct Cfg {
+    static_assert(D == 64 || D == 128, "head dim");
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int BM = 32 * QB * WAVES;    // query rows per workgroup
+    static constexpr int BN = 64;                 // keys per tile
+    static constexpr int CPR = D / 8;             // 16-byte chunks per row
+    static constexpr int TILE = BN * D;           // elements of one K or V tile (dense)
+    static constexpr int LDS_BYTES = 4 * TILE * 2;  // two K and two V tile buffers
+    static constexpr int KB = BN / 32;            // 32-key blocks per tile
+    static constexpr int DS = D / 16;             // MFMA k-steps of S^T = K Q^T
+    static constexpr int DB = D / 32;             // 32-row blocks of O^T
+    static constexpr int KT = BN / 16;            // MFMA k-steps of O^T += V^T P^T
+    static constexpr int LOADS = BN * CPR / THREADS;  // 16-byte copies per thread, each of K and V
+    static_assert(LOADS * THREADS == BN * CPR, "tile split");
+    // rows between a lane's consecutive copies keep the swizzle (period 16)
+    static_assert((64 * WAVES / CPR) % 16 == 0 || LOADS == 1, "copy stride");
+};
+
+// Chunk swizzle: 16-byte chunk c of tile row r is stored at chunk c ^ swz(r).
+// The LDS has 64 four-byte banks; a 16-byte read is served 16 lanes at a
+// time, an 8-byte read 32 lanes at a time.
+//  * K operand (ds_read_b128): 16 consecutive rows read one logical chunk;
+//    swz is a bijection on r mod 16 (d=128) or maps the 8 even and the 8 odd
+//    rows (the two bank halves of a 128-byte row pair, d=64) to distinct
+//    chunks, so the 16 lanes hit 16 distinct bank quads.
+//  * V operand (ds_read_b64_tr_b16): a half-wave reads rows 4a..4a+3 at
+//    logical chunks {4b, 4b+1} (lanes 0-15) and {4b+2, 4b+3} (lanes 16-31);
+//    swz changes bits 2-3 between those rows and leaves bit 1 alone, so the
+//    two lane groups fall in disjoint halves of the 64 banks.
+// swz has period 16 in r (tile_lane_offset relies on it).
+template <int D>
+__device__ __forceinline__ int swz(int row)
+{
+    if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    const int m = (row >> 1) & 7;
+    return ((m & 1) << 2) | ((m >> 1) & 3);
+}
+
+__device__ __forceinline__ float swap_halves_max(float x)
+{
+    // v_permlane32_swap exchanges lanes 0-31 of one operand with lanes 32-63
+    // of the other; with both operands = x, the pair holds x[lane] and
+    // x[lane ^ 32] in some order, which is all a symmetric reduction needs.
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float swap_halves_sum(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <typename V8>
+__device__ __forceinline__ V8 as_vec8(u32x4 x)
+{
+    return __builtin_bit_cast(V8, x);
+}
+
+// K/V tiles are copied with the buffer form of the LDS DMA: a descriptor
+// covering one head (base, size in bytes), a wave-uniform byte offset and one
+// per-lane byte offset. Bytes at or past the head's size read as zero, so a
+// ragged last tile is zero-filled and no copy can leave its head.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRawBufferWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
+
+__device__ __forceinline__ rsrc_t head_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRawBufferWord3);
+}
+
+// 16 bytes per lane into LDS at lds_base + 16 * lane (lds_base wave-uniform).
+// The builtin exists only in the device pass.
+__device__ __forceinline__ void copy16_to_lds(rsrc_t r, uint16_t* lds_base, uint32_t lane_off,
+                                              uint32_t tile_off)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds_base, 16, lane_off, tile_off, 0, 0);
+#endif
+}
+
+// HBM -> LDS copy of rows [k0, k0 + BN) of one K or V head. Wave w, copy i
+// fills 64 consecutive LDS chunks; lane l fetches the global chunk that the
+// swizzle places there. Copy i is 64*WAVES/CPR rows below copy 0, a multiple
+// of the swizzle period, so every copy of a lane is one per-lane byte offset
+// plus a wave-uniform k0 * D * 2 + i * WAVES * 64 * 16.
+template <int D>
+__device__ __forceinline__ uint32_t tile_lane_offset(int wave, int lane)
+{
+    const int c = wave * 64 + lane;
+    const int r0 = c / (D / 8), pc = c % (D / 8);
+    return (uint32_t)(r0 * D * 2 + (pc ^ swz<D>(r0)) * 16);
+}
+
+template <int D, int WAVES, int QB>
+__device__ __forceinline__ void issue_tile(uint16_t* buf, rsrc_t src, int k0, int wave,
+                                           uint32_t lane_off)
+{
+    typedef Cfg<D, WAVES, QB> C;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i)
+        copy16_to_lds(src, buf + (i * WAVES + wave) * 64 * 8, lane_off,
+                      (uint32_t)k0 * (D * 2) + i * (WAVES * 64 * 16));
+}
+
+// Waits for this thread's outstanding LDS copies and LDS reads, then for the
+// whole workgroup.
+__device__ __forceinline__ void stage_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+}
+
+template <typename T>
+__device__ __forceinline__ T to_elem(float x);
+template <>
+__device__ __forceinline__ __bf16 to_elem<__bf16>(float x) { return (__bf16)x; }
+template <>
+__device__ __forceinline__ _Float16 to_elem<_Float16>(float x) { return (_Float16)x; }
+
+// S^T = K Q^T for one key tile: s[qb][kb] holds keys 32*kb + (accumulator
+// rows) of this lane's query in block qb. Each K operand read feeds QB MFMAs.
+template <typename T, int D, int QB, int KB, int DS>
+__device__ __forceinline__ void scores(f32x16 (&s)[QB][KB], const uint16_t* __restrict__ ks,
+                                       const typename Mma<T>::vec8 (&qf)[QB][DS], int l32, int hh)
+{
+    typedef typename Mma<T>::vec8 vec8;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = (f32x16){};
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int row = kb * 32 + l32;
+            const uint16_t* krow = ks + row * D;
+            const int sw = swz<D>(row);
+            vec8 a = as_vec8<vec8>(*(const u32x4*)(krow + (((2 * ds + hh) ^ sw) * 8)));
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) s[qb][kb] = Mma<T>::run(a, qf[qb][ds], s[qb][kb]);
+        }
+    }
+}
+
+// The scores of the next tile fused with the exp2 work of this one: after
+// each score MFMA come the exp2 / row-sum / convert of a few elements of the
+// current tile, so the vector units work while the matrix core runs instead
+// of after it (the two streams are independent). One 32-row block (QB = 1).
+template <typename T, int D, int KB, int DS, int KT>
+__device__ __forceinline__ void scores_with_exp(f32x16 (&sn)[1][KB], const uint16_t* __restrict__ ks,
+                                                const typename Mma<T>::vec8 (&qf)[1][DS], int l32, int hh,
+                                                const f32x16 (&sc)[1][KB], float m, float c_log2,
+                                                typename Mma<T>::vec8 (&p)[1][KT], float (&rs)[1])
+{
+    typedef typename Mma<T>::vec8 vec8;
+    constexpr int n_mfma = KB * DS, n_el = KB * 16, per = n_el / n_mfma;
+    static_assert(per * n_mfma == n_el && per % 2 == 0, "exp work per MFMA");
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sn[0][kb] = (f32x16){};
+    float acc = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int row = kb * 32 + l32;
+            const vec8 a = as_vec8<vec8>(*(const u32x4*)(ks + row * D + (((2 * ds + hh) ^ swz<D>(row)) * 8)));
+            sn[0][kb] = Mma<T>::run(a, qf[0][ds], sn[0][kb]);
+            const int i = ds * KB + kb;
+#pragma unroll
+            for (int e = i * per; e < (i + 1) * per; ++e) {
+                const int eb = e >> 4, r = e & 15;
+                const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][eb][r], c_log2, -m));
+                acc += x;
+                p[0][eb * 2 + (r >> 3)][r & 7] = to_elem<T>(x);
+            }
+        }
+    }
+    rs[0] = acc;
+}
+
+// Diagonal / ragged tiles: keys past N, and for causal attention keys after
+// the lane's query, get score -inf.
+template <int KB, bool CAUSAL>
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[KB], int k0, int qrow, int n_keys, int hh)
+{
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const bool hide = key >= n_keys || (CAUSAL && key > qrow);
+            if (hide) s[kb][r] = -INFINITY;
+        }
+    }
+}
+
+// Row max of one block of scores in log2 units (both lane halves of a row).
+template <int KB>
+__device__ __forceinline__ float row_max_log2(const f32x16 (&s)[KB], float c_log2)
+{
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    return swap_halves_max(mx) * c_log2;
+}
+
+// P = 2^(s * c - m) of one tile, rounded to the input type after the fp32
+// value has been added to the lane's partial row sum (Round 4, "The P cast").
+template <typename T, int QB, int KB, int KT>
+__device__ __forceinline__ void exp_tile(const f32x16 (&s)[QB][KB], const float (&m_run)[QB], float c_log2,
+                                         typename Mma<T>::vec8 (&p)[QB][KT], float (&rs)[QB])
+{
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        float acc = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r], c_log2, -m_run[qb]));
+                acc += e;
+                p[qb][kb * 2 + (r >> 3)][r & 7] = to_elem<T>(e);
+            }
+        }
+        rs[qb] = acc;
+    }
+}
+
+// Online softmax with a lazily updated max. The exponentials of a tile are
+// taken against the running max m of the earlier tiles; the row max of the
+// tile itself is only needed when that makes some P large. The test is on the
+// lane's partial row sum (32 of the tile's 64 keys), which bounds every P of
+// the lane: while it stays <= 2^12 the tile is accepted as it is. P <= 2^12
+// is far inside the fp16/bf16 range, the accumulators cannot overflow, and
+// O / l and m + log2(l) are unchanged because O and l carry the same factor.
+// Otherwise (always on the first tile, where m is still the initial -1e30,
+// and when the scores grew by more than about 2^12 over m) the wave takes the
+// true row max, rescales O and l by alpha = 2^(m_old - m_new) and recomputes
+// the tile's P (the update of "Programming an attention kernel in Triton",
+// online softmax). The branch is wave-uniform.
+constexpr float kLaneSumBound = 4096.0f;
+
+template <typename T, int QB, int KB, int DB, int KT>
+__device__ __forceinline__ void softmax_finish(const f32x16 (&s)[QB][KB], f32x16 (&o)[QB][DB],
+                                               float (&m_run)[QB], float (&l_run)[QB], float c_log2,
+                                               typename Mma<T>::vec8 (&p)[QB][KT], float (&rs)[QB])
+{
+    bool bad = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) bad = bad || !(rs[qb] <= kLaneSumBound);
+    if (__builtin_amdgcn_ballot_w64(bad)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float mx = row_max_log2<KB>(s[qb], c_log2);
+            const float m_new = fmaxf(m_run[qb], mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+            m_run[qb] = m_new;
+            l_run[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
+        }
+        exp_tile<T, QB, KB, KT>(s, m_run, c_log2, p, rs);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
+}
+
+template <typename T, int QB, int KB, int DB, int KT>
+__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[QB][KB], f32x16 (&o)[QB][DB],
+                                             float (&m_run)[QB], float (&l_run)[QB], float c_log2,
+                                             typename Mma<T>::vec8 (&p)[QB][KT])
+{
+    float rs[QB];
+    exp_tile<T, QB, KB, KT>(s, m_run, c_log2, p, rs);
+    softmax_finish<T, QB, KB, DB, KT>(s, o, m_run, l_run, c_log2, p, rs);
+}
+
+// O^T += V^T P^T. V^T operand, lane l = 16g + i: dim 32*db + (l % 32);
+// elements 0..3 are keys 16t + 4h + [0,4), elements 4..7 keys
+// 16t + 8 + 4h + [0,4) (h = g/2), the key order of P^T. Each of the two
+// transposed reads has lane i address key (base + i/4), dims 4*(i%4) + [0,4)
+// of the group's 16 dims. Each V operand feeds QB MFMAs; the t-major order
+// consumes P in the order it is produced.
+template <typename T, int D, int QB, int DB, int KT>
+__device__ __forceinline__ void pv_tile(const typename Mma<T>::vec8 (&p)[QB][KT],
+                                        const uint16_t* __restrict__ vts, f32x16 (&o)[QB][DB], int lane,
+                                        int hh)
+{
+    typedef typename Mma<T>::vec8 vec8;
+    const int gi = lane & 15, g1 = (lane >> 4) & 1;
+    const int half = (gi & 1) * 4;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+        const int key0 = 16 * t + 4 * hh + (gi >> 2);
+        const int key1 = key0 + 8;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int chunk = 4 * db + 2 * g1 + ((gi & 3) >> 1);
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(vts + key0 * D + ((chunk ^ swz<D>(key0)) * 8) + half));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(vts + key1 * D + ((chunk ^ swz<D>(key1)) * 8) + half));
+            u32x4 w;
+            w[0] = __builtin_bit_cast(u32x2, lo)[0];
+            w[1] = __builtin_bit_cast(u32x2, lo)[1];
+            w[2] = __builtin_bit_cast(u32x2, hi)[0];
+            w[3] = __builtin_bit_cast(u32x2, hi)[1];
+            const vec8 a = as_vec8<vec8>(w);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) o[qb][db] = Mma<T>::run(a, p[qb][t], o[qb][db]);
+        }
+    }
+}
+
+template <typename T, int D, int QB, int KB, int DB, int KT>
+__device__ __forceinline__ void softmax_pv(const f32x16 (&s)[QB][KB], const uint16_t* __restrict__ vts,
+                                           f32x16 (&o)[QB][DB], float (&m_run)[QB],
+                                           float (&l_run)[QB], float c_log2, int lane, int hh)
+{
+    typename Mma<T>::vec8 p[QB][KT];
+    softmax_tile<T, QB, KB, DB, KT>(s, o, m_run, l_run, c_log2, p);
+    pv_tile<T, D, QB, DB, KT>(p, vts, o, lane, hh);
+}
+
+// Instruction order of a pipelined tile. The scores of the next tile are
+// issued first (MFMAs that need only K and Q), keeping their K operand reads
+// a few MFMAs ahead; then the P.V MFMAs follow with their transposed V reads
+// issued ahead. Vector instructions keep their program order between the
+// MFMAs (scores_with_exp places them).
+template <int D, int WAVES, int QB>
+__device__ __forceinline__ void order_scores_block()
+{
+    typedef Cfg<D, WAVES, QB> C;
+    constexpr int n_reads = C::KB * C::DS;  // one K read per QB MFMAs
+    constexpr int lead = 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, lead, 0);
+#pragma unroll
+    for (int i = 0; i < n_reads - lead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < lead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+}
+
+template <int D, int WAVES, int QB>
+__device__ __forceinline__ void order_pv_block()
+{
+    typedef Cfg<D, WAVES, QB> C;
+    constexpr int n_ops = C::DB * C::KT;  // two V reads per QB MFMAs
+    constexpr int lead = 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * lead, 0);
+#pragma unroll
+    for (int i = 0; i < n_ops - lead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < lead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+}
+
+// Q fragments: B operand of S^T = K Q^T, query qrow[qb] = row0 + 32*qb +
+// (lane % 32), dims 16*ds + 8*hh + [0, 8). Rows past N are zero (their
+// outputs are not stored).
+template <typename T, int D, int QB, int DS>
+__device__ __forceinline__ void load_q(const T* __restrict__ qh, int row0, int n_rows, int l32, int hh,
+                                       int (&qrow)[QB], typename Mma<T>::vec8 (&qf)[QB][DS])
+{
+    typedef typename Mma<T>::vec8 vec8;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        qrow[qb] = row0 + qb * 32 + l32;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (qrow[qb] < n_rows) x = *(const u32x4*)(qh + (int64_t)qrow[qb] * D + ds * 16 + hh * 8);
+            qf[qb][ds] = as_vec8<vec8>(x);
+        }
+    }
+}
+
+}  // namespace
+}  // namespace fa

@@ -34,4 +34,10 @@ hipError_t launch_fwd_split(const void* q, const void* k, const void* v, void* o
                             int n_splits, float* workspace, hipStream_t stream);
 int split_rows_per_tile();
 
+// Enqueues the backward pass (delta, dK/dV and dQ kernels); arguments were
+// validated by the caller.
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
+                      int d, bool causal, float scale, bool bf16, hipStream_t stream);
+
 }  // namespace fa
