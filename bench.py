@@ -137,6 +137,40 @@ def power_and_clock(step, seconds=2.0):
     return result if "socket_power_w" in result else None
 
 
+def backward_leg(reps=10):
+    """The backward pass at the headline shape, after the timed region: fa.bwd (its three kernels)
+    back to back between HIP events, non-causal and causal, with TFLOP/s in the FlashAttention-2
+    convention (2.5x the forward's 4*B*H*N*N*d, halved for causal)."""
+    import torch
+    import tiled_attention_forward_fwd_amd as fa
+    cfg = HEADLINE
+    dev = torch.device("cuda:0")
+    _, _, _, qd, kd, vd = make_inputs(cfg, dev)
+    from fa_inputs import make_qkv
+    dout = make_qkv(cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["dtype"], cfg["seed"] + 100)[0].to(dev)
+    res = {}
+    for causal in (False, True):
+        o, lse = fa.fwd(qd, kd, vd, causal=causal)
+        f = lambda: fa.bwd(qd, kd, vd, o, lse, dout, causal=causal)  # noqa: E731
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        flops = 2.5 * 4.0 * cfg["B"] * cfg["H"] * cfg["N"] ** 2 * cfg["d"] * (0.5 if causal else 1.0)
+        res["causal" if causal else "noncausal"] = {
+            "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+            "frac_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    res["what"] = ("fa.bwd (delta, dK/dV, dQ kernels) at B=4 H=16 N=4096 d=128 bf16, FLOPs = 2.5x "
+                   "the forward's; the kernels execute 1.4x that (S and dP are recomputed for dQ)")
+    return res
+
+
 def gemm_ceiling(seconds=1.0):
     """Context for the roofline: TFLOP/s of a plain 8192^3 bf16 GEMM (hipBLASLt through
     torch.matmul) on seeded N(0,1) operands, run back to back after the timed region. The
@@ -415,6 +449,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-telemetry", dest="telemetry", action="store_false",
                     help="skip the amd-smi power/clock sample (taken outside the timed region)")
+    ap.add_argument("--no-backward", dest="backward", action="store_false",
+                    help="skip the backward-pass leg (timed after the headline region)")
     ap.add_argument("--no-gemm-ceiling", dest="gemm_ceiling", action="store_false",
                     help="skip the hipBLASLt GEMM reference run (context for the roofline)")
     ap.add_argument("--sweep", action="store_true")
@@ -445,6 +481,8 @@ def main():
         return profile_decode(args)
 
     out, (q, k, v) = headline(args)
+    if args.backward:
+        out["backward"] = backward_leg()
     if args.gemm_ceiling:
         ceil = gemm_ceiling()
         ceil["attention_noncausal_fraction"] = out["roofline"]["achieved"] / ceil["value"]
