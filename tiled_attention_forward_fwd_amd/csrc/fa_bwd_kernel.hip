@@ -14,9 +14,9 @@
 // The two accumulation directions get a kernel each, so nothing is summed
 // with atomics and the results are deterministic; P and dS are recomputed in
 // both. Both kernels reuse the forward's gfx950 layouts:
-//   * dK/dV: a workgroup owns 128 keys (32 per wave) with K and V in registers
-//     in B-operand layout, and streams 64-row tiles of Q and dO (plus L and D)
-//     through LDS. S = Q K^T is computed with queries on the M axis and keys
+//   * dK/dV: a workgroup of 8 waves owns 256 keys (32 per wave) with K in
+//     registers in B-operand layout and V rows in LDS, and streams 64-row
+//     tiles of Q and dO (plus L and D) through LDS, shared by the 8 waves. S = Q K^T is computed with queries on the M axis and keys
 //     on N, so each lane holds 16 queries of ONE key; P and dS then serve
 //     directly as the B operands of dV^T += dO^T P and dK^T += Q^T dS, whose
 //     A operands are transposed reads (ds_read_b64_tr_b16) of the row-major
@@ -108,23 +108,27 @@ __device__ __forceinline__ void bwd_tile(int n_tiles, bool low_first, uint32_t& 
 }
 
 // ---------------------------------------------------------------- dK, dV
-constexpr int kBwdKeys = 128;  // keys per dK/dV workgroup (32 per wave)
-constexpr int kBwdRows = 64;   // query rows per streamed tile
+constexpr int kBwdWaves = 8;                // waves per dK/dV workgroup
+constexpr int kBwdKeys = 32 * kBwdWaves;     // keys per dK/dV workgroup (32 per wave)
+constexpr int kBwdRows = 64;                 // query rows per streamed tile
 
 template <typename T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kBwdWaves, 64 * kBwdWaves),
+                          amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                         const T* __restrict__ dout, const float* __restrict__ lse,
                         const float* __restrict__ delta, T* __restrict__ dk, T* __restrict__ dv, int N,
                         int n_kt, float scale, float c_log2)
 {
-    typedef Cfg<D, 4, 1> C;  // 64-row tiles copied by 256 threads, as the forward's K/V tiles
+    typedef Cfg<D, kBwdWaves, 1> C;  // 64-row copies by the whole workgroup, as the forward's tiles
     typedef typename Mma<T>::vec8 vec8;
     static_assert(C::BN == kBwdRows, "tile rows");
     constexpr int TILE = C::TILE;
-    // per buffer: Q tile, dO tile (TILE elements each), L and D (64 floats each)
+    // per buffer: Q tile, dO tile (TILE elements each), L and D (64 floats each);
+    // then the workgroup's V rows (kBwdKeys of them), read as B operands
     constexpr int BUF = 2 * TILE + 2 * kBwdRows * 2;  // in 2-byte units
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF + (kBwdKeys / kBwdRows) * TILE];
+    uint16_t* const vtile = smem + 2 * BUF;
 
     uint32_t bh, kt;
     bwd_tile<CAUSAL>(n_kt, true, bh, kt);
@@ -135,11 +139,11 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     const int64_t off = (int64_t)bh * N * D;
     const int kw0 = k0 + 32 * wave;  // this wave's first key
 
-    // K and V rows of this wave's keys in B-operand layout (rows >= N zero)
+    // K rows of this wave's keys in B-operand layout (rows >= N zero); V rows
+    // go to LDS once and are read per MFMA (registers hold two waves per SIMD)
     int krow[1];
-    vec8 kf[1][C::DS], vf[1][C::DS];
+    vec8 kf[1][C::DS];
     load_q<T, D, 1, C::DS>(k + off, kw0, N, l32, hh, krow, kf);
-    load_q<T, D, 1, C::DS>(v + off, kw0, N, l32, hh, krow, vf);
 
     f32x16 dk_acc[1][C::DB], dv_acc[1][C::DB];
 #pragma unroll
@@ -150,13 +154,17 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     const rsrc_t lrs = head_rsrc(lse + (int64_t)bh * N, row_bytes);
     const rsrc_t ers = head_rsrc(delta + (int64_t)bh * N, row_bytes);
     const uint32_t lane_off = tile_lane_offset<D>(wave, lane);
+    const rsrc_t vrs = head_rsrc(v + off, head_bytes);
+#pragma unroll
+    for (int i = 0; i < kBwdKeys / kBwdRows; ++i)
+        issue_tile<D, kBwdWaves, 1>(vtile + i * TILE, vrs, k0 + i * kBwdRows, wave, lane_off);
     auto qbuf = [&](int i) { return smem + (i & 1) * BUF; };
     auto dbuf = [&](int i) { return smem + (i & 1) * BUF + TILE; };
     auto lbuf = [&](int i) { return (float*)(smem + (i & 1) * BUF + 2 * TILE); };
     auto ebuf = [&](int i) { return (float*)(smem + (i & 1) * BUF + 2 * TILE) + kBwdRows; };
     auto issue = [&](int t) {
-        issue_tile<D, 4, 1>(qbuf(t), qrs, t * kBwdRows, wave, lane_off);
-        issue_tile<D, 4, 1>(dbuf(t), drs, t * kBwdRows, wave, lane_off);
+        issue_tile<D, kBwdWaves, 1>(qbuf(t), qrs, t * kBwdRows, wave, lane_off);
+        issue_tile<D, kBwdWaves, 1>(dbuf(t), drs, t * kBwdRows, wave, lane_off);
         if (wave == 0 && lane < 16) {  // 64 floats of L and of D: 16 lanes x 16 bytes
             copy16_to_lds(lrs, (uint16_t*)lbuf(t), (uint32_t)lane * 16, (uint32_t)t * kBwdRows * 4);
             copy16_to_lds(ers, (uint16_t*)ebuf(t), (uint32_t)lane * 16, (uint32_t)t * kBwdRows * 4);
@@ -179,14 +187,16 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
             if (CAUSAL && qbase + 31 < kw0) continue;  // every query of the block precedes every key
             // S = Q K^T and dP = dO V^T: queries on M, this wave's keys on N
             f32x16 s = (f32x16){}, dp = (f32x16){};
-            const int row = qb * 32 + l32;
+            const int row = qb * 32 + l32, vrow = 32 * wave + l32;
 #pragma unroll
             for (int dsx = 0; dsx < C::DS; ++dsx) {
                 const int chunk = ((2 * dsx + hh) ^ swz<D>(row)) * 8;
                 const vec8 aq = as_vec8<vec8>(*(const u32x4*)(qs + row * D + chunk));
                 const vec8 ad = as_vec8<vec8>(*(const u32x4*)(ds + row * D + chunk));
+                const vec8 bv = as_vec8<vec8>(
+                    *(const u32x4*)(vtile + vrow * D + ((2 * dsx + hh) ^ swz<D>(vrow)) * 8));
                 s = Mma<T>::run(aq, kf[0][dsx], s);
-                dp = Mma<T>::run(ad, vf[0][dsx], dp);
+                dp = Mma<T>::run(ad, bv, dp);
             }
             // register r holds query qb*32 + 8*(r/4) + 4*hh + (r%4) of the tile
             vec8 pk[2], dsk[2];
@@ -210,6 +220,9 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
             const vec8 d1[1][2] = {{dsk[0], dsk[1]}};
             pv_tile<T, D, 1, C::DB, 2>(p1, ds + qb * 32 * D, dv_acc, lane, hh);
             pv_tile<T, D, 1, C::DB, 2>(d1, qs + qb * 32 * D, dk_acc, lane, hh);
+            // keep the two query blocks apart: interleaved they need more
+            // registers than two waves per SIMD have
+            __builtin_amdgcn_sched_barrier(0);
         }
         stage_barrier();
     }
@@ -219,7 +232,7 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
 
 // ---------------------------------------------------------------- dQ
 template <typename T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                       const T* __restrict__ dout, const float* __restrict__ lse,
                       const float* __restrict__ delta, T* __restrict__ dq, int N, int n_qt, float scale,
@@ -300,7 +313,7 @@ hipError_t launch_bwd_typed(const void* q, const void* k, const void* v, const v
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_kt = (N + kBwdKeys - 1) / kBwdKeys;
-    dim3 g1((unsigned)((int64_t)n_kt * BH)), b1(256);
+    dim3 g1((unsigned)((int64_t)n_kt * BH)), b1(64 * kBwdWaves);
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, CAUSAL>), g1, b1, 0, stream, (const T*)q, (const T*)k,
                        (const T*)v, (const T*)dout, lse, (const float*)delta, (T*)dk, (T*)dv, N, n_kt, scale,
                        c_log2);
