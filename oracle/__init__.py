@@ -44,11 +44,12 @@ def build_all():
 
 
 def _bind(lib):
-    fn = lib.fa_oracle_fwd_qk
+    fn = lib.fa_oracle_fwd_masked
     fn.restype = ctypes.c_int
     fn.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 5 + [
-        ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
-        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_double,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int]
     return lib
 
 
@@ -83,7 +84,8 @@ def _as_f32(x):
     return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
 
 
-def attention_fwd(q, k, v, causal, scale, rows=None, tile_n=0, nthreads=None, lib=None):
+def attention_fwd(q, k, v, causal, scale, rows=None, tile_n=0, nthreads=None, lib=None,
+                  window_left=-1, window_right=-1, key_lens=None):
     """fp64 attention forward on the CPU.
 
     q       : ``[B, H, Nq, d]``; k, v: ``[B, H, Nk, d]`` (torch or numpy; values
@@ -92,6 +94,9 @@ def attention_fwd(q, k, v, causal, scale, rows=None, tile_n=0, nthreads=None, li
               alignment when Nq != Nk).
     rows    : optional sorted list of query rows to evaluate (all by default).
     tile_n  : 0 for the two-pass definition, > 0 for the online order.
+    window_left, window_right, key_lens : the masks of ``fa_oracle_fwd_masked``
+              (-1 = unbounded; key_lens a length-B sequence or None). A row
+              with no visible key gets O = 0 and lse = -inf.
     Returns ``(o, lse)`` as float64 numpy arrays of shape ``[B, H, R, d]`` and
     ``[B, H, R]``, where ``R`` is ``len(rows)`` or ``Nq``; lse is natural-log.
     """
@@ -107,8 +112,12 @@ def attention_fwd(q, k, v, causal, scale, rows=None, tile_n=0, nthreads=None, li
         R, rows_ptr = rows_arr.size, rows_arr.ctypes.data
     o = np.empty((B, H, R, d), dtype=np.float64)
     lse = np.empty((B, H, R), dtype=np.float64)
-    rc = lib.fa_oracle_fwd_qk(qf.ctypes.data, kf.ctypes.data, vf.ctypes.data, B, H, N, Nk, d,
-                           1 if causal else 0, float(scale), rows_ptr,
+    kl = None if key_lens is None else np.ascontiguousarray(np.asarray(key_lens, dtype=np.int64))
+    if kl is not None:
+        assert kl.shape == (B,)
+    rc = lib.fa_oracle_fwd_masked(qf.ctypes.data, kf.ctypes.data, vf.ctypes.data, B, H, N, Nk, d,
+                           1 if causal else 0, int(window_left), int(window_right),
+                           None if kl is None else kl.ctypes.data, float(scale), rows_ptr,
                            0 if rows_arr is None else R, int(tile_n), o.ctypes.data,
                            lse.ctypes.data, int(nthreads or default_threads()))
     if rc != 0:

@@ -23,7 +23,19 @@
  * bounds keys by the key count, so with Nq != Nk the diagonal starts at the
  * top-left corner (row i >= Nk sees every key). Mismatched query and key
  * lengths are the shapes "Programming an attention kernel in Triton"
- * validates in "Kernel 4". The per-row
+ * validates in "Kernel 4".
+ *
+ * Masks (fa_oracle_fwd_masked). "How to optimise a Triton FlashAttention-2
+ * kernel step by step with a profiler", section "Future articles", notes that
+ * a kernel with padding masks or sliding windows must handle rows with no
+ * visible key, which its finite mask sentinel does not. Here a key is visible to row i
+ * of batch b iff j < key_len[b] (padding), j >= i - window_left (when
+ * window_left >= 0) and j <= i (causal) or j <= i + window_right (when not
+ * causal and window_right >= 0). The visible keys of a row are one
+ * contiguous range. A row with none has O = 0 and lse = -infinity (the sum
+ * of no exponentials), which is the rule this oracle fixes for that case.
+ *
+ * The per-row
  * logsumexp is stored in natural-log units (same page, Round 4, "exp2": the
  * kernel converts its base-2 state back because its tests compare against a
  * natural-log logsumexp).
@@ -57,6 +69,8 @@ typedef struct {
     int causal;
     double scale;
     const int64_t *rows; /* NULL: all rows 0..N-1 */
+    int64_t win_left, win_right; /* -1: unbounded */
+    const int64_t *key_lens;     /* NULL: every batch has Nk keys */
     int64_t n_rows;      /* rows per (b, h) in the output */
     int64_t tile_n;      /* 0: two-pass; > 0: online over key tiles */
     double *o, *lse;
@@ -80,6 +94,21 @@ static double score(const float *qi, const float *kj, int64_t d, double scale)
 static int64_t visible_keys(int64_t i, int64_t Nk, int causal)
 {
     return causal ? (i + 1 < Nk ? i + 1 : Nk) : Nk;
+}
+
+/* The visible keys [*lo, *hi) of row i under the masks (see the header). */
+static void visible_range(const job_t *job, int64_t b, int64_t i, int64_t *lo, int64_t *hi)
+{
+    int64_t h = visible_keys(i, job->Nk, job->causal);
+    if (!job->causal && job->win_right >= 0 && i + job->win_right + 1 < h)
+        h = i + job->win_right + 1;
+    if (job->key_lens && job->key_lens[b] < h)
+        h = job->key_lens[b];
+    int64_t l = 0;
+    if (job->win_left >= 0 && i - job->win_left > 0)
+        l = i - job->win_left;
+    *lo = l;
+    *hi = h > l ? h : l;
 }
 
 /* The plain definition, evaluated in two passes over the scores. */
@@ -179,11 +208,24 @@ static void *worker(void *arg)
             int64_t nvis = visible_keys(i, Nk, job->causal);
             double *o_row = job->o + (bh * job->n_rows + r) * d;
             double *lse_out = job->lse + bh * job->n_rows + r;
+            int64_t k_lo = 0;
+            if (job->win_left >= 0 || job->win_right >= 0 || job->key_lens) {
+                int64_t k_hi;
+                visible_range(job, bh / job->H, i, &k_lo, &k_hi);
+                nvis = k_hi - k_lo;
+                if (nvis == 0) { /* no visible key: O = 0, lse = -inf */
+                    for (int64_t c = 0; c < d; ++c)
+                        o_row[c] = 0.0;
+                    *lse_out = -INFINITY;
+                    continue;
+                }
+            }
+            const float *kv0 = kh + k_lo * d, *vv0 = vh + k_lo * d;
             if (job->tile_n > 0)
-                row_online(qh + i * d, kh, vh, nvis, d, job->scale, job->tile_n, s, o_row,
+                row_online(qh + i * d, kv0, vv0, nvis, d, job->scale, job->tile_n, s, o_row,
                            lse_out);
             else
-                row_two_pass(qh + i * d, kh, vh, nvis, d, job->scale, s, o_row, lse_out);
+                row_two_pass(qh + i * d, kv0, vv0, nvis, d, job->scale, s, o_row, lse_out);
         }
     }
     free(s);
@@ -200,11 +242,38 @@ static void *worker(void *arg)
  *   tile_n  : 0 for the two-pass definition, > 0 for the online order.
  * Returns 0 on success, -1 on a bad argument, -2 when memory runs out.
  */
+int fa_oracle_fwd_masked(const float *q, const float *k, const float *v, int64_t B, int64_t H,
+                         int64_t Nq, int64_t Nk, int64_t d, int causal, int64_t window_left,
+                         int64_t window_right, const int64_t *key_lens, double scale,
+                         const int64_t *rows, int64_t n_rows, int64_t tile_n, double *o,
+                         double *lse, int nthreads);
+
 int fa_oracle_fwd_qk(const float *q, const float *k, const float *v, int64_t B, int64_t H,
                      int64_t Nq, int64_t Nk, int64_t d, int causal, double scale,
                      const int64_t *rows, int64_t n_rows, int64_t tile_n, double *o, double *lse,
                      int nthreads)
 {
+    return fa_oracle_fwd_masked(q, k, v, B, H, Nq, Nk, d, causal, -1, -1, NULL, scale, rows,
+                                n_rows, tile_n, o, lse, nthreads);
+}
+
+/*
+ * fa_oracle_fwd_masked: fa_oracle_fwd_qk with the masks of the header:
+ * window_left / window_right (-1: unbounded; window_right is not used when
+ * causal) and key_lens ([B] key counts, each in 0..Nk, or NULL).
+ */
+int fa_oracle_fwd_masked(const float *q, const float *k, const float *v, int64_t B, int64_t H,
+                         int64_t Nq, int64_t Nk, int64_t d, int causal, int64_t window_left,
+                         int64_t window_right, const int64_t *key_lens, double scale,
+                         const int64_t *rows, int64_t n_rows, int64_t tile_n, double *o,
+                         double *lse, int nthreads)
+{
+    if (window_left < -1 || window_right < -1)
+        return -1;
+    if (key_lens)
+        for (int64_t b = 0; b < B; ++b)
+            if (key_lens[b] < 0 || key_lens[b] > Nk)
+                return -1;
     if (!q || !k || !v || !o || !lse || B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1 ||
         tile_n < 0)
         return -1;
@@ -228,6 +297,9 @@ int fa_oracle_fwd_qk(const float *q, const float *k, const float *v, int64_t B, 
     job.H = H;
     job.Nq = Nq;
     job.Nk = Nk;
+    job.win_left = window_left;
+    job.win_right = window_right;
+    job.key_lens = key_lens;
     job.d = d;
     job.causal = causal ? 1 : 0;
     job.scale = scale;

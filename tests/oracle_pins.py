@@ -32,6 +32,15 @@ What pins what:
                        square problem (the diagonal starts at the top left)
   qk_rows_past_keys    causal Nq > Nk: every row i >= Nk - 1 sees all keys and
                        equals the non-causal row
+  masked_decimal       padding and sliding-window masks against the definition
+                       at 50 digits, including rows with no visible key
+                       (O = 0, lse = -inf)
+  masked_torch         the same masks as an explicit boolean matrix built with
+                       broadcast comparisons, fp64 masked softmax in torch
+  padding_is_truncation  a padding length L per batch equals attention over
+                       the first L keys only, bit for bit
+  wide_window_is_none  a window at least as wide as the keys equals no window,
+                       bit for bit
 """
 
 from decimal import Decimal, getcontext
@@ -56,9 +65,17 @@ def _close(a, b, rtol, what):
     assert err <= rtol, f"{what}: max scaled error {err:.3e} > {rtol:.1e}"
 
 
-def _decimal_attention(q, k, v, causal, scale):
+def _visible(i, Nk, causal, wl=-1, wr=-1, klen=None):
+    """Visible keys of row i as a Python list, straight from the mask rules."""
+    return [j for j in range(Nk)
+            if (klen is None or j < klen) and (wl < 0 or j >= i - wl)
+            and (j <= i if causal else (wr < 0 or j <= i + wr))]
+
+
+def _decimal_attention(q, k, v, causal, scale, wl=-1, wr=-1, klen=None):
     """Attention of one head, q [Nq, d] and k, v [Nk, d] float inputs, evaluated in
-    50-digit decimal. A causal row i sees keys j <= i."""
+    50-digit decimal. A causal row i sees keys j <= i; a row with no visible key
+    gives O = 0 and lse = -inf."""
     getcontext().prec = 50
     N, d = q.shape
     Nk = k.shape[0]
@@ -69,7 +86,10 @@ def _decimal_attention(q, k, v, causal, scale):
     o = np.zeros((N, d))
     lse = np.zeros(N)
     for i in range(N):
-        J = range(min(i + 1, Nk)) if causal else range(Nk)
+        J = _visible(i, Nk, causal, wl, wr, klen)
+        if not J:
+            lse[i] = -np.inf
+            continue
         s = [sc * sum(Q[i][c] * K[j][c] for c in range(d)) for j in J]
         e = [x.exp() for x in s]
         den = sum(e)
@@ -302,7 +322,80 @@ def qk_rows_past_keys(fwd):
     assert not np.array_equal(o_c[:, :, :Nk - 1], o_n[:, :, :Nk - 1])
 
 
+# (B, H, Nq, Nk, d, causal, window_left, window_right, key_lens)
+MASK_CASES = [
+    (2, 1, 9, 9, 4, True, 3, -1, [9, 5]),       # causal sliding window, one batch padded
+    (1, 2, 7, 12, 3, False, 2, 1, None),        # banded, Nq < Nk
+    (2, 1, 8, 6, 4, False, -1, -1, [0, 4]),     # a fully padded batch: no visible key anywhere
+    (1, 1, 10, 10, 2, True, 0, -1, None),       # window 0: each row sees itself only
+    (1, 1, 6, 10, 3, False, 1, 0, [3]),         # rows past the padding see nothing
+]
+
+
+def masked_decimal(fwd):
+    for seed, (B, H, Nq, Nk, d, causal, wl, wr, kl) in enumerate(MASK_CASES):
+        q, k, v = _qk_inputs(B, H, Nq, Nk, d, "fp16", 700 + 2 * seed)
+        scale = 0.3
+        o, lse = fwd(q, k, v, causal, scale, window_left=wl, window_right=wr, key_lens=kl)
+        for b in range(B):
+            for h in range(H):
+                od, ld = _decimal_attention(_f(q[b, h]), _f(k[b, h]), _f(v[b, h]), causal, scale,
+                                            wl, wr, None if kl is None else kl[b])
+                fin = np.isfinite(ld)
+                assert np.array_equal(np.isfinite(lse[b, h]), fin), f"masked rows differ {seed}"
+                assert np.all(lse[b, h][~fin] == -np.inf) and np.all(o[b, h][~fin] == 0.0)
+                _close(o[b, h], od, 1e-14, f"masked decimal O case {seed}")
+                _close(lse[b, h][fin], ld[fin], 1e-14, f"masked decimal lse case {seed}")
+
+
+def masked_torch(fwd):
+    B, H, Nq, Nk, d = 2, 2, 70, 90, 16
+    q, k, v = _qk_inputs(B, H, Nq, Nk, d, "bf16", 720)
+    i = torch.arange(Nq)[:, None]
+    j = torch.arange(Nk)[None, :]
+    for causal, wl, wr, kl in [(True, 20, -1, [90, 33]), (False, 5, 9, [60, 90]), (False, -1, -1, [1, 0])]:
+        allow = torch.ones(B, Nq, Nk, dtype=torch.bool)
+        if wl >= 0:
+            allow &= (j >= i - wl)[None]
+        allow &= (j <= i)[None] if causal else ((j <= i + wr)[None] if wr >= 0 else True)
+        allow &= torch.arange(Nk)[None, None, :] < torch.tensor(kl)[:, None, None]
+        s = torch.matmul(q.double(), k.double().transpose(-1, -2).contiguous()) * 0.25
+        s = s.masked_fill(~allow[:, None], float("-inf"))
+        lse_t = torch.logsumexp(s, dim=-1)
+        p = torch.exp(s - lse_t[..., None]).nan_to_num(0.0)
+        o_t = torch.matmul(p, v.double())
+        o, lse = fwd(q, k, v, causal, 0.25, window_left=wl, window_right=wr, key_lens=kl)
+        _close(o, o_t.numpy(), 1e-12, f"masked torch O causal={causal} wl={wl} wr={wr}")
+        fin = np.isfinite(lse_t.numpy())
+        assert np.array_equal(np.isfinite(lse), fin)
+        _close(lse[fin], lse_t.numpy()[fin], 1e-12, f"masked torch lse causal={causal}")
+
+
+def padding_is_truncation(fwd):
+    B, H, Nq, Nk, d = 3, 2, 40, 50, 16
+    q, k, v = _qk_inputs(B, H, Nq, Nk, d, "fp16", 740)
+    kl = [50, 17, 1]
+    for causal in (False, True):
+        o, lse = fwd(q, k, v, causal, 0.25, key_lens=kl)
+        for b, L in enumerate(kl):
+            o_t, lse_t = fwd(q[b:b + 1], k[b:b + 1, :, :L].contiguous(), v[b:b + 1, :, :L].contiguous(),
+                             causal, 0.25)
+            assert np.array_equal(o[b:b + 1], o_t) and np.array_equal(lse[b:b + 1], lse_t), \
+                f"padding to {L} keys differs from truncation causal={causal}"
+
+
+def wide_window_is_none(fwd):
+    q, k, v = _qk_inputs(1, 2, 33, 45, 8, "bf16", 750)
+    for causal in (False, True):
+        o, lse = fwd(q, k, v, causal, 0.25)
+        o_w, lse_w = fwd(q, k, v, causal, 0.25, window_left=45, window_right=45)
+        assert np.array_equal(o, o_w) and np.array_equal(lse, lse_w)
+        o_n, _ = fwd(q, k, v, causal, 0.25, window_left=3)
+        assert not np.array_equal(o, o_n)
+
+
 ALL_PINS = [decimal_bruteforce, torch_sdpa, keys_zero, causal_row0, causal_last_row,
             prefix_truncation, v_ones, v_identity, online_equals_twopass, linearity,
             permutation, single_key, shift, qk_decimal_bruteforce, qk_torch_sdpa,
-            qk_square_prefix, qk_rows_past_keys]
+            qk_square_prefix, qk_rows_past_keys, masked_decimal, masked_torch,
+            padding_is_truncation, wide_window_is_none]

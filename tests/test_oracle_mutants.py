@@ -34,6 +34,14 @@ MUTANTS = [
     ("online_sum_not_rescaled", [("l *= alpha;", "l *= 1.0;")]),
     ("online_alpha_inverted", [("exp(m - m_new)", "exp(m_new - m)")]),
     ("online_output_not_rescaled", [("o_row[c] *= alpha;", "o_row[c] *= 1.0;")]),
+    ("window_left_off_by_one", [("l = i - job->win_left;", "l = i - job->win_left + 1;")]),
+    ("window_right_off_by_one", [("h = i + job->win_right + 1;", "h = i + job->win_right;")]),
+    ("padding_ignored", [("h = job->key_lens[b];", "h = h;")]),
+    ("padding_of_first_batch", [("visible_range(job, bh / job->H, i, &k_lo, &k_hi);",
+                                 "visible_range(job, 0, i, &k_lo, &k_hi);")]),
+    ("window_keys_not_offset", [("const float *kv0 = kh + k_lo * d, *vv0 = vh + k_lo * d;",
+                                 "const float *kv0 = kh, *vv0 = vh;")]),
+    ("empty_row_lse_zero", [("*lse_out = -INFINITY;", "*lse_out = 0.0;")]),
 ]
 
 
