@@ -128,6 +128,42 @@ int fa_fwd_split_qk(const void *q, const void *k, const void *v, void *o, float 
                     void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * Padding masks and sliding windows. "How to optimise a Triton
+ * FlashAttention-2 kernel step by step with a profiler", section "Future
+ * articles", names them as the case where a query row can be left with no
+ * visible key, which a finite mask sentinel gets wrong. Row i of batch b sees
+ * key j iff
+ *   j < key_lens[b]                         (padding; all Nk keys when NULL),
+ *   j >= i - window_left                    (when window_left >= 0),
+ *   j <= i             when causal,
+ *   j <= i + window_right when not causal   (when window_right >= 0).
+ * -1 leaves a window unbounded; window_right is not used when causal. A row
+ * that sees no key gets O = 0 and lse = -infinity (the logsumexp of an empty
+ * set), never NaN. Only the key tiles some row of a query tile can see are
+ * visited, and only tiles at the edges of the visible band get the mask.
+ *
+ * fa_fwd_masked -- arguments as fa_fwd_qk, plus:
+ *   window_left, window_right : >= -1.
+ *   key_lens : device, [B] int32, 4-byte aligned, or NULL. Read by the kernel;
+ *              values outside [0, Nk] are clamped into it. It must not
+ *              overlap o or lse.
+ * With no mask in effect (key_lens NULL, window_left -1, and causal or
+ * window_right -1) the call is fa_fwd_qk.
+ *
+ * fa_fwd_split_masked -- the split-key launch of fa_fwd_split_qk with the same
+ *   masks (KV-cache decode over batches of different cache lengths). Split
+ *   count, workspace and ordering rules as fa_fwd_split_qk; key_lens must not
+ *   overlap the workspace either.
+ */
+int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                  int Nq, int Nk, int d, int causal, int window_left, int window_right,
+                  const int32_t *key_lens, float scale, int dtype, void *stream);
+int fa_fwd_split_masked(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                        int H, int Nq, int Nk, int d, int causal, int window_left, int window_right,
+                        const int32_t *key_lens, float scale, int dtype, int n_splits,
+                        void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * fa_bwd -- attention backward pass: the gradients of sum(dO * O) with respect
  * to q, k and v, where O = fa_fwd(q, k, v) with the same causal flag and
  * scale. "How to optimise a Triton FlashAttention-2 kernel step by step with
@@ -186,6 +222,15 @@ int fa_tile_counts(int64_t N, int block_m, int block_n, int causal, int64_t coun
 int fa_tile_counts_qk(int64_t Nq, int64_t Nk, int block_m, int block_n, int causal,
                       int64_t counts[4]);
 
+/* fa_tile_counts_masked -- the same for one batch under the masks of
+ * fa_fwd_masked with key_len keys (0 <= key_len <= Nk): counts[1] the visited
+ * pairs (key tiles holding a key some row of the query tile sees), counts[2]
+ * those every row of the query tile sees in full (no mask), counts[3] the
+ * rest. */
+int fa_tile_counts_masked(int64_t Nq, int64_t Nk, int block_m, int block_n, int causal,
+                          int64_t window_left, int64_t window_right, int64_t key_len,
+                          int64_t counts[4]);
+
 /* Launch plan of fa_fwd for a problem (host only, no HIP call). */
 typedef struct {
     int block_m;            /* query rows per workgroup */
@@ -214,6 +259,14 @@ int fa_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t *plan);
 
 /* fa_plan_qk -- the plan of fa_fwd_qk; fa_plan is the case Nq = Nk = N. */
 int fa_plan_qk(int B, int H, int Nq, int Nk, int d, int causal, int dtype, fa_plan_t *plan);
+
+/* fa_plan_masked -- the plan of fa_fwd_masked. key_lens is a HOST array of B
+ * values in [0, Nk] (or NULL). Here algo_flops is 4*d per visible (query,
+ * key) pair counted exactly (the diagonal included), and algo_bytes reads q
+ * and writes o and lse once and reads each key and value row that some row
+ * sees once. */
+int fa_plan_masked(int B, int H, int Nq, int Nk, int d, int causal, int window_left, int window_right,
+                   const int32_t *key_lens, int dtype, fa_plan_t *plan);
 
 #ifdef __cplusplus
 }

@@ -221,3 +221,130 @@ def test_plan_qk_flops_and_bytes(lib):
         assert nc["algo_bytes"] == 2 * B * H * d * (2 * Nq + 2 * Nk) + 4 * B * H * Nq
         assert nc["workgroups"] == B * H * -(-Nq // nc["block_m"])
     assert fa.fa_plan_qk(4, 8, 4096, 4096, 64, 1, 1) == fa.fa_plan(4, 8, 4096, 64, 1, 1)
+
+
+# ---- padding lengths and sliding windows (fa_fwd_masked, fa_fwd_split_masked,
+# fa_tile_counts_masked, fa_plan_masked)
+
+def _visible_matrix(Nq, Nk, causal, wl, wr, klen):
+    """[Nq, Nk] booleans straight from the mask rules."""
+    import numpy as np
+    i = np.arange(Nq)[:, None]
+    j = np.arange(Nk)[None, :]
+    vis = np.broadcast_to(j < klen, (Nq, Nk)).copy()
+    if wl >= 0:
+        vis = vis & (j >= i - wl)
+    if causal:
+        vis = vis & (j <= i)
+    elif wr >= 0:
+        vis = vis & (j <= i + wr)
+    return vis
+
+
+MASK_GRID = [(Nq, Nk, causal, wl, wr, klen, bm)
+             for (Nq, Nk) in [(1, 1), (5, 300), (257, 130), (300, 513), (640, 640)]
+             for causal in (0, 1)
+             for (wl, wr) in [(-1, -1), (0, -1), (63, 5), (100, 0), (200, 150)]
+             for klen in sorted({Nk, 0, 1, Nk // 2})
+             for bm in (128, 256)]
+
+
+@pytest.mark.parametrize("Nq,Nk,causal,wl,wr,klen,bm", MASK_GRID)
+def test_tile_counts_masked_are_exact(lib, Nq, Nk, causal, wl, wr, klen, bm):
+    """Visited key tiles are exactly those holding a visible key of some row of the
+    query tile; unmasked ones are exactly those every row of the tile sees in full."""
+    bn = 64
+    vis = _visible_matrix(Nq, Nk, causal, wl, wr, klen)
+    n_qt, n_kt = -(-Nq // bm), -(-Nk // bn)
+    visited = unmasked = 0
+    for qt in range(n_qt):
+        rows = vis[qt * bm:(qt + 1) * bm]
+        for kt in range(n_kt):
+            block = rows[:, kt * bn:(kt + 1) * bn]
+            visited += bool(block.any())
+            unmasked += bool(block.all()) and (kt + 1) * bn <= Nk
+    total, v, u, m = fa.fa_tile_counts_masked(Nq, Nk, bm, bn, causal, wl, wr, klen)
+    assert (total, v, u, m) == (n_qt * n_kt, visited, unmasked, visited - unmasked)
+
+
+def test_tile_counts_masked_without_masks_visit_what_fa_tile_counts_visits(lib):
+    for Nq, Nk in [(1000, 1000), (300, 1000), (1000, 300), (4096, 4096)]:
+        for causal in (0, 1):
+            plain = fa.fa_tile_counts_qk(Nq, Nk, 128, 64, causal)
+            masked = fa.fa_tile_counts_masked(Nq, Nk, 128, 64, causal, -1, -1, Nk)
+            assert masked[:2] == plain[:2]
+            assert masked[2] >= plain[2]  # the masked split is exact, the plain one conservative
+
+
+def test_plan_masked_counts_visible_pairs_and_keys(lib):
+    B, H, d = 3, 2, 64
+    for Nq, Nk, causal, wl, wr, kls in [(300, 513, 0, 63, 5, [513, 100, 0]),
+                                        (257, 130, 1, 200, -1, [130, 1, 65]),
+                                        (640, 640, 1, 100, -1, None),
+                                        (64, 4096, 0, -1, -1, [4096, 2048, 17])]:
+        plan = fa.fa_plan_masked(B, H, Nq, Nk, d, causal, wl, wr, kls, fa.FA_DTYPE_BF16)
+        pairs = keys = 0
+        for b in range(B):
+            vis = _visible_matrix(Nq, Nk, causal, wl, wr, Nk if kls is None else kls[b])
+            pairs += int(vis.sum())
+            keys += int(vis.any(axis=0).sum())
+        assert plan["algo_flops"] == 4 * H * pairs * d
+        assert plan["algo_bytes"] == 4 * H * (B * Nq + keys) * d + 4 * B * H * Nq
+        tiles = sum(fa.fa_tile_counts_masked(Nq, Nk, plan["block_m"], 64, causal, wl, wr,
+                                             Nk if kls is None else kls[b])[1] for b in range(B))
+        assert plan["pairs_visited"] == H * tiles
+        assert plan["mfma_flops"] == 4 * d * plan["block_m"] * 64 * plan["pairs_visited"]
+
+
+def test_plan_masked_shape(lib):
+    # masked d = 128 keeps 128-row workgroups; d = 64 takes the unmasked choice
+    p128 = fa.fa_plan_masked(4, 16, 4096, 4096, 128, 0, -1, -1, [4096] * 4, fa.FA_DTYPE_BF16)
+    assert (p128["block_m"], p128["threads"]) == (128, 256)
+    p64 = fa.fa_plan_masked(4, 16, 4096, 4096, 64, 0, -1, -1, [4096] * 4, fa.FA_DTYPE_BF16)
+    assert (p64["block_m"], p64["threads"]) == (256, 512)
+    # no mask in effect: the unmasked launch and its plan
+    off = fa.fa_plan_masked(4, 16, 4096, 4096, 128, 1, -1, 7, None, fa.FA_DTYPE_BF16)
+    assert off["block_m"] == fa.fa_plan_qk(4, 16, 4096, 4096, 128, 1, 1)["block_m"]
+    with pytest.raises(fa.FaError):
+        fa.fa_plan_masked(2, 1, 64, 64, 64, 0, -1, -1, [64, 65], fa.FA_DTYPE_BF16)
+    with pytest.raises(fa.FaError):
+        fa.fa_plan_masked(1, 1, 64, 64, 64, 0, -2, -1, None, fa.FA_DTYPE_BF16)
+
+
+KL = 0x60000  # fake 4-byte aligned device address for key_lens
+
+
+def call_masked(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, H=1, Nq=16, Nk=48, d=64, causal=0,
+             wl=-1, wr=-1, kl=KL, scale=0.125, dtype=fa.FA_DTYPE_BF16, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                            a["Nk"], a["d"], a["causal"], a["wl"], a["wr"], a["kl"], a["scale"],
+                            a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(wl=-2), dict(wr=-5), dict(kl=KL + 2),            # bad window, misaligned key_lens
+    dict(kl=P[3] + 8), dict(kl=P[4]),                     # key_lens inside o or lse
+    dict(Nk=0), dict(q=None), dict(scale=0.0),
+])
+def test_fa_fwd_masked_rejects_before_any_hip_call(lib, kw):
+    assert call_masked(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+def test_fa_fwd_split_masked_rejects_before_any_hip_call(lib):
+    ws = 0x100000
+    base = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, H=1, Nq=16, Nk=4096, d=64,
+                causal=0, wl=-1, wr=-1, kl=KL, scale=0.125, dtype=fa.FA_DTYPE_BF16, n=4,
+                ws=ws, wsb=fa.fa_split_workspace_bytes(2, 1, 16, 64, 4))
+
+    def run(**kw):
+        a = dict(base)
+        a.update(kw)
+        return fa.fa_fwd_split_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                      a["Nq"], a["Nk"], a["d"], a["causal"], a["wl"], a["wr"],
+                                      a["kl"], a["scale"], a["dtype"], a["n"], a["ws"], a["wsb"],
+                                      None)
+    for kw in [dict(wl=-3), dict(n=0), dict(n=65), dict(ws=None), dict(wsb=base["wsb"] - 4),
+               dict(kl=ws + 64), dict(ws=ws + 8)]:
+        assert run(**kw) == fa.FA_ERR_INVALID_ARG, kw

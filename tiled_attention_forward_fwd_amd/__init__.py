@@ -8,9 +8,9 @@ functions here raise.
     o, lse = fwd(q, k, v, causal=False, scale=None)
 
 q is ``[B, H, Nq, d]`` and k, v are ``[B, H, Nk, d]``; Nq may differ from Nk
-(a causal row i sees keys j <= i). The C entry points are exposed under
-their own names (``fa_fwd``, ``fa_fwd_qk``, ``fa_status_string``,
-``fa_tile_counts``, ``fa_tile_counts_qk``, ``fa_plan``, ``fa_plan_qk``) for
+(a causal row i sees keys j <= i). ``fwd`` also takes padding lengths and
+sliding windows (``key_lens``, ``window_left``, ``window_right``). The C
+entry points are exposed under their own names (those in ``EXPORTED``) for
 callers that manage their own buffers.
 """
 
@@ -26,8 +26,8 @@ FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1
 
 # Entry points declared in include/fa.h.
 EXPORTED = ("fa_fwd", "fa_fwd_qk", "fa_fwd_split_qk", "fa_split_count", "fa_split_workspace_bytes",
-            "fa_bwd", "fa_status_string", "fa_tile_counts", "fa_tile_counts_qk", "fa_plan",
-            "fa_plan_qk")
+            "fa_fwd_masked", "fa_fwd_split_masked", "fa_bwd", "fa_status_string", "fa_tile_counts",
+            "fa_tile_counts_qk", "fa_tile_counts_masked", "fa_plan", "fa_plan_qk", "fa_plan_masked")
 
 
 class FaPlan(ctypes.Structure):
@@ -68,6 +68,20 @@ def load_library(path=LIB_PATH):
     lib.fa_fwd_split_qk.restype = ctypes.c_int
     lib.fa_fwd_split_qk.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.fa_fwd_masked.restype = ctypes.c_int
+    lib.fa_fwd_masked.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 8 + [
+        ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_fwd_split_masked.restype = ctypes.c_int
+    lib.fa_fwd_split_masked.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 8 + [
+        ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_void_p]
+    lib.fa_tile_counts_masked.restype = ctypes.c_int
+    lib.fa_tile_counts_masked.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.POINTER(ctypes.c_int64)]
+    lib.fa_plan_masked.restype = ctypes.c_int
+    lib.fa_plan_masked.argtypes = [ctypes.c_int] * 8 + [ctypes.c_void_p, ctypes.c_int,
+                                                        ctypes.POINTER(FaPlan)]
     lib.fa_split_count.restype = ctypes.c_int
     lib.fa_split_count.argtypes = [ctypes.c_int] * 6
     lib.fa_split_workspace_bytes.restype = ctypes.c_int64
@@ -119,6 +133,44 @@ def fa_fwd_split_qk(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, n_sp
     return load_library().fa_fwd_split_qk(q, k, v, o, lse, int(B), int(H), int(Nq), int(Nk), int(d),
                                           int(causal), float(scale), int(dtype), int(n_splits),
                                           workspace, int(workspace_bytes), stream)
+
+
+def fa_fwd_masked(q, k, v, o, lse, B, H, Nq, Nk, d, causal, window_left, window_right, key_lens,
+                  scale, dtype, stream):
+    """Direct call of the C entry point with raw pointers (ints; key_lens a device
+    pointer or None); returns the status."""
+    return load_library().fa_fwd_masked(q, k, v, o, lse, int(B), int(H), int(Nq), int(Nk), int(d),
+                                        int(causal), int(window_left), int(window_right), key_lens,
+                                        float(scale), int(dtype), stream)
+
+
+def fa_fwd_split_masked(q, k, v, o, lse, B, H, Nq, Nk, d, causal, window_left, window_right,
+                        key_lens, scale, dtype, n_splits, workspace, workspace_bytes, stream):
+    """Direct call of the C entry point with raw pointers (ints); returns the status."""
+    return load_library().fa_fwd_split_masked(q, k, v, o, lse, int(B), int(H), int(Nq), int(Nk),
+                                              int(d), int(causal), int(window_left),
+                                              int(window_right), key_lens, float(scale), int(dtype),
+                                              int(n_splits), workspace, int(workspace_bytes), stream)
+
+
+def fa_tile_counts_masked(Nq, Nk, block_m, block_n, causal, window_left, window_right, key_len):
+    """fa_tile_counts for one batch under padding and window masks."""
+    out = (ctypes.c_int64 * 4)()
+    _check(load_library().fa_tile_counts_masked(int(Nq), int(Nk), int(block_m), int(block_n),
+                                                int(causal), int(window_left), int(window_right),
+                                                int(key_len), out))
+    return tuple(out)
+
+
+def fa_plan_masked(B, H, Nq, Nk, d, causal, window_left, window_right, key_lens, dtype):
+    """The plan of fa_fwd_masked; key_lens is a host sequence of B ints or None."""
+    plan = FaPlan()
+    arr = None if key_lens is None else (ctypes.c_int32 * int(B))(*[int(x) for x in key_lens])
+    _check(load_library().fa_plan_masked(int(B), int(H), int(Nq), int(Nk), int(d), int(causal),
+                                         int(window_left), int(window_right),
+                                         None if arr is None else ctypes.addressof(arr), int(dtype),
+                                         ctypes.byref(plan)))
+    return plan.as_dict()
 
 
 def fa_split_count(B, H, Nq, Nk, d, causal):
@@ -215,7 +267,7 @@ def default_scale(d):
 
 
 def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None, splits=None,
-        workspace=None):
+        workspace=None, window_left=-1, window_right=-1, key_lens=None):
     """Attention forward on the GPU: returns ``(o, lse)``.
 
     q       : CUDA (HIP) tensor ``[B, H, Nq, d]``; k, v: ``[B, H, Nk, d]``;
@@ -228,6 +280,10 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None, spli
               takes ``fa_split_count``'s suggestion, which is 1 (the direct
               path) unless the grid is too small to fill the GPU; the
               workspace is then allocated with torch unless given.
+    window_left, window_right, key_lens : the masks of ``fa_fwd_masked``
+              (-1 = unbounded; key_lens a length-B int32 GPU tensor or a
+              sequence, copied to the GPU). A row that sees no key gets O = 0
+              and lse = -inf.
     The kernels are enqueued on ``stream`` (default: torch's current stream).
     """
     import torch
@@ -260,8 +316,33 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None, spli
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     if splits is None:
         splits = fa_split_count(B, H, N, Nk, d, causal) or 1
+    masked = key_lens is not None or window_left != -1 or window_right != -1
+    kl_ptr = None
+    if key_lens is not None:
+        if not torch.is_tensor(key_lens):
+            key_lens = torch.tensor([int(x) for x in key_lens], dtype=torch.int32, device=q.device)
+        if (key_lens.dtype != torch.int32 or not key_lens.is_cuda or key_lens.shape != (B,)
+                or not key_lens.is_contiguous()):
+            raise ValueError("key_lens must be a contiguous int32 [B] GPU tensor")
+        kl_ptr = key_lens.data_ptr()
     with torch.cuda.device(q.device):
-        if splits == 1:
+        if masked:
+            if splits == 1:
+                rc = fa_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), B, H, N, Nk, d, causal, window_left, window_right,
+                                   kl_ptr, scale, code, handle)
+            else:
+                need = fa_split_workspace_bytes(B, H, N, d, splits)
+                if workspace is None:
+                    workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
+                if workspace.numel() * workspace.element_size() < need or not workspace.is_contiguous():
+                    raise ValueError(f"workspace must be a contiguous tensor of at least {need} bytes")
+                rc = fa_fwd_split_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                         lse.data_ptr(), B, H, N, Nk, d, causal, window_left,
+                                         window_right, kl_ptr, scale, code, splits,
+                                         workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(), handle)
+        elif splits == 1:
             rc = fa_fwd_qk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                            B, H, N, Nk, d, causal, scale, code, handle)
         else:

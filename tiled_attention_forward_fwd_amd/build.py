@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_fwd_kernel.hip", "fa_bwd_kernel.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd_kernel.hip", "fa_fwd_masked.hip", "fa_bwd_kernel.hip"]
 ARCH = "gfx950"
 
 
@@ -22,23 +22,43 @@ def hipcc():
     return os.path.join(rocm, "bin", "hipcc")
 
 
+def _filtered(text):
+    return "\n".join(line for line in text.splitlines() if "packed-fp32-ops" not in line)
+
+
 def build(resource_usage=False, out=LIB):
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           # packed fp32 VALU forms are kept out of the generated code
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-Wl,-rpath," + os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")]
+    """Compiles every source to an object in parallel, then links libfa.so."""
+    flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+             # packed fp32 VALU forms are kept out of the generated code
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
     if resource_usage:
-        cmd.append("-Rpass-analysis=kernel-resource-usage")
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
-    cmd += ["-o", out + ".tmp"]
-    proc = subprocess.run(cmd, capture_output=True, text=True)
-    log = "\n".join(line for line in (proc.stdout + proc.stderr).splitlines()
-                    if "packed-fp32-ops" not in line)
-    if proc.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + log)
-    os.replace(out + ".tmp", out)
-    return log
+        flags.append("-Rpass-analysis=kernel-resource-usage")
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = f"{out}.{src}.o"
+        objs.append(obj)
+        procs.append(subprocess.Popen([hipcc()] + flags + ["-c", os.path.join(CSRC, src), "-o", obj],
+                                      stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+    logs, failed = [], False
+    for src, proc in zip(SOURCES, procs):
+        text = proc.communicate()[0]
+        logs.append(_filtered(text))
+        failed = failed or proc.returncode != 0
+    try:
+        if failed:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(logs))
+        link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC",
+                "-Wl,-rpath," + os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")]
+        proc = subprocess.run(link + objs + ["-o", out + ".tmp"], capture_output=True, text=True)
+        if proc.returncode != 0:
+            raise RuntimeError("link failed:\n" + _filtered(proc.stdout + proc.stderr))
+        os.replace(out + ".tmp", out)
+    finally:
+        for obj in objs:
+            if os.path.exists(obj):
+                os.remove(obj)
+    return "\n".join(logs)
 
 
 if __name__ == "__main__":

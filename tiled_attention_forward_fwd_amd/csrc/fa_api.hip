@@ -52,6 +52,82 @@ int check_problem(int B, int H, int Nq, int Nk, int d, int causal, int dtype)
     return FA_OK;
 }
 
+// Pointer, alignment, scale and overlap checks of the forward entry points.
+int check_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+              int Nk, int d, int causal, float scale, int dtype)
+{
+    if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+        return fail(FA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+    if (!aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    const int rc = check_problem(B, H, Nq, Nk, d, causal, dtype);
+    if (rc != FA_OK) return rc;
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    const size_t qb = (size_t)B * H * Nq * d * 2, kb = (size_t)B * H * Nk * d * 2;
+    const size_t lb = (size_t)B * H * Nq * 4;
+    if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb))
+        return fail(FA_ERR_INVALID_ARG, "o overlaps q, k or v");
+    if (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) ||
+        overlap(lse, lb, o, qb))
+        return fail(FA_ERR_INVALID_ARG, "lse overlaps q, k, v or o");
+    return FA_OK;
+}
+
+// The split launch's own checks, after check_fwd.
+int check_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                int Nq, int Nk, int d, int n_splits, void* workspace, int64_t workspace_bytes)
+{
+    if (!workspace) return fail(FA_ERR_INVALID_ARG, "NULL workspace pointer");
+    if (!aligned(workspace, 16)) return fail(FA_ERR_INVALID_ARG, "the workspace must be 16-byte aligned");
+    if (n_splits < 1 || n_splits > (Nk + 63) / 64)
+        return fail(FA_ERR_INVALID_ARG, "n_splits must be between 1 and ceil(Nk / 64)");
+    const int64_t need = (int64_t)n_splits * B * H * Nq * (d + 1) * 4;
+    if ((int64_t)B * H * ((Nq + 127) / 128) * n_splits > (int64_t)UINT32_MAX)
+        return fail(FA_ERR_INVALID_ARG, "B*H*ceil(Nq/128)*n_splits exceeds the grid limit");
+    if (workspace_bytes < need) return fail(FA_ERR_INVALID_ARG, "workspace too small");
+    const size_t qb = (size_t)B * H * Nq * d * 2, kb = (size_t)B * H * Nk * d * 2;
+    const size_t lb = (size_t)B * H * Nq * 4, wb = (size_t)need;
+    if (overlap(workspace, wb, q, qb) || overlap(workspace, wb, k, kb) ||
+        overlap(workspace, wb, v, kb) || overlap(workspace, wb, o, qb) ||
+        overlap(workspace, wb, lse, lb))
+        return fail(FA_ERR_INVALID_ARG, "the workspace overlaps a tensor argument");
+    return FA_OK;
+}
+
+// Mask arguments: windows >= -1; key_lens (device, read by the kernel)
+// 4-byte aligned and clear of everything the call writes.
+int check_masks(int B, int H, int Nq, int d, int window_left, int window_right,
+                const int32_t* key_lens, const void* o, const float* lse, const void* workspace,
+                int64_t workspace_bytes)
+{
+    if (window_left < -1 || window_right < -1)
+        return fail(FA_ERR_INVALID_ARG, "window_left and window_right must be >= -1");
+    if (key_lens) {
+        if (!aligned(key_lens, 4)) return fail(FA_ERR_INVALID_ARG, "key_lens must be 4-byte aligned");
+        const size_t nb = (size_t)B * 4;
+        if (overlap(key_lens, nb, o, (size_t)B * H * Nq * d * 2) ||
+            overlap(key_lens, nb, lse, (size_t)B * H * Nq * 4) ||
+            (workspace && overlap(key_lens, nb, workspace, (size_t)workspace_bytes)))
+            return fail(FA_ERR_INVALID_ARG, "key_lens overlaps an output or the workspace");
+    }
+    return FA_OK;
+}
+
+// True when the masks hide nothing beyond the causal/tail masks of the
+// unmasked kernels.
+bool masks_off(int causal, int window_left, int window_right, const int32_t* key_lens)
+{
+    return !key_lens && window_left < 0 && (causal || window_right < 0);
+}
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return FA_OK;
+    snprintf(g_msg, sizeof g_msg, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+    return FA_ERR_HIP;
+}
+
 // Causal visible area below the diagonal in the pages' convention (N*N/2
 // for a square problem).
 double causal_area(double Nq, double Nk)
@@ -126,6 +202,76 @@ int fa_plan_qk(int B, int H, int Nq, int Nk, int d, int causal, int dtype, fa_pl
     return FA_OK;
 }
 
+int fa_tile_counts_masked(int64_t Nq, int64_t Nk, int block_m, int block_n, int causal,
+                          int64_t window_left, int64_t window_right, int64_t key_len,
+                          int64_t counts[4])
+{
+    g_msg[0] = 0;
+    if (!counts || Nq < 1 || Nk < 1 || block_m < 1 || block_n < 1 || (causal != 0 && causal != 1) ||
+        window_left < -1 || window_right < -1 || key_len < 0 || key_len > Nk)
+        return fail(FA_ERR_INVALID_ARG, "fa_tile_counts_masked: invalid argument");
+    const int64_t n_qt = (Nq + block_m - 1) / block_m, n_kt = (Nk + block_n - 1) / block_n;
+    counts[0] = n_qt * n_kt;
+    counts[1] = counts[2] = counts[3] = 0;
+    for (int64_t i = 0; i < n_qt; ++i) {
+        const fa::MaskedSpan s = fa::masked_span(i * block_m, block_m, block_n, Nq, Nk, causal != 0,
+                                                 window_left, window_right, key_len);
+        counts[1] += s.end - s.first;
+        counts[2] += s.unmasked_end - s.unmasked_begin;
+    }
+    counts[3] = counts[1] - counts[2];
+    return FA_OK;
+}
+
+int fa_plan_masked(int B, int H, int Nq, int Nk, int d, int causal, int window_left, int window_right,
+                   const int32_t* key_lens, int dtype, fa_plan_t* plan)
+{
+    g_msg[0] = 0;
+    if (!plan) return fail(FA_ERR_INVALID_ARG, "plan is NULL");
+    const int rc = check_problem(B, H, Nq, Nk, d, causal, dtype);
+    if (rc != FA_OK) return rc;
+    if (window_left < -1 || window_right < -1)
+        return fail(FA_ERR_INVALID_ARG, "window_left and window_right must be >= -1");
+    if (key_lens)
+        for (int b = 0; b < B; ++b)
+            if (key_lens[b] < 0 || key_lens[b] > Nk)
+                return fail(FA_ERR_INVALID_ARG, "key_lens values must lie in [0, Nk]");
+    const bool off = masks_off(causal, window_left, window_right, key_lens);
+    const fa::Shape sh = off ? fa::pick_shape(B, H, Nq, d, causal != 0)
+                             : fa::pick_shape_masked(B, H, Nq, d, causal != 0);
+    const int bm = sh.block_m, bn = fa::block_n(d);
+    double pairs = 0, tiles = 0, keys_read = 0;
+    for (int b = 0; b < B; ++b) {
+        const int64_t kl = key_lens ? key_lens[b] : Nk;
+        int64_t counts[4];
+        if (off)
+            fa_tile_counts_qk(Nq, Nk, bm, bn, causal, counts);
+        else
+            fa_tile_counts_masked(Nq, Nk, bm, bn, causal, window_left, window_right, kl, counts);
+        tiles += (double)counts[1];
+        // visible (query, key) pairs, and the keys some row sees (the union
+        // of the rows' ranges; lo and hi never decrease with the row)
+        int64_t reach = 0;
+        for (int64_t i = 0; i < Nq; ++i) {
+            const fa::RowKeys r = fa::row_keys(i, Nk, causal != 0, window_left, window_right, kl);
+            if (r.hi > r.lo) pairs += (double)(r.hi - r.lo);
+            const int64_t from = r.lo > reach ? r.lo : reach;
+            if (r.hi > from) keys_read += (double)(r.hi - from);
+            if (r.hi > reach) reach = r.hi;
+        }
+    }
+    plan->block_m = bm;
+    plan->block_n = bn;
+    plan->threads = sh.threads;
+    plan->lds_bytes = fa::lds_bytes(d);
+    plan->workgroups = (int64_t)B * H * ((Nq + bm - 1) / bm);
+    plan->pairs_visited = (int64_t)(tiles * H);
+    plan->mfma_flops = 4.0 * d * (double)bm * bn * (double)plan->pairs_visited;
+    plan->algo_flops = 4.0 * H * pairs * d;
+    plan->algo_bytes = 4.0 * H * ((double)B * Nq + keys_read) * d + 4.0 * (double)B * H * Nq;
+    return FA_OK;
+}
+
 int fa_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t* plan)
 {
     return fa_plan_qk(B, H, N, N, d, causal, dtype, plan);
@@ -135,28 +281,27 @@ int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, 
               int Nq, int Nk, int d, int causal, float scale, int dtype, void* stream)
 {
     g_msg[0] = 0;
-    if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "NULL tensor pointer");
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
-        return fail(FA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
-    if (!aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-    const int rc = check_problem(B, H, Nq, Nk, d, causal, dtype);
+    const int rc = check_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype);
     if (rc != FA_OK) return rc;
-    if (!(scale > 0.f) || !isfinite(scale))
-        return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
-    const size_t qb = (size_t)B * H * Nq * d * 2, kb = (size_t)B * H * Nk * d * 2;
-    const size_t lb = (size_t)B * H * Nq * 4;
-    if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb))
-        return fail(FA_ERR_INVALID_ARG, "o overlaps q, k or v");
-    if (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) ||
-        overlap(lse, lb, o, qb))
-        return fail(FA_ERR_INVALID_ARG, "lse overlaps q, k, v or o");
-    const hipError_t e = fa::launch_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, scale,
-                                        dtype == FA_DTYPE_BF16, (hipStream_t)stream);
-    if (e != hipSuccess) {
-        snprintf(g_msg, sizeof g_msg, "HIP error %d: %s", (int)e, hipGetErrorString(e));
-        return FA_ERR_HIP;
-    }
-    return FA_OK;
+    return hip_status(fa::launch_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, scale,
+                                     dtype == FA_DTYPE_BF16, (hipStream_t)stream));
+}
+
+int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int Nq, int Nk, int d, int causal, int window_left, int window_right,
+                  const int32_t* key_lens, float scale, int dtype, void* stream)
+{
+    g_msg[0] = 0;
+    int rc = check_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype);
+    if (rc != FA_OK) return rc;
+    rc = check_masks(B, H, Nq, d, window_left, window_right, key_lens, o, lse, nullptr, 0);
+    if (rc != FA_OK) return rc;
+    if (masks_off(causal, window_left, window_right, key_lens))
+        return hip_status(fa::launch_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, scale,
+                                         dtype == FA_DTYPE_BF16, (hipStream_t)stream));
+    const fa::MaskArgs mask{window_left, window_right, key_lens, H};
+    return hip_status(fa::launch_fwd_masked(q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, mask,
+                                            scale, dtype == FA_DTYPE_BF16, (hipStream_t)stream));
 }
 
 int fa_split_count(int B, int H, int Nq, int Nk, int d, int causal)
@@ -187,41 +332,36 @@ int fa_fwd_split_qk(const void* q, const void* k, const void* v, void* o, float*
                     void* workspace, int64_t workspace_bytes, void* stream)
 {
     g_msg[0] = 0;
-    if (!q || !k || !v || !o || !lse || !workspace)
-        return fail(FA_ERR_INVALID_ARG, "NULL tensor or workspace pointer");
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-        !aligned(workspace, 16))
-        return fail(FA_ERR_INVALID_ARG, "q, k, v, o and the workspace must be 16-byte aligned");
-    if (!aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-    const int rc = check_problem(B, H, Nq, Nk, d, causal, dtype);
+    int rc = check_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype);
     if (rc != FA_OK) return rc;
-    if (!(scale > 0.f) || !isfinite(scale))
-        return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
-    if (n_splits < 1 || n_splits > (Nk + 63) / 64)
-        return fail(FA_ERR_INVALID_ARG, "n_splits must be between 1 and ceil(Nk / 64)");
-    const int64_t need = fa_split_workspace_bytes(B, H, Nq, d, n_splits);
-    if ((int64_t)B * H * ((Nq + 127) / 128) * n_splits > (int64_t)UINT32_MAX)
-        return fail(FA_ERR_INVALID_ARG, "B*H*ceil(Nq/128)*n_splits exceeds the grid limit");
-    if (workspace_bytes < need) return fail(FA_ERR_INVALID_ARG, "workspace too small");
-    const size_t qb = (size_t)B * H * Nq * d * 2, kb = (size_t)B * H * Nk * d * 2;
-    const size_t lb = (size_t)B * H * Nq * 4, wb = (size_t)need;
-    if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb))
-        return fail(FA_ERR_INVALID_ARG, "o overlaps q, k or v");
-    if (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) ||
-        overlap(lse, lb, o, qb))
-        return fail(FA_ERR_INVALID_ARG, "lse overlaps q, k, v or o");
-    if (overlap(workspace, wb, q, qb) || overlap(workspace, wb, k, kb) ||
-        overlap(workspace, wb, v, kb) || overlap(workspace, wb, o, qb) ||
-        overlap(workspace, wb, lse, lb))
-        return fail(FA_ERR_INVALID_ARG, "the workspace overlaps a tensor argument");
-    const hipError_t e = fa::launch_fwd_split(q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, scale,
-                                              dtype == FA_DTYPE_BF16, n_splits, (float*)workspace,
-                                              (hipStream_t)stream);
-    if (e != hipSuccess) {
-        snprintf(g_msg, sizeof g_msg, "HIP error %d: %s", (int)e, hipGetErrorString(e));
-        return FA_ERR_HIP;
-    }
-    return FA_OK;
+    rc = check_split(q, k, v, o, lse, B, H, Nq, Nk, d, n_splits, workspace, workspace_bytes);
+    if (rc != FA_OK) return rc;
+    return hip_status(fa::launch_fwd_split(q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, scale,
+                                           dtype == FA_DTYPE_BF16, n_splits, (float*)workspace,
+                                           (hipStream_t)stream));
+}
+
+int fa_fwd_split_masked(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int H, int Nq, int Nk, int d, int causal, int window_left, int window_right,
+                        const int32_t* key_lens, float scale, int dtype, int n_splits,
+                        void* workspace, int64_t workspace_bytes, void* stream)
+{
+    g_msg[0] = 0;
+    int rc = check_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype);
+    if (rc != FA_OK) return rc;
+    rc = check_split(q, k, v, o, lse, B, H, Nq, Nk, d, n_splits, workspace, workspace_bytes);
+    if (rc != FA_OK) return rc;
+    rc = check_masks(B, H, Nq, d, window_left, window_right, key_lens, o, lse, workspace,
+                     workspace_bytes);
+    if (rc != FA_OK) return rc;
+    if (masks_off(causal, window_left, window_right, key_lens))
+        return hip_status(fa::launch_fwd_split(q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, scale,
+                                               dtype == FA_DTYPE_BF16, n_splits, (float*)workspace,
+                                               (hipStream_t)stream));
+    const fa::MaskArgs mask{window_left, window_right, key_lens, H};
+    return hip_status(fa::launch_fwd_split_masked(q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0,
+                                                  mask, scale, dtype == FA_DTYPE_BF16, n_splits,
+                                                  (float*)workspace, (hipStream_t)stream));
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -244,6 +244,21 @@ __device__ __forceinline__ void mask_scores(f32x16 (&s)[KB], int k0, int qrow, i
     }
 }
 
+// Mask of a tile under padding and window masks: the lane's query row sees
+// the keys [lo, hi) only (fa_tiles.h, row_keys).
+template <int KB>
+__device__ __forceinline__ void mask_range(f32x16 (&s)[KB], int k0, int lo, int hi, int hh)
+{
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key < lo || key >= hi) s[kb][r] = -INFINITY;
+        }
+    }
+}
+
 // Row max of one block of scores in log2 units (both lane halves of a row).
 template <int KB>
 __device__ __forceinline__ float row_max_log2(const f32x16 (&s)[KB], float c_log2)

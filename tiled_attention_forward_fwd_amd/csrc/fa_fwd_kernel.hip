@@ -1,473 +1,9 @@
-// fa_fwd_kernel.hip -- attention forward (FlashAttention-2 form) for gfx950.
-//
-// Method: "How to optimise a Triton FlashAttention-2 kernel step by step with
-// a profiler" ("Where the last article left off", Round 1, Round 4): one
-// workgroup per tile of query rows; K and V tiles stream through LDS; the
-// running max m, running sum l and unnormalised O stay in fp32 registers and
-// are rescaled when a tile raises the max (the online softmax named at the end
-// of "Programming an attention kernel in Triton"); O and the logsumexp are
-// written once.
-//
-// gfx950 mapping (our design, not the pages'):
-//   * A workgroup is WAVES waves; each wave owns QB blocks of 32 whole query
-//     rows, so row reductions never leave the wave (the pages' rule that every
-//     warp must own whole rows, Round 0 / Round 1). With QB = 2 every K and V
-//     operand read from LDS feeds two MFMAs.
-//   * Scores are computed transposed, S^T = K Q^T, with
-//     v_mfma_f32_32x32x16_{bf16,f16}: keys on the M axis, queries on N. In the
-//     32x32 accumulator each lane holds 16 keys of ONE query, and the other 16
-//     keys of that query sit in lane ^ 32. The row max and row sum are
-//     in-lane plus one v_permlane32_swap, and the rescale of O by alpha is one
-//     scalar per lane. Consecutive score MFMAs share their Q operand (the
-//     32-key blocks of a tile run interleaved), which lowers operand toggling
-//     and with it the energy per MFMA on this power-limited part.
-//   * O^T += V^T P^T takes P^T straight from the score registers as the B
-//     operand: the accumulator hands lane half h, element e the key
-//     16t + 8(e/4) + 4h + (e%4), and the V^T operand is read in that key
-//     order, so P never goes through LDS.
-//   * Q is loaded once into registers in B-operand layout.
-//   * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 ... lds,
-//     16 bytes per lane, no staging registers), row-major and dense. The
-//     16-byte chunks of each row are XOR-swizzled by a function of the row so
-//     that the operand reads below hit distinct banks.
-//   * K is read as the A operand of S^T = K Q^T with one ds_read_b128 per
-//     MFMA. V is read as the A operand of O^T = V^T P^T with two
-//     ds_read_b64_tr_b16: within each 16-lane group that instruction hands
-//     lane j element (j mod 4) of the 8-byte chunk addressed by lane
-//     4e + j/4, so 16 lanes addressing 4 keys x 4 dim-quads receive 4 keys of
-//     one dim each: a transposed read of the row-major tile.
-//   * Software pipeline over key tiles, two K and two V buffers in LDS:
-//     iteration j computes the scores of tile j+1 on the matrix cores with
-//     the exp2 work of tile j interleaved between those MFMAs in program
-//     order (the two are independent, so the vector units run while the
-//     matrix core does), then P_j V_j; the copies of K_{j+2} and V_{j+1}
-//     are in flight meanwhile; one barrier per tile. The last tile runs
-//     without a successor, so no score MFMA is wasted. The copies go through
-//     a buffer descriptor bounded to the head, so the rows of a ragged last
-//     tile past N arrive as zeros (and are masked).
-//   * exp2 with the softmax scale and log2(e) folded into one constant
-//     (Round 4, "exp2"); the running max is kept in log2 units. The max is
-//     updated lazily: a tile's P is taken against the running max and the
-//     tile's own row max is reduced only when a partial row sum shows that P
-//     grew past 2^12 (always on the first tile); O and l carry the same
-//     factor, so O / l is unchanged.
-//   * P is rounded to the input type after l has been summed from fp32 P
-//     (Round 4, "The P cast").
-//   * Causal attention visits no key tile above the diagonal and masks only
-//     the diagonal tiles; non-causal attention masks only a ragged last tile
-//     (Round 4, "Causal tile-skipping"). Masked scores are -inf; the running
-//     max starts at a finite very negative value so a row with no visible key
-//     in a tile never forms -inf - (-inf).
-//   * Workgroup ids are remapped. Non-causal: all query tiles of one (b, h)
-//     run on the same XCD (workgroups are dealt round-robin over the 8 XCDs,
-//     each with its own L2), which keeps that head's K and V in one L2.
-//     Causal: longest tiles of every head first, which balances the uneven
-//     causal work over the XCDs.
+// fa_fwd_kernel.hip -- host dispatch of the attention forward without masks:
+// workgroup shape, direct and split launches (kernels in fa_fwd_kernel.h).
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include <type_traits>
-
-#include "fa_device.h"
-#include "fa_launch.h"
-#include "fa_tiles.h"
+#include "fa_fwd_kernel.h"
 
 namespace fa {
-namespace {
-
-// blockIdx -> (b*H + h, query tile). Hardware id i runs on XCD i % 8 and
-// the ids are dealt in order.
-//  * Non-causal (equal tiles): each XCD gets a contiguous range of
-//    head-major ids, so a head's query tiles share one L2.
-//  * Causal (a tile's work grows with its index): tile-major, longest tiles
-//    of all heads first, id i -> head i % BH. Greedy dispatch of
-//    longest-first work then keeps every XCD busy to the end, and when BH is
-//    a multiple of 8 every tile of a head still lands on one XCD.
-template <bool CAUSAL>
-__device__ __forceinline__ void workgroup_tile(int n_qt, uint32_t& bh, uint32_t& qt)
-{
-    const uint32_t nwg = gridDim.x, hw = blockIdx.x;
-    if (CAUSAL) {
-        const uint32_t n_bh = nwg / (uint32_t)n_qt;
-        bh = hw % n_bh;
-        qt = (uint32_t)n_qt - 1 - hw / n_bh;
-    } else {
-        const uint32_t xcd = hw % kXcds, slot = hw / kXcds;
-        const uint32_t per = nwg / kXcds, extra = nwg % kXcds;
-        const uint32_t logical = xcd < extra ? xcd * (per + 1) + slot
-                                             : extra * (per + 1) + (xcd - extra) * per + slot;
-        bh = logical / (uint32_t)n_qt;
-        qt = logical % (uint32_t)n_qt;
-    }
-}
-
-// Epilogue: O = O_acc / l in the input type, lse = (m + log2 l) * ln 2.
-template <typename T, int D, int QB, int DB>
-__device__ __forceinline__ void store_outputs(const f32x16 (&oacc)[QB][DB], const float (&m_run)[QB],
-                                              const float (&l_run)[QB], const int (&qrow)[QB], int n_rows,
-                                              T* __restrict__ oh, float* __restrict__ lseh, int hh)
-{
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float l_tot = swap_halves_sum(l_run[qb]);
-        if (qrow[qb] < n_rows) {
-            const float inv = 1.0f / l_tot;
-            T* orow = oh + (int64_t)qrow[qb] * D;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    T vals[4];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) vals[t] = to_elem<T>(oacc[qb][db][4 * g + t] * inv);
-                    u32x2 packed = __builtin_bit_cast(u32x2, vals);
-                    *(u32x2*)(orow + db * 32 + 8 * g + 4 * hh) = packed;
-                }
-            }
-            if (hh == 0) lseh[qrow[qb]] = (m_run[qb] + log2f(l_tot)) * 0.69314718055994531f;
-        }
-    }
-}
-
-// SPLIT: the key tiles of a query tile are divided into n_splits contiguous
-// chunks, one workgroup each, and every workgroup writes the normalised
-// partial output of its chunk (fp32) and the chunk's logsumexp to a
-// workspace instead of O and lse; fa_merge_kernel combines them. This is for
-// problems with too few query tiles to fill the GPU (KV-cache decode). A
-// chunk's partial result is exact for its keys, and the merge is the online
-// softmax identity applied once per chunk.
-// Partial result of a key chunk: O_chunk = O_acc / l in fp32 and the chunk's
-// logsumexp (natural log). A row that sees no key of the chunk gets O = 0
-// and lse = -inf, which gives it weight zero in the merge.
-template <int D, int QB, int DB>
-__device__ __forceinline__ void store_partials(const f32x16 (&oacc)[QB][DB], const float (&m_run)[QB],
-                                               const float (&l_run)[QB], const int (&qrow)[QB], int n_rows,
-                                               float* __restrict__ ws_o, float* __restrict__ ws_lse, int hh)
-{
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float l_tot = swap_halves_sum(l_run[qb]);
-        if (qrow[qb] < n_rows) {
-            const bool seen = l_tot > 0.f;
-            const float inv = seen ? 1.0f / l_tot : 0.f;
-            float* orow = ws_o + (int64_t)qrow[qb] * D;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    typedef float f32x4 __attribute__((ext_vector_type(4)));
-                    f32x4 vals;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) vals[t] = oacc[qb][db][4 * g + t] * inv;
-                    *(f32x4*)(orow + db * 32 + 8 * g + 4 * hh) = vals;
-                }
-            }
-            if (hh == 0) ws_lse[qrow[qb]] = seen ? (m_run[qb] + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-        }
-    }
-}
-
-// Merge of the key chunks of a split launch, per query row:
-// lse = ln sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s. Each thread
-// owns 8 consecutive dims of one row; rows are [B*H*Nq] in order. Chunks go
-// in groups of 16 whose loads are all issued before any is used, so a call
-// with up to 16 chunks makes two rounds of memory reads (the logsumexps, then
-// the partial outputs) instead of one per chunk.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__ ws_o,
-                                                       const float* __restrict__ ws_lse, T* __restrict__ o,
-                                                       float* __restrict__ lse, int64_t n_rows, int n_splits)
-{
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-    constexpr int TPR = D / 8, G = 16;  // threads per row, chunks per group
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t row = t / TPR;
-    const int c0 = (int)(t % TPR) * 8;
-    if (row >= n_rows) return;
-    float mx = -INFINITY;
-    for (int s0 = 0; s0 < n_splits; s0 += G) {
-        float l[G];
-#pragma unroll
-        for (int i = 0; i < G; ++i) l[i] = s0 + i < n_splits ? ws_lse[(int64_t)(s0 + i) * n_rows + row] : -INFINITY;
-#pragma unroll
-        for (int i = 0; i < G; ++i) mx = fmaxf(mx, l[i]);
-    }
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
-    if (mx > -INFINITY) {
-        for (int s0 = 0; s0 < n_splits; s0 += G) {
-            float l[G];
-            f32x4 a[G], b[G];
-#pragma unroll
-            for (int i = 0; i < G; ++i) {
-                if (s0 + i < n_splits) {
-                    const float* src = ws_o + ((int64_t)(s0 + i) * n_rows + row) * D + c0;
-                    l[i] = ws_lse[(int64_t)(s0 + i) * n_rows + row];
-                    a[i] = *(const f32x4*)src;
-                    b[i] = *(const f32x4*)(src + 4);
-                } else {
-                    l[i] = -INFINITY;
-                    a[i] = b[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < G; ++i) {
-                const float w = expf(l[i] - mx);  // exp(-inf) = 0 for absent or empty chunks
-                wsum += w;
-                acc0 += w * a[i];
-                acc1 += w * b[i];
-            }
-        }
-    }
-    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-    T vals[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        vals[e] = to_elem<T>(acc0[e] * inv);
-        vals[4 + e] = to_elem<T>(acc1[e] * inv);
-    }
-    *(u32x4*)(o + row * D + c0) = __builtin_bit_cast(u32x4, vals);
-    if (c0 == 0) lse[row] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
-}
-
-template <typename T, int D, bool CAUSAL, int WAVES, int QB, bool SPLIT>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
-                          amdgpu_waves_per_eu(2 / QB, 2 / QB)))
-void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                   T* __restrict__ o, float* __restrict__ lse, int Nq, int Nk, int n_qt, float c_log2,
-                   int n_splits, float* __restrict__ ws_o, float* __restrict__ ws_lse)
-{
-    typedef Cfg<D, WAVES, QB> C;
-    typedef typename Mma<T>::vec8 vec8;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * C::TILE];
-
-    uint32_t bh, qt, split = 0;
-    if (SPLIT) {
-        const uint32_t rest = blockIdx.x / (uint32_t)n_splits;
-        split = blockIdx.x % (uint32_t)n_splits;
-        bh = rest / (uint32_t)n_qt;
-        qt = rest % (uint32_t)n_qt;
-    } else {
-        workgroup_tile<CAUSAL>(n_qt, bh, qt);
-    }
-    const int q0 = (int)qt * C::BM;
-
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
-    const int64_t q_off = (int64_t)bh * Nq * D, kv_off = (int64_t)bh * Nk * D;
-    const T* kh = k + kv_off;
-    const T* vh = v + kv_off;
-
-    int qrow[QB];
-    vec8 qf[QB][C::DS];
-    load_q<T, D, QB, C::DS>(q + q_off, q0 + wave * QB * 32, Nq, l32, hh, qrow, qf);
-
-    const TileSpan span = tile_span(q0, C::BM, C::BN, Nq, Nk, CAUSAL);
-    const int n_unmasked = (int)span.unmasked, n_tiles = (int)span.total;
-    // key tiles [jb, je) of this workgroup: all of them, or one chunk
-    int jb = 0, je = n_tiles;
-    if (SPLIT) {
-        const int per = (n_tiles + n_splits - 1) / n_splits;
-        jb = min(n_tiles, (int)split * per);
-        je = min(n_tiles, jb + per);
-    }
-
-    f32x16 oacc[QB][C::DB];
-    float m_run[QB], l_run[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) oacc[qb][db] = (f32x16){};
-        m_run[qb] = -1e30f;
-        l_run[qb] = 0.f;
-    }
-
-    // LDS: K tiles in buffers 0/1, V tiles in buffers 2/3. Iteration j reads
-    // K_{j+1} (scores of the next tile) and V_j (P.V of this tile) while the
-    // copies of K_{j+2} and V_{j+1} are in flight; one barrier per tile.
-    auto kbuf = [&](int i) { return smem + (i & 1) * C::TILE; };
-    auto vbuf = [&](int i) { return smem + (2 + (i & 1)) * C::TILE; };
-
-    const uint32_t head_bytes = (uint32_t)Nk * (D * 2);
-    const rsrc_t krs = head_rsrc(kh, head_bytes), vrs = head_rsrc(vh, head_bytes);
-    const uint32_t lane_off = tile_lane_offset<D>(wave, lane);
-    // Causal: the key tiles this wave's rows can see form the prefix
-    // [0, n_wave); in the diagonal tiles past it the wave only helps with the
-    // copies and the barriers. In a split launch a wave whose rows all lie
-    // past Nq computes nothing either.
-    int n_wave = CAUSAL ? min(je, (q0 + (wave + 1) * QB * 32 - 1) / C::BN + 1) : je;
-    if (SPLIT && q0 + wave * QB * 32 >= Nq) n_wave = jb;
-
-    f32x16 sa[QB][C::KB], sb[QB][C::KB];
-    if (SPLIT && jb == je) {
-        // an empty chunk: no key of this query tile falls in it
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb) sa[qb][kb] = (f32x16){};
-    } else {
-        issue_tile<D, WAVES, QB>(kbuf(jb), krs, jb * C::BN, wave, lane_off);
-        issue_tile<D, WAVES, QB>(vbuf(jb), vrs, jb * C::BN, wave, lane_off);
-        if (jb + 1 < je) issue_tile<D, WAVES, QB>(kbuf(jb + 1), krs, (jb + 1) * C::BN, wave, lane_off);
-        stage_barrier();
-        if (!SPLIT || jb < n_wave) scores<T, D, QB, C::KB, C::DS>(sa, kbuf(jb), qf, l32, hh);
-        stage_barrier();  // K_jb's buffer is refilled in the first iteration
-    }
-
-    // One tile that has a successor: sc holds the scores of tile j; sn
-    // receives those of tile j+1.
-    // The exp2 work of tile j is interleaved with the score MFMAs of tile j+1
-    // (scores_with_exp). The 4-wave d=128 shape keeps them apart: with its
-    // four copies per thread and tile it runs out of registers when fused.
-    constexpr bool kFuseExp = QB == 1 && !(D == 128 && WAVES == 4);
-    auto step = [&](auto masked, int j, f32x16 (&sc)[QB][C::KB], f32x16 (&sn)[QB][C::KB]) {
-        // M: the tile gets the mask; G: per-wave limits apply (masked tiles,
-        // and every tile of a split launch)
-        constexpr bool M = decltype(masked)::value, G = M || SPLIT;
-        if (j + 2 < je)
-            issue_tile<D, WAVES, QB>(kbuf(j), krs, (j + 2) * C::BN, wave, lane_off);
-        issue_tile<D, WAVES, QB>(vbuf(j + 1), vrs, (j + 1) * C::BN, wave, lane_off);
-        if (kFuseExp) {
-            if (!G || j < n_wave) {
-                if (M) mask_scores<C::KB, CAUSAL>(sc[0], j * C::BN, qrow[0], Nk, hh);
-                vec8 p[QB][C::KT];
-                float rs[QB];
-                if (!G || j + 1 < n_wave) {
-                    scores_with_exp<T, D, C::KB, C::DS, C::KT>(sn, kbuf(j + 1), qf, l32, hh, sc, m_run[0],
-                                                               c_log2, p, rs);
-                    order_scores_block<D, WAVES, QB>();
-                } else {
-                    exp_tile<T, QB, C::KB, C::KT>(sc, m_run, c_log2, p, rs);
-                }
-                softmax_finish<T, QB, C::KB, C::DB, C::KT>(sc, oacc, m_run, l_run, c_log2, p, rs);
-                pv_tile<T, D, QB, C::DB, C::KT>(p, vbuf(j), oacc, lane, hh);
-                order_pv_block<D, WAVES, QB>();
-            }
-        } else {
-            if (!G || j + 1 < n_wave) {
-                scores<T, D, QB, C::KB, C::DS>(sn, kbuf(j + 1), qf, l32, hh);
-                order_scores_block<D, WAVES, QB>();
-            }
-            if (!G || j < n_wave) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    if (M) mask_scores<C::KB, CAUSAL>(sc[qb], j * C::BN, qrow[qb], Nk, hh);
-                softmax_pv<T, D, QB, C::KB, C::DB, C::KT>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
-                order_pv_block<D, WAVES, QB>();
-            }
-        }
-        stage_barrier();
-    };
-    typedef std::integral_constant<bool, false> unmasked_t;
-    typedef std::integral_constant<bool, true> masked_t;
-
-    // The last tile has no successor whose scores would be computed, so it
-    // runs a step of its own. Before it: tiles [0, n_unmasked) need no mask,
-    // the rest get it; the loops are unrolled by two so the score registers
-    // alternate.
-    auto last_step = [&](auto masked, int j, f32x16 (&sc)[QB][C::KB]) {
-        constexpr bool M = decltype(masked)::value, G = M || SPLIT;
-        if (!G || j < n_wave) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-                if (M) mask_scores<C::KB, CAUSAL>(sc[qb], j * C::BN, qrow[qb], Nk, hh);
-            softmax_pv<T, D, QB, C::KB, C::DB, C::KT>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
-            order_pv_block<D, WAVES, QB>();
-        }
-    };
-    auto shift_scores = [&]() {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb) sa[qb][kb] = sb[qb][kb];
-    };
-    const int n_lead = je - 1;
-    const int n_u = n_unmasked < n_lead ? n_unmasked : n_lead;
-    int j = jb;
-    for (; j + 2 <= n_u; j += 2) {
-        step(unmasked_t(), j, sa, sb);
-        step(unmasked_t(), j + 1, sb, sa);
-    }
-    if (j < n_u) {
-        step(unmasked_t(), j, sa, sb);
-        ++j;
-        shift_scores();
-    }
-    for (; j + 2 <= n_lead; j += 2) {
-        step(masked_t(), j, sa, sb);
-        step(masked_t(), j + 1, sb, sa);
-    }
-    if (j < n_lead) {
-        step(masked_t(), j, sa, sb);
-        ++j;
-        shift_scores();
-    }
-    if (j < je) {
-        if (j < n_unmasked)
-            last_step(unmasked_t(), j, sa);
-        else
-            last_step(masked_t(), j, sa);
-    }
-
-    if (SPLIT) {
-        const int64_t slot = ((int64_t)split * (gridDim.x / ((uint32_t)n_splits * (uint32_t)n_qt)) + bh) * Nq;
-        store_partials<D, QB, C::DB>(oacc, m_run, l_run, qrow, Nq, ws_o + slot * D, ws_lse + slot, hh);
-    } else {
-        store_outputs<T, D, QB, C::DB>(oacc, m_run, l_run, qrow, Nq, o + q_off, lse + (int64_t)bh * Nq, hh);
-    }
-}
-
-template <typename T, int D, bool CAUSAL, int WAVES, int QB>
-hipError_t launch_one(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                      int Nq, int Nk, float scale, hipStream_t stream)
-{
-    typedef Cfg<D, WAVES, QB> C;
-    const int n_qt = (Nq + C::BM - 1) / C::BM;
-    const float c_log2 = scale * 1.4426950408889634f;
-    dim3 grid((unsigned)((int64_t)n_qt * BH)), block(C::THREADS);
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, WAVES, QB, false>), grid, block, 0, stream,
-                       (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, Nq, Nk, n_qt, c_log2, 1,
-                       (float*)nullptr, (float*)nullptr);
-    return hipGetLastError();
-}
-
-// Split launch (4-wave, 128-row workgroups) followed by the merge; the
-// workspace holds n_splits * B*H*Nq partial rows of D floats and then as many
-// logsumexps.
-template <typename T, int D, bool CAUSAL>
-hipError_t launch_split(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                        int Nq, int Nk, float scale, int n_splits, float* ws, hipStream_t stream)
-{
-    typedef Cfg<D, 4, 1> C;
-    const int n_qt = (Nq + C::BM - 1) / C::BM;
-    const float c_log2 = scale * 1.4426950408889634f;
-    const int64_t n_rows = (int64_t)BH * Nq;
-    float* ws_o = ws;
-    float* ws_lse = ws + (int64_t)n_splits * n_rows * D;
-    dim3 grid((unsigned)((int64_t)n_qt * BH * n_splits)), block(C::THREADS);
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, 4, 1, true>), grid, block, 0, stream, (const T*)q,
-                       (const T*)k, (const T*)v, (T*)o, lse, Nq, Nk, n_qt, c_log2, n_splits, ws_o,
-                       ws_lse);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t threads = n_rows * (D / 8);
-    dim3 mgrid((unsigned)((threads + 255) / 256)), mblock(256);
-    hipLaunchKernelGGL((fa_merge_kernel<T, D>), mgrid, mblock, 0, stream, (const float*)ws_o,
-                       (const float*)ws_lse, (T*)o, lse, n_rows, n_splits);
-    return hipGetLastError();
-}
-
-template <typename T, int D, bool CAUSAL>
-hipError_t launch_shape(const Shape& sh, const void* q, const void* k, const void* v, void* o,
-                        float* lse, int BH, int Nq, int Nk, float scale, hipStream_t stream)
-{
-    if (sh.waves == 8) return launch_one<T, D, CAUSAL, 8, 1>(q, k, v, o, lse, BH, Nq, Nk, scale, stream);
-    return launch_one<T, D, CAUSAL, 4, 1>(q, k, v, o, lse, BH, Nq, Nk, scale, stream);
-}
-
-}  // namespace
 
 // Workgroup shape per problem. 256-row workgroups (8 waves) stream each K/V
 // tile from L2 once for twice the rows, which lowers L2 and LDS-fill traffic
@@ -499,10 +35,10 @@ hipError_t launch_fwd_split(const void* q, const void* k, const void* v, void* o
 {
     const int BH = B * H;
 #define FA_DISPATCH(T, D)                                                                         \
-    return causal ? launch_split<T, D, true>(q, k, v, o, lse, BH, Nq, Nk, scale, n_splits, workspace, \
-                                             stream)                                              \
-                  : launch_split<T, D, false>(q, k, v, o, lse, BH, Nq, Nk, scale, n_splits, workspace, \
-                                              stream)
+    return causal ? launch_split<T, D, true, false>(q, k, v, o, lse, BH, Nq, Nk, scale, n_splits,  \
+                                                    workspace, MaskArgs{}, stream)                 \
+                  : launch_split<T, D, false, false>(q, k, v, o, lse, BH, Nq, Nk, scale, n_splits, \
+                                                     workspace, MaskArgs{}, stream)
     if (bf16) {
         if (d == 64) FA_DISPATCH(__bf16, 64);
         FA_DISPATCH(__bf16, 128);
@@ -521,8 +57,10 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
     const int BH = B * H;
     const Shape sh = pick_shape(B, H, Nq, d, causal);
 #define FA_DISPATCH(T, D)                                                                        \
-    return causal ? launch_shape<T, D, true>(sh, q, k, v, o, lse, BH, Nq, Nk, scale, stream)     \
-                  : launch_shape<T, D, false>(sh, q, k, v, o, lse, BH, Nq, Nk, scale, stream)
+    return causal ? launch_shape<T, D, true, false>(sh, q, k, v, o, lse, BH, Nq, Nk, scale,      \
+                                                    MaskArgs{}, stream)                           \
+                  : launch_shape<T, D, false, false>(sh, q, k, v, o, lse, BH, Nq, Nk, scale,     \
+                                                     MaskArgs{}, stream)
     if (bf16) {
         if (d == 64) FA_DISPATCH(__bf16, 64);
         FA_DISPATCH(__bf16, 128);

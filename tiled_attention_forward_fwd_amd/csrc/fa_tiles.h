@@ -64,4 +64,62 @@ FA_HD inline TileSpan tile_span(int64_t q0, int64_t block_m, int64_t block_n, in
     return s;
 }
 
+// Padding and sliding-window masks. "How to optimise a Triton FlashAttention-2
+// kernel step by step with a profiler" ("Future articles") names them as the
+// case where a row can see no key at all. Row i of a batch with key_len keys
+// sees key j iff j < key_len, j >= i - window_left (window_left >= 0) and
+// j <= i (causal) or j <= i + window_right (not causal, window_right >= 0);
+// -1 leaves a window unbounded. The visible keys form one range [lo, hi),
+// with lo and hi non-decreasing in i; an empty row has hi <= lo. A row can
+// only be empty when hi is capped by key_len or the key count (the caps
+// i + 1 and i + window_right + 1 always exceed i - window_left), and since lo
+// keeps growing every later row is empty too: the non-empty rows of a tile
+// are a prefix of it, and their ranges overlap or touch, so their union is
+// the one range [lo of the first row, hi of the last row).
+struct RowKeys {
+    int64_t lo, hi;
+};
+
+FA_HD inline RowKeys row_keys(int64_t i, int64_t n_keys, bool causal, int64_t window_left,
+                              int64_t window_right, int64_t key_len)
+{
+    int64_t hi = causal ? i + 1 : (window_right >= 0 ? i + window_right + 1 : n_keys);
+    if (hi > n_keys) hi = n_keys;
+    if (hi > key_len) hi = key_len;
+    const int64_t lo = (window_left >= 0 && i - window_left > 0) ? i - window_left : 0;
+    RowKeys r;
+    r.lo = lo;
+    r.hi = hi;
+    return r;
+}
+
+// Key tiles of the rows [q0, min(q0 + block_m, n_queries)) under the masks:
+// tiles [first, end) are exactly those holding a key some row sees (none when
+// the first row is empty); within them the tiles [unmasked_begin,
+// unmasked_end) are seen in full by every row and need no mask. Since lo and
+// hi grow with the row, the first row bounds the start of the visited range
+// and the end of the unmasked one, and the last row the other two.
+struct MaskedSpan {
+    int64_t first, unmasked_begin, unmasked_end, end;
+};
+
+FA_HD inline MaskedSpan masked_span(int64_t q0, int64_t block_m, int64_t block_n, int64_t n_queries,
+                                    int64_t n_keys, bool causal, int64_t window_left,
+                                    int64_t window_right, int64_t key_len)
+{
+    const int64_t last = (q0 + block_m < n_queries ? q0 + block_m : n_queries) - 1;
+    const RowKeys a = row_keys(q0, n_keys, causal, window_left, window_right, key_len);
+    const RowKeys z = row_keys(last, n_keys, causal, window_left, window_right, key_len);
+    MaskedSpan s;
+    s.first = a.lo / block_n;
+    s.end = (z.hi + block_n - 1) / block_n;
+    if (a.hi <= a.lo || s.end < s.first) s.end = s.first;
+    int64_t ub = (z.lo + block_n - 1) / block_n, ue = a.hi / block_n;
+    ub = ub < s.first ? s.first : (ub > s.end ? s.end : ub);
+    ue = ue < ub ? ub : (ue > s.end ? s.end : ue);
+    s.unmasked_begin = ub;
+    s.unmasked_end = ue;
+    return s;
+}
+
 }  // namespace fa
