@@ -22,8 +22,11 @@ Other modes (used to collect counters; each runs a few launches only):
     --profile-kernels   a few launches of each headline kernel, nothing else
     --copy-calibration  a plain device-to-device copy of a known size
     --profile-decode    the split-key decode path (one query x 16384 keys, B=1 H=32)
+    --profile-masked    the padding and sliding-window workloads of the sweep
     --sweep             medians of 50 for every configuration of the workload
-                        list, with peak memory (one extra JSON object)
+                        list, with peak memory (one extra JSON object); the
+                        masked rows count exactly the visible (query, key)
+                        pairs (fa_plan_masked)
 """
 
 import argparse
@@ -41,7 +44,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk/CU x 2.4 GHz, dense (no sparsity)
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_forward_fwd_amd", "csrc", f)
-                  for f in ("fa_fwd_kernel.hip", "fa_device.h", "fa_tiles.h")]
+                  for f in ("fa_fwd_kernel.h", "fa_fwd_kernel.hip", "fa_device.h", "fa_tiles.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_bf16_d128_N4096.txt")
 
 HEADLINE = dict(B=4, H=16, N=4096, d=128, dtype="bf16", seed=7)
@@ -337,13 +340,16 @@ def sweep(args):
         dict(B=1, H=32, Nq=1, N=16384, d=128, dtype="bf16", seed=10, flags=(0,)),
         dict(B=4, H=32, Nq=1, N=16384, d=128, dtype="bf16", seed=11, flags=(0,)),
         dict(B=1, H=32, Nq=4096, N=16384, d=128, dtype="bf16", seed=12, flags=(1,)),
-    ]
+    ] + MASKED_WORKLOADS
     for cfg in configs:
         _, _, _, qd, kd, vd = make_inputs(cfg, dev)
         B, H, Nk, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
         Nq = cfg.get("Nq", Nk)
         qd = qd[:, :, :Nq].contiguous()
         code = fa.FA_DTYPE_BF16 if cfg["dtype"] == "bf16" else fa.FA_DTYPE_F16
+        wl, wr, kls = cfg.get("wl", -1), cfg.get("wr", -1), cfg.get("key_lens")
+        masked = wl != -1 or wr != -1 or kls is not None
+        kl_dev = None if kls is None else torch.tensor(kls, dtype=torch.int32, device=dev)
         for causal in cfg["flags"]:
             splits = fa.fa_split_count(B, H, Nq, Nk, d, causal)
             out = torch.empty_like(qd)
@@ -352,14 +358,19 @@ def sweep(args):
                               dtype=torch.float32) if splits > 1 else None)
 
             def fn(causal=causal, splits=splits, out=out, lse=lse, ws=ws):
-                fa.fwd(qd, kd, vd, causal=bool(causal), out=out, lse=lse, splits=splits, workspace=ws)
+                fa.fwd(qd, kd, vd, causal=bool(causal), out=out, lse=lse, splits=splits, workspace=ws,
+                       window_left=wl, window_right=wr, key_lens=kl_dev)
             warm(fn, 20, 0.5)
             torch.cuda.reset_peak_memory_stats(dev)
             ts = timed_launches(fn, 50, torch.cuda.current_stream(dev))
-            plan = fa.fa_plan_qk(B, H, Nq, Nk, d, causal, code)
+            if masked:
+                plan = fa.fa_plan_masked(B, H, Nq, Nk, d, causal, wl, wr, kls, code)
+            else:
+                plan = fa.fa_plan_qk(B, H, Nq, Nk, d, causal, code)
             med = statistics.median(ts)
             rows.append({"B": B, "H": H, "Nq": Nq, "N": Nk, "d": d,
                          "dtype": cfg["dtype"], "q_scale": cfg.get("q_scale", 1.0),
+                         **({"window_left": wl, "window_right": wr, "key_lens": kls} if masked else {}),
                          "causal": bool(causal), "splits": splits, "median_ms": med,
                          "min_ms": min(ts), "max_ms": max(ts),
                          "tflops": plan["algo_flops"] / (med * 1e-3) / 1e12,
@@ -371,6 +382,43 @@ def sweep(args):
         del qd, kd, vd
         torch.cuda.empty_cache()
     return rows
+
+
+# Padding and sliding-window workloads (sweep rows and --profile-masked):
+# a padded batch at the headline shape, the headline problem through the
+# masked kernel with a window that hides nothing (the cost of the masked
+# launch itself), a 4096-key sliding window over a 16384-token causal
+# sequence, the same at d = 64, and decode over four caches of different
+# lengths (split-key path).
+MASKED_WORKLOADS = [
+    dict(B=4, H=16, N=4096, d=128, dtype="bf16", seed=13, key_lens=[4096, 3072, 2048, 1024], flags=(0, 1)),
+    dict(B=4, H=16, N=4096, d=128, dtype="bf16", seed=7, wl=4096, flags=(0, 1)),
+    dict(B=1, H=32, N=16384, d=128, dtype="bf16", seed=14, wl=4095, flags=(1,)),
+    dict(B=4, H=16, N=8192, d=64, dtype="fp16", seed=15, wl=1023, flags=(1,)),
+    dict(B=4, H=32, Nq=1, N=16384, d=128, dtype="bf16", seed=16, key_lens=[16384, 12000, 8000, 4000],
+         flags=(0,)),
+]
+
+
+def profile_masked(args):
+    """`steps` calls of each masked workload (MASKED_WORKLOADS), after 5 untimed ones."""
+    import torch
+    import tiled_attention_forward_fwd_amd as fa
+    dev = torch.device("cuda:0")
+    for cfg in MASKED_WORKLOADS:
+        _, _, _, qd, kd, vd = make_inputs(cfg, dev)
+        Nq = cfg.get("Nq", cfg["N"])
+        qd = qd[:, :, :Nq].contiguous()
+        kl = None if cfg.get("key_lens") is None else torch.tensor(cfg["key_lens"], dtype=torch.int32,
+                                                                   device=dev)
+        for causal in cfg["flags"]:
+            for _ in range(5 + args.steps):
+                fa.fwd(qd, kd, vd, causal=bool(causal), window_left=cfg.get("wl", -1),
+                       window_right=cfg.get("wr", -1), key_lens=kl)
+        torch.cuda.synchronize()
+        del qd, kd, vd
+    print(json.dumps({"profiled": "masked workloads", "workloads": MASKED_WORKLOADS,
+                      "calls_each": 5 + args.steps}))
 
 
 def profile_kernels(args):
@@ -458,6 +506,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--profile-decode", action="store_true",
                     help="split-key decode calls only (one query x 16384 keys), for rocprofv3")
+    ap.add_argument("--profile-masked", action="store_true",
+                    help="padding and sliding-window workloads only, for rocprofv3")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -479,6 +529,8 @@ def main():
         return copy_calibration(args)
     if args.profile_decode:
         return profile_decode(args)
+    if args.profile_masked:
+        return profile_masked(args)
 
     out, (q, k, v) = headline(args)
     if args.backward:

@@ -89,11 +89,14 @@ namespace {
 //    of all heads first, id i -> head i % BH. Greedy dispatch of
 //    longest-first work then keeps every XCD busy to the end, and when BH is
 //    a multiple of 8 every tile of a head still lands on one XCD.
+//  * Padding lengths (the work of a head depends on its batch): the same
+//    tile-major order, so that every XCD gets heads of every batch instead
+//    of the contiguous range that would leave some XCDs all the long batches.
 template <bool CAUSAL>
-__device__ __forceinline__ void workgroup_tile(int n_qt, uint32_t& bh, uint32_t& qt)
+__device__ __forceinline__ void workgroup_tile(int n_qt, bool uneven_heads, uint32_t& bh, uint32_t& qt)
 {
     const uint32_t nwg = gridDim.x, hw = blockIdx.x;
-    if (CAUSAL) {
+    if (CAUSAL || uneven_heads) {
         const uint32_t n_bh = nwg / (uint32_t)n_qt;
         bh = hw % n_bh;
         qt = (uint32_t)n_qt - 1 - hw / n_bh;
@@ -105,6 +108,33 @@ __device__ __forceinline__ void workgroup_tile(int n_qt, uint32_t& bh, uint32_t&
         bh = logical / (uint32_t)n_qt;
         qt = logical % (uint32_t)n_qt;
     }
+}
+
+// Non-causal launches with padding lengths: every query tile of a batch costs
+// about the same, in proportion to the batch's key count, and dealing the
+// batches interleaved leaves the long ones to finish alone at the end.
+// Batches are taken longest first (largest key count, then lowest index),
+// each batch's heads tile-major as above, so that greedy dispatch runs the
+// longest work first. Each wave ranks the batches itself, one lane per batch
+// (B <= 64); the ranks form a permutation, so exactly one lane matches.
+__device__ __forceinline__ void padded_batch_tile(int n_qt, int heads, const int* key_lens, int n_keys,
+                                                  uint32_t& bh, uint32_t& qt)
+{
+    const uint32_t per_batch = (uint32_t)heads * (uint32_t)n_qt;
+    const int n_batch = (int)(gridDim.x / per_batch);
+    const int want = (int)(blockIdx.x / per_batch);
+    const uint32_t j = blockIdx.x % per_batch;
+    const int lane = threadIdx.x & 63;
+    const int mine = lane < n_batch ? min(max(key_lens[lane], 0), n_keys) : -1;
+    int rank = 0;
+    for (int u = 0; u < n_batch; ++u) {
+        const int other = __builtin_amdgcn_readlane(mine, u);
+        rank += (other > mine || (other == mine && u < lane)) ? 1 : 0;
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < n_batch && rank == want);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+    bh = b * (uint32_t)heads + j % (uint32_t)heads;
+    qt = j / (uint32_t)heads;
 }
 
 // Epilogue: O = O_acc / l in the input type, lse = (m + log2 l) * ln 2.
@@ -262,7 +292,11 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
         bh = rest / (uint32_t)n_qt;
         qt = rest % (uint32_t)n_qt;
     } else {
-        workgroup_tile<CAUSAL>(n_qt, bh, qt);
+        const bool padded = MASKS && mask.key_lens != nullptr;
+        if (!CAUSAL && padded && gridDim.x / ((uint32_t)mask.heads * (uint32_t)n_qt) <= 64)
+            padded_batch_tile(n_qt, mask.heads, mask.key_lens, Nk, bh, qt);
+        else
+            workgroup_tile<CAUSAL>(n_qt, padded, bh, qt);
     }
     const int q0 = (int)qt * C::BM;
 
