@@ -401,10 +401,13 @@ MASKED_WORKLOADS = [
 
 
 def profile_masked(args):
-    """`steps` calls of each masked workload (MASKED_WORKLOADS), after 5 untimed ones."""
+    """Each masked workload (MASKED_WORKLOADS, in order, each causal flag): untimed calls for at
+    least half a second (the clock ramps up under load), then `steps` calls; the JSON line lists
+    the (untimed, counted) call numbers in launch order."""
     import torch
     import tiled_attention_forward_fwd_amd as fa
     dev = torch.device("cuda:0")
+    calls = []
     for cfg in MASKED_WORKLOADS:
         _, _, _, qd, kd, vd = make_inputs(cfg, dev)
         Nq = cfg.get("Nq", cfg["N"])
@@ -412,13 +415,21 @@ def profile_masked(args):
         kl = None if cfg.get("key_lens") is None else torch.tensor(cfg["key_lens"], dtype=torch.int32,
                                                                    device=dev)
         for causal in cfg["flags"]:
-            for _ in range(5 + args.steps):
+            def fn(causal=causal):
                 fa.fwd(qd, kd, vd, causal=bool(causal), window_left=cfg.get("wl", -1),
                        window_right=cfg.get("wr", -1), key_lens=kl)
-        torch.cuda.synchronize()
+            n_warm, t0 = 0, time.perf_counter()
+            while n_warm < 5 or time.perf_counter() - t0 < 0.5:
+                fn()
+                n_warm += 1
+                if n_warm % 16 == 0:
+                    torch.cuda.synchronize()
+            for _ in range(args.steps):
+                fn()
+            torch.cuda.synchronize()
+            calls.append([n_warm, args.steps])
         del qd, kd, vd
-    print(json.dumps({"profiled": "masked workloads", "workloads": MASKED_WORKLOADS,
-                      "calls_each": 5 + args.steps}))
+    print(json.dumps({"profiled": "masked workloads", "workloads": MASKED_WORKLOADS, "calls": calls}))
 
 
 def profile_kernels(args):

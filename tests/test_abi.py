@@ -348,3 +348,15 @@ def test_fa_fwd_split_masked_rejects_before_any_hip_call(lib):
     for kw in [dict(wl=-3), dict(n=0), dict(n=65), dict(ws=None), dict(wsb=base["wsb"] - 4),
                dict(kl=ws + 64), dict(ws=ws + 8)]:
         assert run(**kw) == fa.FA_ERR_INVALID_ARG, kw
+
+
+def test_split_count_suggestion(lib):
+    # decode grids get 8 chunks, a full grid gets none, short keys stay direct
+    assert fa.fa_split_count(1, 32, 1, 16384, 128, 0) == 8
+    assert fa.fa_split_count(4, 32, 1, 16384, 128, 0) == 8
+    assert fa.fa_split_count(4, 16, 4096, 4096, 128, 0) == 1
+    assert fa.fa_split_count(1, 1, 1, 512, 64, 0) == 1
+    assert fa.fa_split_count(0, 1, 1, 512, 64, 0) == 0  # invalid
+    for B, H, Nq, Nk in [(1, 1, 1, 100000), (2, 8, 300, 5000), (16, 32, 1, 2048), (1, 64, 129, 65536)]:
+        s = fa.fa_split_count(B, H, Nq, Nk, 128, 0)
+        assert 1 <= s <= max(1, -(-Nk // 64) // 16)

@@ -311,12 +311,17 @@ int fa_split_count(int B, int H, int Nq, int Nk, int d, int causal)
     // keys: the best split gives the grid about 256 to 1024 workgroups and
     // every chunk at least 16 key tiles (a shorter chunk spends too much of
     // its time filling its pipeline). Short key sequences stay on the direct
-    // path, which needs no merge.
+    // path, which needs no merge. The smallest grids take at least 8 chunks:
+    // equal cache lengths run as fast with 8 as with 2 to 4, and caches of
+    // different lengths (padding) need the extra chunks to balance.
     const int64_t rows = fa::split_rows_per_tile();
     const int64_t wgs = (int64_t)B * H * (((int64_t)Nq + rows - 1) / rows);
     const int64_t n_kt = ((int64_t)Nk + 63) / 64;
     int64_t s = (256 + wgs - 1) / wgs;
-    if (wgs < 512 && s < 4) s = 4;
+    if (wgs <= 128 && s < 8)
+        s = 8;
+    else if (wgs < 512 && s < 4)
+        s = 4;
     if (s > n_kt / 16) s = n_kt / 16;
     return (int)(s < 1 ? 1 : s);
 }
