@@ -340,6 +340,9 @@ def sweep(args):
         dict(B=1, H=32, Nq=1, N=16384, d=128, dtype="bf16", seed=10, flags=(0,)),
         dict(B=4, H=32, Nq=1, N=16384, d=128, dtype="bf16", seed=11, flags=(0,)),
         dict(B=1, H=32, Nq=4096, N=16384, d=128, dtype="bf16", seed=12, flags=(1,)),
+        # head dims other than 64 and 128 (run by the d = 128 / d = 64 kernels, padded)
+        dict(B=4, H=16, N=4096, d=96, dtype="bf16", seed=17, flags=(0, 1)),
+        dict(B=4, H=16, N=4096, d=32, dtype="fp16", seed=18, flags=(0, 1)),
     ] + MASKED_WORKLOADS
     for cfg in configs:
         _, _, _, qd, kd, vd = make_inputs(cfg, dev)

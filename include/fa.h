@@ -40,7 +40,8 @@ extern "C" {
 typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1, /* NULL/misaligned/overlapping pointer, bad size, dtype or scale */
-    FA_ERR_UNSUPPORTED = 2, /* well-formed but not built: head dim other than 64 or 128 */
+    FA_ERR_UNSUPPORTED = 2, /* well-formed but not built: a head dim that is not a multiple of
+                               8 from 8 to 128 (backward: not 64 or 128) */
     FA_ERR_HIP = 3          /* the HIP runtime reported an error (see fa_status_string) */
 } fa_status;
 
@@ -63,7 +64,13 @@ typedef enum {
  *             in "How to optimise a Triton FlashAttention-2 kernel step by
  *             step with a profiler", Round 4, "exp2").
  *   B, H, N : >= 1, with N*d*2 < 2^32 (one head below 4 GiB).
- *   d       : 64 or 128 (other values: FA_ERR_UNSUPPORTED).
+ *   d       : a multiple of 8 from 8 to 128 (other values: FA_ERR_UNSUPPORTED).
+ *             64 and 128 have kernels of their own; any other d runs with
+ *             the d = 64 kernel (d < 64) or the d = 128 kernel, the missing
+ *             dims held at zero on chip, so the result is that of head dim d
+ *             at the MFMA cost of the larger one. ("How to optimise a Triton
+ *             FlashAttention-2 kernel step by step with a profiler" runs its
+ *             tests over several shapes, input types and head dims, Round 3.)
  *   causal  : 0 or 1.
  *   scale   : finite and > 0; multiplies Q K^T before the softmax
  *             (1/sqrt(d) is the usual choice, the caller computes it).
@@ -110,7 +117,8 @@ int fa_fwd_qk(const void *q, const void *k, const void *v, void *o, float *lse, 
  *   workgroups in all and at least 16 key tiles of 64 per chunk (1, the
  *   direct path, for short key sequences). Returns 0 on invalid arguments.
  * fa_split_workspace_bytes -- bytes of workspace fa_fwd_split_qk needs:
- *   n_splits * B*H*Nq * (d + 1) * 4. Returns 0 on invalid arguments.
+ *   n_splits * B*H*Nq * (D + 1) * 4, with D = 64 for d <= 64 and 128
+ *   otherwise (the kernel's head dim). Returns 0 on invalid arguments.
  * fa_fwd_split_qk -- arguments as fa_fwd_qk, plus:
  *   n_splits        : 1 .. ceil(Nk / 64).
  *   workspace       : device, >= fa_split_workspace_bytes(...) bytes,
@@ -182,8 +190,9 @@ int fa_fwd_split_masked(const void *q, const void *k, const void *v, void *o, fl
  *   delta            : device, [B, H, N] fp32, 16-byte aligned, owned by the
  *                      caller: scratch that receives D (libfa allocates
  *                      nothing).
- * Other arguments as fa_fwd. Three kernels are enqueued on `stream`; nothing
- * uses atomics, so results are deterministic.
+ * Other arguments as fa_fwd, except that d must be 64 or 128. Three kernels
+ * are enqueued on `stream`; nothing uses atomics, so results are
+ * deterministic.
  */
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
            const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H, int N, int d,
@@ -239,8 +248,9 @@ typedef struct {
     int lds_bytes;          /* LDS per workgroup */
     int64_t workgroups;     /* grid size */
     int64_t pairs_visited;  /* visited (query tile, key tile) pairs, all heads */
-    double mfma_flops;      /* FLOPs the matrix cores execute: 4*d per (row, key)
-                               of every visited tile pair, masked ones included */
+    double mfma_flops;      /* FLOPs the matrix cores execute: 4*D per (row, key)
+                               of every visited tile pair, masked ones included,
+                               D the kernel's head dim (64 or 128) */
     double algo_flops;      /* 4*d per (query, key) pair of the visible region:
                                4*B*H*Nq*Nk*d non-causal; causal counts the area
                                below the diagonal, Nq*Nq/2 for Nq <= Nk and

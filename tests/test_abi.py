@@ -62,8 +62,9 @@ def call(**kw):
     (dict(N=0), fa.FA_ERR_INVALID_ARG),              # empty sequence
     (dict(B=0), fa.FA_ERR_INVALID_ARG),
     (dict(H=-1), fa.FA_ERR_INVALID_ARG),
-    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
-    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=100), fa.FA_ERR_UNSUPPORTED),            # not a multiple of 8
+    (dict(d=136), fa.FA_ERR_UNSUPPORTED),            # above 128
+    (dict(d=0), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=7), fa.FA_ERR_INVALID_ARG),
     (dict(causal=2), fa.FA_ERR_INVALID_ARG),
     (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
@@ -145,7 +146,7 @@ def test_plan_flop_convention_matches_t4_table(lib):
 
 def test_plan_rejects_like_fa_fwd(lib):
     with pytest.raises(fa.FaError) as e:
-        fa.fa_plan(1, 1, 16, 80, 0, fa.FA_DTYPE_BF16)
+        fa.fa_plan(1, 1, 16, 84, 0, fa.FA_DTYPE_BF16)
     assert e.value.status == fa.FA_ERR_UNSUPPORTED
     with pytest.raises(fa.FaError):
         fa.fa_plan(1, 1, 0, 64, 0, fa.FA_DTYPE_BF16)
@@ -176,7 +177,8 @@ def call_qk(**kw):
     (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
     (dict(Nq=0), fa.FA_ERR_INVALID_ARG),
     (dict(Nk=-5), fa.FA_ERR_INVALID_ARG),
-    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=4), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=81), fa.FA_ERR_UNSUPPORTED),
     (dict(Nk=1 << 24, d=128), fa.FA_ERR_INVALID_ARG),   # one key head >= 4 GiB
     (dict(Nq=1 << 24, d=128), fa.FA_ERR_INVALID_ARG),   # one query head >= 4 GiB
     (dict(o=P[1] + 32 * 64 * 2), fa.FA_ERR_INVALID_ARG),  # o inside k's 48 rows (not q's 16)
@@ -360,3 +362,25 @@ def test_split_count_suggestion(lib):
     for B, H, Nq, Nk in [(1, 1, 1, 100000), (2, 8, 300, 5000), (16, 32, 1, 2048), (1, 64, 129, 65536)]:
         s = fa.fa_split_count(B, H, Nq, Nk, 128, 0)
         assert 1 <= s <= max(1, -(-Nk // 64) // 16)
+
+
+# ---- head dims other than 64 and 128 (run padded by the d = 64 / 128 kernels)
+
+@pytest.mark.parametrize("d", [8, 16, 32, 40, 48, 56, 72, 80, 96, 112, 120])
+def test_plan_other_head_dims(lib, d):
+    D = 64 if d <= 64 else 128
+    for causal in (0, 1):
+        p = fa.fa_plan_qk(2, 8, 1000, 1500, d, causal, fa.FA_DTYPE_BF16)
+        ref = fa.fa_plan_qk(2, 8, 1000, 1500, D, causal, fa.FA_DTYPE_BF16)
+        # same grid and tiles as the kernel head dim; algorithmic work at d,
+        # executed MFMA work at the kernel head dim
+        for key in ("block_m", "block_n", "threads", "lds_bytes", "workgroups", "pairs_visited", "mfma_flops"):
+            assert p[key] == ref[key], key
+        assert p["algo_flops"] == ref["algo_flops"] * d / D
+        assert p["algo_bytes"] == 4 * 2 * 8 * (1000 + 1500) * d + 4 * 2 * 8 * 1000
+    assert fa.fa_split_workspace_bytes(1, 4, 3, d, 5) == 5 * 4 * 3 * (D + 1) * 4
+
+
+def test_backward_keeps_head_dims_64_and_128(lib):
+    args = [P[0], P[1], P[2], P[3], P[4], 0x60000, 0x70000, 0x80000, 0x90000, 0xa0000]
+    assert fa.fa_bwd(*args, 1, 1, 16, 96, 0, 0.1, fa.FA_DTYPE_BF16, None) == fa.FA_ERR_UNSUPPORTED

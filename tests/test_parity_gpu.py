@@ -322,7 +322,11 @@ def test_python_binding_rejects_bad_tensors():
         fa.fwd(q.transpose(2, 3), k, v)
     with pytest.raises(fa.FaError):
         fa.fwd(q, k, v, scale=-1.0)
-    q96 = torch.zeros(1, 1, 64, 96, dtype=torch.bfloat16, device="cuda")
+    q100 = torch.zeros(1, 1, 64, 100, dtype=torch.bfloat16, device="cuda")  # not a multiple of 8
     with pytest.raises(fa.FaError) as e:
-        fa.fwd(q96, q96, q96)
+        fa.fwd(q100, q100, q100)
+    assert e.value.status == fa.FA_ERR_UNSUPPORTED
+    q256 = torch.zeros(1, 1, 64, 256, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FaError) as e:
+        fa.fwd(q256, q256, q256)
     assert e.value.status == fa.FA_ERR_UNSUPPORTED

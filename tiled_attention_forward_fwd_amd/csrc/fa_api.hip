@@ -40,7 +40,8 @@ int check_problem(int B, int H, int Nq, int Nk, int d, int causal, int dtype)
     if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
     if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
         return fail(FA_ERR_INVALID_ARG, "dtype must be FA_DTYPE_F16 or FA_DTYPE_BF16");
-    if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+    if (d < 8 || d > 128 || d % 8 != 0)
+        return fail(FA_ERR_UNSUPPORTED, "head dim must be a multiple of 8 from 8 to 128");
     const int64_t bh = (int64_t)B * H;
     const int64_t n_qt = ((int64_t)Nq + 127) / 128;  // the smallest workgroup tile
     if (bh > INT32_MAX || bh * n_qt > (int64_t)UINT32_MAX)
@@ -82,7 +83,7 @@ int check_split(const void* q, const void* k, const void* v, void* o, float* lse
     if (!aligned(workspace, 16)) return fail(FA_ERR_INVALID_ARG, "the workspace must be 16-byte aligned");
     if (n_splits < 1 || n_splits > (Nk + 63) / 64)
         return fail(FA_ERR_INVALID_ARG, "n_splits must be between 1 and ceil(Nk / 64)");
-    const int64_t need = (int64_t)n_splits * B * H * Nq * (d + 1) * 4;
+    const int64_t need = (int64_t)n_splits * B * H * Nq * (fa::kernel_dim(d) + 1) * 4;
     if ((int64_t)B * H * ((Nq + 127) / 128) * n_splits > (int64_t)UINT32_MAX)
         return fail(FA_ERR_INVALID_ARG, "B*H*ceil(Nq/128)*n_splits exceeds the grid limit");
     if (workspace_bytes < need) return fail(FA_ERR_INVALID_ARG, "workspace too small");
@@ -119,6 +120,27 @@ int check_masks(int B, int H, int Nq, int d, int window_left, int window_right,
 bool masks_off(int causal, int window_left, int window_right, const int32_t* key_lens)
 {
     return !key_lens && window_left < 0 && (causal || window_right < 0);
+}
+
+fa::FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                     int Nq, int Nk, int d, int causal, float scale, int dtype, void* stream)
+{
+    fa::FwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.B = B;
+    a.H = H;
+    a.Nq = Nq;
+    a.Nk = Nk;
+    a.d = d;
+    a.causal = causal != 0;
+    a.scale = scale;
+    a.bf16 = dtype == FA_DTYPE_BF16;
+    a.stream = (hipStream_t)stream;
+    return a;
 }
 
 int hip_status(hipError_t e)
@@ -194,8 +216,9 @@ int fa_plan_qk(int B, int H, int Nq, int Nk, int d, int causal, int dtype, fa_pl
     plan->lds_bytes = fa::lds_bytes(d);
     plan->workgroups = bh * ((Nq + bm - 1) / bm);
     plan->pairs_visited = bh * counts[1];
-    // every visited pair costs S = Q K^T and P V, masked pairs included
-    plan->mfma_flops = 4.0 * d * (double)bm * bn * (double)plan->pairs_visited;
+    // every visited pair costs S = Q K^T and P V, masked pairs included, at
+    // the kernel's head dim
+    plan->mfma_flops = 4.0 * fa::kernel_dim(d) * (double)bm * bn * (double)plan->pairs_visited;
     const double pairs = causal ? causal_area(Nq, Nk) : (double)Nq * (double)Nk;
     plan->algo_flops = 4.0 * (double)bh * pairs * d;
     plan->algo_bytes = 4.0 * (double)bh * ((double)Nq + Nk) * d + 4.0 * (double)bh * Nq;
@@ -266,7 +289,7 @@ int fa_plan_masked(int B, int H, int Nq, int Nk, int d, int causal, int window_l
     plan->lds_bytes = fa::lds_bytes(d);
     plan->workgroups = (int64_t)B * H * ((Nq + bm - 1) / bm);
     plan->pairs_visited = (int64_t)(tiles * H);
-    plan->mfma_flops = 4.0 * d * (double)bm * bn * (double)plan->pairs_visited;
+    plan->mfma_flops = 4.0 * fa::kernel_dim(d) * (double)bm * bn * (double)plan->pairs_visited;
     plan->algo_flops = 4.0 * H * pairs * d;
     plan->algo_bytes = 4.0 * H * ((double)B * Nq + keys_read) * d + 4.0 * (double)B * H * Nq;
     return FA_OK;
@@ -283,8 +306,8 @@ int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, 
     g_msg[0] = 0;
     const int rc = check_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype);
     if (rc != FA_OK) return rc;
-    return hip_status(fa::launch_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, scale,
-                                     dtype == FA_DTYPE_BF16, (hipStream_t)stream));
+    return hip_status(fa::launch_forward(fwd_args(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype,
+                                                  stream)));
 }
 
 int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -296,12 +319,10 @@ int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* l
     if (rc != FA_OK) return rc;
     rc = check_masks(B, H, Nq, d, window_left, window_right, key_lens, o, lse, nullptr, 0);
     if (rc != FA_OK) return rc;
-    if (masks_off(causal, window_left, window_right, key_lens))
-        return hip_status(fa::launch_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, scale,
-                                         dtype == FA_DTYPE_BF16, (hipStream_t)stream));
-    const fa::MaskArgs mask{window_left, window_right, key_lens, H};
-    return hip_status(fa::launch_fwd_masked(q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, mask,
-                                            scale, dtype == FA_DTYPE_BF16, (hipStream_t)stream));
+    fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, stream);
+    a.masked = !masks_off(causal, window_left, window_right, key_lens);
+    a.mask = fa::MaskArgs{window_left, window_right, key_lens, H};
+    return hip_status(fa::launch_forward(a));
 }
 
 int fa_split_count(int B, int H, int Nq, int Nk, int d, int causal)
@@ -328,8 +349,8 @@ int fa_split_count(int B, int H, int Nq, int Nk, int d, int causal)
 
 int64_t fa_split_workspace_bytes(int B, int H, int Nq, int d, int n_splits)
 {
-    if (B < 1 || H < 1 || Nq < 1 || (d != 64 && d != 128) || n_splits < 1) return 0;
-    return (int64_t)n_splits * B * H * Nq * (d + 1) * 4;
+    if (B < 1 || H < 1 || Nq < 1 || d < 8 || d > 128 || d % 8 != 0 || n_splits < 1) return 0;
+    return (int64_t)n_splits * B * H * Nq * (fa::kernel_dim(d) + 1) * 4;
 }
 
 int fa_fwd_split_qk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -341,9 +362,11 @@ int fa_fwd_split_qk(const void* q, const void* k, const void* v, void* o, float*
     if (rc != FA_OK) return rc;
     rc = check_split(q, k, v, o, lse, B, H, Nq, Nk, d, n_splits, workspace, workspace_bytes);
     if (rc != FA_OK) return rc;
-    return hip_status(fa::launch_fwd_split(q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, scale,
-                                           dtype == FA_DTYPE_BF16, n_splits, (float*)workspace,
-                                           (hipStream_t)stream));
+    fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, stream);
+    a.split = true;
+    a.n_splits = n_splits;
+    a.workspace = (float*)workspace;
+    return hip_status(fa::launch_forward(a));
 }
 
 int fa_fwd_split_masked(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -359,14 +382,13 @@ int fa_fwd_split_masked(const void* q, const void* k, const void* v, void* o, fl
     rc = check_masks(B, H, Nq, d, window_left, window_right, key_lens, o, lse, workspace,
                      workspace_bytes);
     if (rc != FA_OK) return rc;
-    if (masks_off(causal, window_left, window_right, key_lens))
-        return hip_status(fa::launch_fwd_split(q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, scale,
-                                               dtype == FA_DTYPE_BF16, n_splits, (float*)workspace,
-                                               (hipStream_t)stream));
-    const fa::MaskArgs mask{window_left, window_right, key_lens, H};
-    return hip_status(fa::launch_fwd_split_masked(q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0,
-                                                  mask, scale, dtype == FA_DTYPE_BF16, n_splits,
-                                                  (float*)workspace, (hipStream_t)stream));
+    fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, stream);
+    a.masked = !masks_off(causal, window_left, window_right, key_lens);
+    a.mask = fa::MaskArgs{window_left, window_right, key_lens, H};
+    a.split = true;
+    a.n_splits = n_splits;
+    a.workspace = (float*)workspace;
+    return hip_status(fa::launch_forward(a));
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -382,6 +404,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     if (!aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
     const int rc = check_problem(B, H, N, N, d, causal, dtype);
     if (rc != FA_OK) return rc;
+    if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "the backward pass takes head dim 64 or 128");
     if (!(scale > 0.f) || !isfinite(scale))
         return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
     const size_t tb = (size_t)B * H * N * d * 2, lb = (size_t)B * H * N * 4;

@@ -446,5 +446,69 @@ __device__ __forceinline__ void load_q(const T* __restrict__ qh, int row0, int n
     }
 }
 
+// Head dims below the kernel's D (PADDED launches): the head's rows are dm
+// elements apart in memory (dm a multiple of 8, dm < D) and the kernel runs
+// with D, the missing dims held at zero. Q dims past dm load as zero.
+template <typename T, int D, int QB, int DS>
+__device__ __forceinline__ void load_q_padded(const T* __restrict__ qh, int dm, int row0, int n_rows, int l32,
+                                              int hh, int (&qrow)[QB], typename Mma<T>::vec8 (&qf)[QB][DS])
+{
+    typedef typename Mma<T>::vec8 vec8;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        qrow[qb] = row0 + qb * 32 + l32;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            const int c0 = ds * 16 + hh * 8;
+            if (qrow[qb] < n_rows && c0 < dm) x = *(const u32x4*)(qh + (int64_t)qrow[qb] * dm + c0);
+            qf[qb][ds] = as_vec8<vec8>(x);
+        }
+    }
+}
+
+// K/V copies of a PADDED launch: the lane's logical chunk (pc ^ swz) is a
+// real one iff it lies below dm / 8; the other lanes copy nothing, and the
+// LDS chunks they would fill hold zeros written once (zero_pad_chunks). The
+// swizzle has period 16 in the row and consecutive copies of a lane are a
+// multiple of 16 rows apart, so a lane's chunk is real for all its copies or
+// for none.
+template <int D>
+__device__ __forceinline__ uint32_t tile_lane_offset_padded(int wave, int lane, int dm, bool& real)
+{
+    const int c = wave * 64 + lane;
+    const int r0 = c / (D / 8), lc = (c % (D / 8)) ^ swz<D>(r0);
+    real = lc < dm / 8;
+    return (uint32_t)(r0 * dm * 2 + lc * 16);
+}
+
+template <int D, int WAVES, int QB>
+__device__ __forceinline__ void issue_tile_padded(uint16_t* buf, rsrc_t src, int k0, int wave, uint32_t lane_off,
+                                                  bool real, int dm)
+{
+    typedef Cfg<D, WAVES, QB> C;
+    constexpr int rows_per_copy = WAVES * 64 / C::CPR;
+    if (real) {
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i)
+            copy16_to_lds(src, buf + (i * WAVES + wave) * 64 * 8, lane_off,
+                          (uint32_t)(k0 + i * rows_per_copy) * (uint32_t)(dm * 2));
+    }
+}
+
+// Zeros the LDS chunks of the dims past dm in n_tiles consecutive tile
+// buffers (their positions are the same in every tile and no copy writes
+// them).
+template <int D, int WAVES, int QB>
+__device__ __forceinline__ void zero_pad_chunks(uint16_t* buf0, int n_tiles, int dm, int tid)
+{
+    typedef Cfg<D, WAVES, QB> C;
+    for (int c = tid; c < C::BN * C::CPR; c += C::THREADS) {
+        const int r = c / C::CPR, lc = (c % C::CPR) ^ swz<D>(r);
+        if (lc >= dm / 8)
+            for (int t = 0; t < n_tiles; ++t) *(u32x4*)(buf0 + t * C::TILE + c * 8) = (u32x4){0u, 0u, 0u, 0u};
+    }
+}
+
 }  // namespace
 }  // namespace fa

@@ -140,18 +140,20 @@ __device__ __forceinline__ void padded_batch_tile(int n_qt, int heads, const int
 // Epilogue: O = O_acc / l in the input type, lse = (m + log2 l) * ln 2.
 // EMPTY: rows may have seen no key (masks); such a row has l = 0 and gets
 // O = 0 and lse = -inf.
-template <typename T, int D, int QB, int DB, bool EMPTY>
+// PADDED: rows are dm elements apart and only dims below dm are written.
+template <typename T, int D, int QB, int DB, bool EMPTY, bool PADDED>
 __device__ __forceinline__ void store_outputs(const f32x16 (&oacc)[QB][DB], const float (&m_run)[QB],
                                               const float (&l_run)[QB], const int (&qrow)[QB], int n_rows,
-                                              T* __restrict__ oh, float* __restrict__ lseh, int hh)
+                                              T* __restrict__ oh, float* __restrict__ lseh, int hh, int dm)
 {
+    const int stride = PADDED ? dm : D;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float l_tot = swap_halves_sum(l_run[qb]);
         if (qrow[qb] < n_rows) {
             const bool seen = !EMPTY || l_tot > 0.f;
             const float inv = seen ? 1.0f / l_tot : 0.f;
-            T* orow = oh + (int64_t)qrow[qb] * D;
+            T* orow = oh + (int64_t)qrow[qb] * stride;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -160,7 +162,8 @@ __device__ __forceinline__ void store_outputs(const f32x16 (&oacc)[QB][DB], cons
 #pragma unroll
                     for (int t = 0; t < 4; ++t) vals[t] = to_elem<T>(oacc[qb][db][4 * g + t] * inv);
                     u32x2 packed = __builtin_bit_cast(u32x2, vals);
-                    *(u32x2*)(orow + db * 32 + 8 * g + 4 * hh) = packed;
+                    const int col = db * 32 + 8 * g + 4 * hh;
+                    if (!PADDED || col < dm) *(u32x2*)(orow + col) = packed;
                 }
             }
             if (hh == 0) lseh[qrow[qb]] = seen ? (m_run[qb] + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
@@ -212,10 +215,12 @@ __device__ __forceinline__ void store_partials(const f32x16 (&oacc)[QB][DB], con
 // in groups of 16 whose loads are all issued before any is used, so a call
 // with up to 16 chunks makes two rounds of memory reads (the logsumexps, then
 // the partial outputs) instead of one per chunk.
+// The partial rows hold D floats (a PADDED launch's extra dims are zero);
+// O rows are dm elements apart and only dims below dm are written.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__ ws_o,
                                                        const float* __restrict__ ws_lse, T* __restrict__ o,
-                                                       float* __restrict__ lse, int64_t n_rows, int n_splits)
+                                                       float* __restrict__ lse, int64_t n_rows, int n_splits, int dm)
 {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     constexpr int TPR = D / 8, G = 16;  // threads per row, chunks per group
@@ -265,7 +270,7 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
         vals[e] = to_elem<T>(acc0[e] * inv);
         vals[4 + e] = to_elem<T>(acc1[e] * inv);
     }
-    *(u32x4*)(o + row * D + c0) = __builtin_bit_cast(u32x4, vals);
+    if (c0 < dm) *(u32x4*)(o + row * dm + c0) = __builtin_bit_cast(u32x4, vals);
     if (c0 == 0) lse[row] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
@@ -274,12 +279,15 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
 // left window edge), an unmasked middle and a masked suffix (diagonal, right
 // window edge, padding); each wave computes only the tiles its own rows can
 // see, and a row that sees nothing ends with O = 0 and lse = -inf.
-template <typename T, int D, bool CAUSAL, int WAVES, int QB, bool SPLIT, bool MASKS>
+// PADDED: the head dim dm (a multiple of 8 below D) is run with D; K/V
+// lanes of the missing dims copy nothing and their LDS chunks stay zero, Q
+// loads zeros there, and only dm dims of O are written.
+template <typename T, int D, bool CAUSAL, int WAVES, int QB, bool SPLIT, bool MASKS, bool PADDED>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
                           amdgpu_waves_per_eu(2 / QB, 2 / QB)))
 void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                    T* __restrict__ o, float* __restrict__ lse, int Nq, int Nk, int n_qt, float c_log2,
-                   int n_splits, float* __restrict__ ws_o, float* __restrict__ ws_lse, MaskArgs mask)
+                   int n_splits, float* __restrict__ ws_o, float* __restrict__ ws_lse, MaskArgs mask, int dm)
 {
     typedef Cfg<D, WAVES, QB> C;
     typedef typename Mma<T>::vec8 vec8;
@@ -303,7 +311,8 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
-    const int64_t q_off = (int64_t)bh * Nq * D, kv_off = (int64_t)bh * Nk * D;
+    const int dmem = PADDED ? dm : D;  // row length in memory
+    const int64_t q_off = (int64_t)bh * Nq * dmem, kv_off = (int64_t)bh * Nk * dmem;
     const T* kh = k + kv_off;
     const T* vh = v + kv_off;
     // The exp2 work of tile j is interleaved with the score MFMAs of tile j+1
@@ -313,7 +322,10 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 
     int qrow[QB];
     vec8 qf[QB][C::DS];
-    load_q<T, D, QB, C::DS>(q + q_off, q0 + wave * QB * 32, Nq, l32, hh, qrow, qf);
+    if (PADDED)
+        load_q_padded<T, D, QB, C::DS>(q + q_off, dm, q0 + wave * QB * 32, Nq, l32, hh, qrow, qf);
+    else
+        load_q<T, D, QB, C::DS>(q + q_off, q0 + wave * QB * 32, Nq, l32, hh, qrow, qf);
 
     // key tiles [t0, t1) of the query tile, of which [u_lo, u_hi) need no mask
     int t0 = 0, t1, u_lo = 0, u_hi;
@@ -355,9 +367,18 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     auto kbuf = [&](int i) { return smem + (i & 1) * C::TILE; };
     auto vbuf = [&](int i) { return smem + (2 + (i & 1)) * C::TILE; };
 
-    const uint32_t head_bytes = (uint32_t)Nk * (D * 2);
+    const uint32_t head_bytes = (uint32_t)Nk * (uint32_t)(dmem * 2);
     const rsrc_t krs = head_rsrc(kh, head_bytes), vrs = head_rsrc(vh, head_bytes);
-    const uint32_t lane_off = tile_lane_offset<D>(wave, lane);
+    bool real_chunk = true;
+    const uint32_t lane_off = PADDED ? tile_lane_offset_padded<D>(wave, lane, dm, real_chunk)
+                                     : tile_lane_offset<D>(wave, lane);
+    if (PADDED) zero_pad_chunks<D, WAVES, QB>(smem, 4, dm, tid);
+    auto issue = [&](uint16_t* buf, rsrc_t src, int k0) {
+        if (PADDED)
+            issue_tile_padded<D, WAVES, QB>(buf, src, k0, wave, lane_off, real_chunk, dm);
+        else
+            issue_tile<D, WAVES, QB>(buf, src, k0, wave, lane_off);
+    };
     // Causal: the key tiles this wave's rows can see form the prefix
     // [0, n_wave); in the diagonal tiles past it the wave only helps with the
     // copies and the barriers. In a split launch a wave whose rows all lie
@@ -415,9 +436,9 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 #pragma unroll
             for (int kb = 0; kb < C::KB; ++kb) sa[qb][kb] = (f32x16){};
     } else {
-        issue_tile<D, WAVES, QB>(kbuf(jb), krs, jb * C::BN, wave, lane_off);
-        issue_tile<D, WAVES, QB>(vbuf(jb), vrs, jb * C::BN, wave, lane_off);
-        if (jb + 1 < je) issue_tile<D, WAVES, QB>(kbuf(jb + 1), krs, (jb + 1) * C::BN, wave, lane_off);
+        issue(kbuf(jb), krs, jb * C::BN);
+        issue(vbuf(jb), vrs, jb * C::BN);
+        if (jb + 1 < je) issue(kbuf(jb + 1), krs, (jb + 1) * C::BN);
         stage_barrier();
         // every wave processes an unmasked tile of a direct launch
         if ((!SPLIT && (!MASKS || (jb >= u_lo && jb < u_hi))) || wave_sees(jb))
@@ -431,9 +452,8 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
         // M: the tile gets the mask; G: per-wave limits apply (masked tiles,
         // and every tile of a split launch)
         constexpr bool M = decltype(masked)::value, G = M || SPLIT;
-        if (j + 2 < je)
-            issue_tile<D, WAVES, QB>(kbuf(j), krs, (j + 2) * C::BN, wave, lane_off);
-        issue_tile<D, WAVES, QB>(vbuf(j + 1), vrs, (j + 1) * C::BN, wave, lane_off);
+        if (j + 2 < je) issue(kbuf(j), krs, (j + 2) * C::BN);
+        issue(vbuf(j + 1), vrs, (j + 1) * C::BN);
         if (kFuseExp) {
             if (!G || wave_sees(j)) {
                 if (M) apply_mask(sc[0], j, 0);
@@ -528,32 +548,32 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
         const int64_t slot = ((int64_t)split * (gridDim.x / ((uint32_t)n_splits * (uint32_t)n_qt)) + bh) * Nq;
         store_partials<D, QB, C::DB>(oacc, m_run, l_run, qrow, Nq, ws_o + slot * D, ws_lse + slot, hh);
     } else {
-        store_outputs<T, D, QB, C::DB, MASKS>(oacc, m_run, l_run, qrow, Nq, o + q_off, lse + (int64_t)bh * Nq,
-                                              hh);
+        store_outputs<T, D, QB, C::DB, MASKS, PADDED>(oacc, m_run, l_run, qrow, Nq, o + q_off,
+                                                      lse + (int64_t)bh * Nq, hh, dm);
     }
 }
 
-template <typename T, int D, bool CAUSAL, int WAVES, int QB, bool MASKS>
+template <typename T, int D, bool CAUSAL, int WAVES, int QB, bool MASKS, bool PADDED>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                      int Nq, int Nk, float scale, const MaskArgs& mask, hipStream_t stream)
+                      int Nq, int Nk, float scale, const MaskArgs& mask, int dm, hipStream_t stream)
 {
     typedef Cfg<D, WAVES, QB> C;
     const int n_qt = (Nq + C::BM - 1) / C::BM;
     const float c_log2 = scale * 1.4426950408889634f;
     dim3 grid((unsigned)((int64_t)n_qt * BH)), block(C::THREADS);
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, WAVES, QB, false, MASKS>), grid, block, 0, stream,
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, WAVES, QB, false, MASKS, PADDED>), grid, block, 0, stream,
                        (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, Nq, Nk, n_qt, c_log2, 1,
-                       (float*)nullptr, (float*)nullptr, mask);
+                       (float*)nullptr, (float*)nullptr, mask, dm);
     return hipGetLastError();
 }
 
 // Split launch (4-wave, 128-row workgroups) followed by the merge; the
 // workspace holds n_splits * B*H*Nq partial rows of D floats and then as many
 // logsumexps.
-template <typename T, int D, bool CAUSAL, bool MASKS>
+template <typename T, int D, bool CAUSAL, bool MASKS, bool PADDED>
 hipError_t launch_split(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                         int Nq, int Nk, float scale, int n_splits, float* ws, const MaskArgs& mask,
-                        hipStream_t stream)
+                        int dm, hipStream_t stream)
 {
     typedef Cfg<D, 4, 1> C;
     const int n_qt = (Nq + C::BM - 1) / C::BM;
@@ -562,30 +582,64 @@ hipError_t launch_split(const void* q, const void* k, const void* v, void* o, fl
     float* ws_o = ws;
     float* ws_lse = ws + (int64_t)n_splits * n_rows * D;
     dim3 grid((unsigned)((int64_t)n_qt * BH * n_splits)), block(C::THREADS);
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, 4, 1, true, MASKS>), grid, block, 0, stream, (const T*)q,
-                       (const T*)k, (const T*)v, (T*)o, lse, Nq, Nk, n_qt, c_log2, n_splits, ws_o,
-                       ws_lse, mask);
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, 4, 1, true, MASKS, PADDED>), grid, block, 0, stream,
+                       (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, Nq, Nk, n_qt, c_log2, n_splits,
+                       ws_o, ws_lse, mask, dm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t threads = n_rows * (D / 8);
     dim3 mgrid((unsigned)((threads + 255) / 256)), mblock(256);
     hipLaunchKernelGGL((fa_merge_kernel<T, D>), mgrid, mblock, 0, stream, (const float*)ws_o,
-                       (const float*)ws_lse, (T*)o, lse, n_rows, n_splits);
+                       (const float*)ws_lse, (T*)o, lse, n_rows, n_splits, PADDED ? dm : D);
     return hipGetLastError();
 }
 
-template <typename T, int D, bool CAUSAL, bool MASKS>
+template <typename T, int D, bool CAUSAL, bool MASKS, bool PADDED>
 hipError_t launch_shape(const Shape& sh, const void* q, const void* k, const void* v, void* o,
-                        float* lse, int BH, int Nq, int Nk, float scale, const MaskArgs& mask,
+                        float* lse, int BH, int Nq, int Nk, float scale, const MaskArgs& mask, int dm,
                         hipStream_t stream)
 {
-    // masked d=128 stays on 4 waves: the 8-wave kernel has no registers left
-    // for the per-row key ranges
-    if constexpr (!(MASKS && D == 128)) {
+    // 8 waves for non-causal problems only (pick_shape), and never for masked
+    // d=128: that kernel has no registers left for the per-row key ranges
+    if constexpr (!CAUSAL && !(MASKS && D == 128)) {
         if (sh.waves == 8)
-            return launch_one<T, D, CAUSAL, 8, 1, MASKS>(q, k, v, o, lse, BH, Nq, Nk, scale, mask, stream);
+            return launch_one<T, D, CAUSAL, 8, 1, MASKS, PADDED>(q, k, v, o, lse, BH, Nq, Nk, scale, mask, dm,
+                                                                 stream);
     }
-    return launch_one<T, D, CAUSAL, 4, 1, MASKS>(q, k, v, o, lse, BH, Nq, Nk, scale, mask, stream);
+    return launch_one<T, D, CAUSAL, 4, 1, MASKS, PADDED>(q, k, v, o, lse, BH, Nq, Nk, scale, mask, dm, stream);
+}
+
+template <typename T>
+struct TypeTag {
+    typedef T type;
+};
+
+// One forward launch of the MASKS / PADDED variant: dispatch on dtype, the
+// kernel head dim and causality, then the direct or the split launch.
+template <bool MASKS, bool PADDED>
+hipError_t launch_variant(const FwdArgs& a)
+{
+    const int BH = a.B * a.H;
+    auto go = [&](auto t, auto dd, auto cc) -> hipError_t {
+        typedef typename decltype(t)::type T;
+        constexpr int D = decltype(dd)::value;
+        constexpr bool CAUSAL = decltype(cc)::value;
+        if (a.split)
+            return launch_split<T, D, CAUSAL, MASKS, PADDED>(a.q, a.k, a.v, a.o, a.lse, BH, a.Nq, a.Nk, a.scale,
+                                                             a.n_splits, a.workspace, a.mask, a.d, a.stream);
+        const Shape sh = MASKS ? pick_shape_masked(a.B, a.H, a.Nq, a.d, a.causal)
+                               : pick_shape(a.B, a.H, a.Nq, a.d, a.causal);
+        return launch_shape<T, D, CAUSAL, MASKS, PADDED>(sh, a.q, a.k, a.v, a.o, a.lse, BH, a.Nq, a.Nk, a.scale,
+                                                         a.mask, a.d, a.stream);
+    };
+    auto by_causal = [&](auto t, auto dd) -> hipError_t {
+        return a.causal ? go(t, dd, std::true_type()) : go(t, dd, std::false_type());
+    };
+    auto by_dim = [&](auto t) -> hipError_t {
+        return kernel_dim(a.d) == 64 ? by_causal(t, std::integral_constant<int, 64>())
+                                     : by_causal(t, std::integral_constant<int, 128>());
+    };
+    return a.bf16 ? by_dim(TypeTag<__bf16>()) : by_dim(TypeTag<_Float16>());
 }
 
 }  // namespace

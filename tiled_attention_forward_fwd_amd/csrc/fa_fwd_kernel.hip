@@ -1,5 +1,6 @@
-// fa_fwd_kernel.hip -- host dispatch of the attention forward without masks:
-// workgroup shape, direct and split launches (kernels in fa_fwd_kernel.h).
+// fa_fwd_kernel.hip -- host side of the attention forward: workgroup shape,
+// the choice among the four launch variants, and the variant without masks at
+// head dims 64 and 128 (kernels in fa_fwd_kernel.h).
 
 #include "fa_fwd_kernel.h"
 
@@ -27,47 +28,15 @@ Shape pick_shape(int B, int H, int n_queries, int d, bool causal)
 }
 
 int block_n(int) { return 64; }
-int lds_bytes(int d) { return 4 * 64 * d * 2; }
-
-hipError_t launch_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                            int H, int Nq, int Nk, int d, bool causal, float scale, bool bf16,
-                            int n_splits, float* workspace, hipStream_t stream)
-{
-    const int BH = B * H;
-#define FA_DISPATCH(T, D)                                                                         \
-    return causal ? launch_split<T, D, true, false>(q, k, v, o, lse, BH, Nq, Nk, scale, n_splits,  \
-                                                    workspace, MaskArgs{}, stream)                 \
-                  : launch_split<T, D, false, false>(q, k, v, o, lse, BH, Nq, Nk, scale, n_splits, \
-                                                     workspace, MaskArgs{}, stream)
-    if (bf16) {
-        if (d == 64) FA_DISPATCH(__bf16, 64);
-        FA_DISPATCH(__bf16, 128);
-    }
-    if (d == 64) FA_DISPATCH(_Float16, 64);
-    FA_DISPATCH(_Float16, 128);
-#undef FA_DISPATCH
-}
-
+int lds_bytes(int d) { return 4 * 64 * kernel_dim(d) * 2; }
 int split_rows_per_tile() { return 128; }
 
-hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                      int H, int Nq, int Nk, int d, bool causal, float scale, bool bf16,
-                      hipStream_t stream)
+hipError_t launch_forward(const FwdArgs& a)
 {
-    const int BH = B * H;
-    const Shape sh = pick_shape(B, H, Nq, d, causal);
-#define FA_DISPATCH(T, D)                                                                        \
-    return causal ? launch_shape<T, D, true, false>(sh, q, k, v, o, lse, BH, Nq, Nk, scale,      \
-                                                    MaskArgs{}, stream)                           \
-                  : launch_shape<T, D, false, false>(sh, q, k, v, o, lse, BH, Nq, Nk, scale,     \
-                                                     MaskArgs{}, stream)
-    if (bf16) {
-        if (d == 64) FA_DISPATCH(__bf16, 64);
-        FA_DISPATCH(__bf16, 128);
-    }
-    if (d == 64) FA_DISPATCH(_Float16, 64);
-    FA_DISPATCH(_Float16, 128);
-#undef FA_DISPATCH
+    const bool padded = a.d != 64 && a.d != 128;
+    if (a.masked) return padded ? launch_forward_hdim_masked(a) : launch_forward_masked(a);
+    if (padded) return launch_forward_hdim(a);
+    return launch_variant<false, false>(a);
 }
 
 }  // namespace fa

@@ -1,5 +1,9 @@
 // fa_launch.h -- internal interface between the C ABI (fa_api.hip) and the
-// kernels (fa_fwd_kernel.hip, fa_fwd_masked.hip, fa_bwd_kernel.hip). Not installed; the public header is include/fa.h.
+// kernels. The forward launches are split over four sources by variant
+// (fa_fwd_kernel.hip: no masks, head dim 64 or 128; fa_fwd_masked.hip: masks;
+// fa_fwd_hdim.hip and fa_fwd_hdim_masked.hip: other head dims), all built
+// from the kernel template in fa_fwd_kernel.h; fa_bwd_kernel.hip holds the
+// backward pass. Not installed; the public header is include/fa.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,36 +27,41 @@ struct MaskArgs {
     int heads;            // H: head bh belongs to batch bh / H
 };
 
+// One forward launch, arguments already validated by the caller.
+struct FwdArgs {
+    const void *q, *k, *v;
+    void* o;
+    float* lse;
+    int B, H, Nq, Nk;
+    int d;            // head dim: 64 or 128, or a multiple of 8 below 128 (run padded)
+    bool causal;
+    float scale;
+    bool bf16;
+    bool masked;      // padding / window masks in effect (mask below)
+    MaskArgs mask;
+    bool split;       // split-key launch: n_splits chunks through workspace, then the merge
+    int n_splits;
+    float* workspace; // n_splits * B*H*Nq * (kernel_dim(d) + 1) floats
+    hipStream_t stream;
+};
+
+// The head dim the kernel runs with: 64 or 128.
+inline int kernel_dim(int d) { return d <= 64 ? 64 : 128; }
+
 Shape pick_shape(int B, int H, int n_queries, int d, bool causal);
-// The shape of a masked launch: pick_shape's, except that d = 128 keeps 4 waves.
+// The shape of a masked launch: pick_shape's, except that a kernel head dim
+// of 128 keeps 4 waves.
 Shape pick_shape_masked(int B, int H, int n_queries, int d, bool causal);
 int block_n(int d);
 int lds_bytes(int d);
-
-// Enqueues the forward kernel for Nq query rows against Nk keys per head;
-// arguments were validated by the caller.
-hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                      int H, int Nq, int Nk, int d, bool causal, float scale, bool bf16,
-                      hipStream_t stream);
-
-// Split launch for few query tiles (KV-cache decode): the key tiles of each
-// 128-row query tile are divided into n_splits chunks whose partial results
-// go to `workspace` (n_splits * B*H*Nq * (d + 1) floats) and are then merged
-// into o and lse; arguments were validated by the caller.
-hipError_t launch_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                            int H, int Nq, int Nk, int d, bool causal, float scale, bool bf16,
-                            int n_splits, float* workspace, hipStream_t stream);
 int split_rows_per_tile();
 
-// The same two launches with padding and window masks; rows that see no key
-// get O = 0 and lse = -inf.
-hipError_t launch_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                             int H, int Nq, int Nk, int d, bool causal, const MaskArgs& mask,
-                             float scale, bool bf16, hipStream_t stream);
-hipError_t launch_fwd_split_masked(const void* q, const void* k, const void* v, void* o, float* lse,
-                                   int B, int H, int Nq, int Nk, int d, bool causal,
-                                   const MaskArgs& mask, float scale, bool bf16, int n_splits,
-                                   float* workspace, hipStream_t stream);
+// Enqueues the forward pass (one kernel, or the split kernel and the merge).
+hipError_t launch_forward(const FwdArgs& a);
+// The variants launch_forward picks from, one per source file.
+hipError_t launch_forward_masked(const FwdArgs& a);
+hipError_t launch_forward_hdim(const FwdArgs& a);
+hipError_t launch_forward_hdim_masked(const FwdArgs& a);
 
 // Enqueues the backward pass (delta, dK/dV and dQ kernels); arguments were
 // validated by the caller.
