@@ -343,6 +343,9 @@ def sweep(args):
         # head dims other than 64 and 128 (run by the d = 128 / d = 64 kernels, padded)
         dict(B=4, H=16, N=4096, d=96, dtype="bf16", seed=17, flags=(0, 1)),
         dict(B=4, H=16, N=4096, d=32, dtype="fp16", seed=18, flags=(0, 1)),
+        # fp32 inputs and outputs (split-bf16 products; FLOPs counted as for any dtype)
+        dict(B=4, H=16, N=4096, d=128, dtype="fp32", seed=19, flags=(0, 1)),
+        dict(B=4, H=16, N=4096, d=64, dtype="fp32", seed=20, flags=(0, 1)),
     ] + MASKED_WORKLOADS
     for cfg in configs:
         _, _, _, qd, kd, vd = make_inputs(cfg, dev)

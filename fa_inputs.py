@@ -12,7 +12,8 @@ a profiler", "A small program to profile" and "The sweep"):
 * a CPU ``torch.Generator`` seeded with ``seed``;
 * fp32 standard-normal draws for q, then k, then v, each of shape
   ``[B, H, N, d]`` (contiguous, row-major);
-* each rounded to the storage dtype with ``Tensor.to`` (round to nearest even);
+* each rounded to the storage dtype with ``Tensor.to`` (round to nearest even;
+  fp32 keeps the draws as they are);
 * for the heavy-tailed variant, q is multiplied by ``q_scale`` after rounding.
   A power-of-two ``q_scale`` (4 for the long-context case) is exact in
   fp16/bf16 at these magnitudes.
@@ -20,7 +21,7 @@ a profiler", "A small program to profile" and "The sweep"):
 
 import torch
 
-DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
+DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
 
 
 def as_torch_dtype(dtype):

@@ -172,6 +172,34 @@ int fa_fwd_split_masked(const void *q, const void *k, const void *v, void *o, fl
                         void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * fa_fwd_f32 -- attention forward for fp32 inputs and outputs ("How to
+ * optimise a Triton FlashAttention-2 kernel step by step with a profiler",
+ * Round 1: the test file includes fp32 inputs at D = 128, whose products
+ * that page's kernel forms in a reduced-precision fp32 format).
+ *
+ * Each fp32 value x is split into hi = bf16(x) (round to nearest even) and
+ * lo = bf16(x - hi), and every product of Q K^T and P V is formed on the bf16
+ * matrix cores as hi*hi + hi*lo + lo*hi with fp32 accumulation: about 16
+ * significant bits per product, at a third of the bf16 rate (the fp32 matrix
+ * rate of gfx950 is a sixteenth). Softmax state and accumulation are fp32.
+ *
+ *   q, o      : device, [B, H, Nq, d] fp32, 16-byte aligned (o written).
+ *   k, v      : device, [B, H, Nk, d] fp32, 16-byte aligned.
+ *   lse       : device, [B, H, Nq] fp32 (written, natural log).
+ *   d         : 64 or 128 (others: FA_ERR_UNSUPPORTED); Nk*d*4 < 2^32.
+ *   workspace : device, >= fa_f32_workspace_bytes(B, H, Nk, d) bytes
+ *               (8*B*H*Nk*d: the hi and lo parts of K and V in bf16),
+ *               16-byte aligned, owned by the caller, overlapping no tensor
+ *               argument; contents on entry do not matter.
+ * causal, scale, stream as fa_fwd_qk. Three kernels are enqueued (the split
+ * of K, the split of V, the attention kernel); deterministic.
+ */
+int64_t fa_f32_workspace_bytes(int B, int H, int Nk, int d);
+int fa_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse, int B, int H,
+               int Nq, int Nk, int d, int causal, float scale, void *workspace,
+               int64_t workspace_bytes, void *stream);
+
+/*
  * fa_bwd -- attention backward pass: the gradients of sum(dO * O) with respect
  * to q, k and v, where O = fa_fwd(q, k, v) with the same causal flag and
  * scale. "How to optimise a Triton FlashAttention-2 kernel step by step with

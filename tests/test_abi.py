@@ -384,3 +384,22 @@ def test_plan_other_head_dims(lib, d):
 def test_backward_keeps_head_dims_64_and_128(lib):
     args = [P[0], P[1], P[2], P[3], P[4], 0x60000, 0x70000, 0x80000, 0x90000, 0xa0000]
     assert fa.fa_bwd(*args, 1, 1, 16, 96, 0, 0.1, fa.FA_DTYPE_BF16, None) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_fa_fwd_f32_rejects_before_any_hip_call(lib):
+    ws = 0x200000
+    base = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, Nq=16, Nk=16, d=64, causal=0,
+                scale=0.125, ws=ws, wsb=fa.fa_f32_workspace_bytes(1, 1, 16, 64))
+
+    def run(**kw):
+        a = dict(base)
+        a.update(kw)
+        return fa.fa_fwd_f32(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"],
+                             a["d"], a["causal"], a["scale"], a["ws"], a["wsb"], None)
+    assert fa.fa_f32_workspace_bytes(2, 3, 100, 128) == 8 * 2 * 3 * 100 * 128
+    assert fa.fa_f32_workspace_bytes(1, 1, 16, 96) == 0
+    for kw, st in [(dict(ws=None), fa.FA_ERR_INVALID_ARG), (dict(wsb=base["wsb"] - 1), fa.FA_ERR_INVALID_ARG),
+                   (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(ws=ws + 8), fa.FA_ERR_INVALID_ARG),
+                   (dict(o=P[0]), fa.FA_ERR_INVALID_ARG), (dict(ws=P[2]), fa.FA_ERR_INVALID_ARG),
+                   (dict(scale=0.0), fa.FA_ERR_INVALID_ARG), (dict(Nk=0), fa.FA_ERR_INVALID_ARG)]:
+        assert run(**kw) == st, kw

@@ -26,7 +26,8 @@ FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1
 
 # Entry points declared in include/fa.h.
 EXPORTED = ("fa_fwd", "fa_fwd_qk", "fa_fwd_split_qk", "fa_split_count", "fa_split_workspace_bytes",
-            "fa_fwd_masked", "fa_fwd_split_masked", "fa_bwd", "fa_status_string", "fa_tile_counts",
+            "fa_fwd_masked", "fa_fwd_split_masked", "fa_fwd_f32", "fa_f32_workspace_bytes", "fa_bwd",
+            "fa_status_string", "fa_tile_counts",
             "fa_tile_counts_qk", "fa_tile_counts_masked", "fa_plan", "fa_plan_qk", "fa_plan_masked")
 
 
@@ -82,6 +83,11 @@ def load_library(path=LIB_PATH):
     lib.fa_plan_masked.restype = ctypes.c_int
     lib.fa_plan_masked.argtypes = [ctypes.c_int] * 8 + [ctypes.c_void_p, ctypes.c_int,
                                                         ctypes.POINTER(FaPlan)]
+    lib.fa_fwd_f32.restype = ctypes.c_int
+    lib.fa_fwd_f32.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.fa_f32_workspace_bytes.restype = ctypes.c_int64
+    lib.fa_f32_workspace_bytes.argtypes = [ctypes.c_int] * 4
     lib.fa_split_count.restype = ctypes.c_int
     lib.fa_split_count.argtypes = [ctypes.c_int] * 6
     lib.fa_split_workspace_bytes.restype = ctypes.c_int64
@@ -171,6 +177,16 @@ def fa_plan_masked(B, H, Nq, Nk, d, causal, window_left, window_right, key_lens,
                                          None if arr is None else ctypes.addressof(arr), int(dtype),
                                          ctypes.byref(plan)))
     return plan.as_dict()
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, workspace, workspace_bytes, stream):
+    """Direct call of the C entry point with raw pointers (ints); returns the status."""
+    return load_library().fa_fwd_f32(q, k, v, o, lse, int(B), int(H), int(Nq), int(Nk), int(d),
+                                     int(causal), float(scale), workspace, int(workspace_bytes), stream)
+
+
+def fa_f32_workspace_bytes(B, H, Nk, d):
+    return int(load_library().fa_f32_workspace_bytes(int(B), int(H), int(Nk), int(d)))
 
 
 def fa_split_count(B, H, Nq, Nk, d, causal):
@@ -266,13 +282,48 @@ def default_scale(d):
     return float(np.float32(1.0 / math.sqrt(d)))
 
 
+def _fwd_f32(q, k, v, causal, scale, out, lse, stream, workspace, splits, window_left, window_right,
+             key_lens):
+    import torch
+    if splits not in (None, 1) or key_lens is not None or window_left != -1 or window_right != -1:
+        raise ValueError("float32 inputs take neither key splits nor masks")
+    B, H, N, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = default_scale(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    need = fa_f32_workspace_bytes(B, H, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16) // 2, device=q.device, dtype=torch.bfloat16)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if ws_bytes < need or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor of at least {need} bytes")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        rc = fa_fwd_f32(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+                        N, Nk, d, causal, scale, workspace.data_ptr(), ws_bytes, handle)
+    _check(rc)
+    return out, lse
+
+
 def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None, splits=None,
         workspace=None, window_left=-1, window_right=-1, key_lens=None):
     """Attention forward on the GPU: returns ``(o, lse)``.
 
     q       : CUDA (HIP) tensor ``[B, H, Nq, d]``; k, v: ``[B, H, Nk, d]``;
-              contiguous, float16 or bfloat16, all the same dtype. A causal
-              row i sees keys j <= i.
+              contiguous, float16, bfloat16 or float32, all the same dtype.
+              A causal row i sees keys j <= i. float32 runs ``fa_fwd_f32``
+              (split-bf16 products; no masks or key splits) with a workspace
+              from torch unless ``workspace`` is given.
     scale   : defaults to 1/sqrt(d) in fp32.
     out/lse : optional preallocated outputs (``[B, H, Nq, d]`` dtype and
               ``[B, H, Nq]`` float32).
@@ -300,6 +351,9 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None, spli
         raise ValueError("q, k and v must have the same dtype")
     B, H, N, d = q.shape
     Nk = k.shape[2]
+    if q.dtype == torch.float32:
+        return _fwd_f32(q, k, v, causal, scale, out, lse, stream, workspace, splits, window_left,
+                        window_right, key_lens)
     code = dtype_code(q.dtype)
     if scale is None:
         scale = default_scale(d)

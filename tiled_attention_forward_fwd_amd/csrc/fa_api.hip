@@ -391,6 +391,44 @@ int fa_fwd_split_masked(const void* q, const void* k, const void* v, void* o, fl
     return hip_status(fa::launch_forward(a));
 }
 
+int64_t fa_f32_workspace_bytes(int B, int H, int Nk, int d)
+{
+    if (B < 1 || H < 1 || Nk < 1 || (d != 64 && d != 128)) return 0;
+    return (int64_t)8 * B * H * Nk * d;
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Nq,
+               int Nk, int d, int causal, float scale, void* workspace, int64_t workspace_bytes, void* stream)
+{
+    g_msg[0] = 0;
+    if (!q || !k || !v || !o || !lse || !workspace)
+        return fail(FA_ERR_INVALID_ARG, "NULL tensor or workspace pointer");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(workspace, 16))
+        return fail(FA_ERR_INVALID_ARG, "q, k, v, o and the workspace must be 16-byte aligned");
+    if (!aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    const int rc = check_problem(B, H, Nq, Nk, d, causal, FA_DTYPE_BF16);
+    if (rc != FA_OK) return rc;
+    if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "fp32 inputs take head dim 64 or 128");
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    const int64_t need = fa_f32_workspace_bytes(B, H, Nk, d);
+    if (workspace_bytes < need) return fail(FA_ERR_INVALID_ARG, "workspace too small");
+    if ((int64_t)Nk * d * 4 > (int64_t)UINT32_MAX)
+        return fail(FA_ERR_INVALID_ARG, "one fp32 head (Nk*d*4 bytes) must be below 4 GiB");
+    const size_t qb = (size_t)B * H * Nq * d * 4, kb = (size_t)B * H * Nk * d * 4;
+    const size_t lb = (size_t)B * H * Nq * 4, wb = (size_t)need;
+    if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb))
+        return fail(FA_ERR_INVALID_ARG, "o overlaps q, k or v");
+    if (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) ||
+        overlap(lse, lb, o, qb))
+        return fail(FA_ERR_INVALID_ARG, "lse overlaps q, k, v or o");
+    if (overlap(workspace, wb, q, qb) || overlap(workspace, wb, k, kb) || overlap(workspace, wb, v, kb) ||
+        overlap(workspace, wb, o, qb) || overlap(workspace, wb, lse, lb))
+        return fail(FA_ERR_INVALID_ARG, "the workspace overlaps a tensor argument");
+    return hip_status(fa::launch_fwd_f32(q, k, v, o, lse, B, H, Nq, Nk, d, causal != 0, scale, workspace,
+                                         (hipStream_t)stream));
+}
+
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d,
            int causal, float scale, int dtype, void* stream)

@@ -167,6 +167,39 @@ __device__ __forceinline__ __bf16 to_elem<__bf16>(float x) { return (__bf16)x; }
 template <>
 __device__ __forceinline__ _Float16 to_elem<_Float16>(float x) { return (_Float16)x; }
 
+// The K operand of S^T = K Q^T: key `row` of the tile, the 8 dims of
+// k-step ds that lane half hh holds (one ds_read_b128).
+template <typename V8, int D>
+__device__ __forceinline__ V8 k_operand(const uint16_t* __restrict__ ks, int row, int ds, int hh)
+{
+    return as_vec8<V8>(*(const u32x4*)(ks + row * D + (((2 * ds + hh) ^ swz<D>(row)) * 8)));
+}
+
+// The V^T operand of O^T += V^T P^T for k-step t and dim block db (two
+// transposed reads). Lane l = 16g + i: dim 32*db + (l % 32); elements 0..3
+// are keys 16t + 4h + [0,4), elements 4..7 keys 16t + 8 + 4h + [0,4)
+// (h = g/2), the key order of P^T. Each transposed read has lane i address
+// key (base + i/4), dims 4*(i%4) + [0,4) of the group's 16 dims.
+template <typename V8, int D>
+__device__ __forceinline__ V8 vt_operand(const uint16_t* __restrict__ vts, int t, int db, int lane, int hh)
+{
+    const int gi = lane & 15, g1 = (lane >> 4) & 1;
+    const int half = (gi & 1) * 4;
+    const int key0 = 16 * t + 4 * hh + (gi >> 2);
+    const int key1 = key0 + 8;
+    const int chunk = 4 * db + 2 * g1 + ((gi & 3) >> 1);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(vts + key0 * D + ((chunk ^ swz<D>(key0)) * 8) + half));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(vts + key1 * D + ((chunk ^ swz<D>(key1)) * 8) + half));
+    u32x4 w;
+    w[0] = __builtin_bit_cast(u32x2, lo)[0];
+    w[1] = __builtin_bit_cast(u32x2, lo)[1];
+    w[2] = __builtin_bit_cast(u32x2, hi)[0];
+    w[3] = __builtin_bit_cast(u32x2, hi)[1];
+    return as_vec8<V8>(w);
+}
+
 // S^T = K Q^T for one key tile: s[qb][kb] holds keys 32*kb + (accumulator
 // rows) of this lane's query in block qb. Each K operand read feeds QB MFMAs.
 template <typename T, int D, int QB, int KB, int DS>
@@ -182,10 +215,7 @@ __device__ __forceinline__ void scores(f32x16 (&s)[QB][KB], const uint16_t* __re
     for (int ds = 0; ds < DS; ++ds) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const int row = kb * 32 + l32;
-            const uint16_t* krow = ks + row * D;
-            const int sw = swz<D>(row);
-            vec8 a = as_vec8<vec8>(*(const u32x4*)(krow + (((2 * ds + hh) ^ sw) * 8)));
+            const vec8 a = k_operand<vec8, D>(ks, kb * 32 + l32, ds, hh);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) s[qb][kb] = Mma<T>::run(a, qf[qb][ds], s[qb][kb]);
         }
@@ -212,8 +242,7 @@ __device__ __forceinline__ void scores_with_exp(f32x16 (&sn)[1][KB], const uint1
     for (int ds = 0; ds < DS; ++ds) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const int row = kb * 32 + l32;
-            const vec8 a = as_vec8<vec8>(*(const u32x4*)(ks + row * D + (((2 * ds + hh) ^ swz<D>(row)) * 8)));
+            const vec8 a = k_operand<vec8, D>(ks, kb * 32 + l32, ds, hh);
             sn[0][kb] = Mma<T>::run(a, qf[0][ds], sn[0][kb]);
             const int i = ds * KB + kb;
 #pragma unroll
@@ -342,37 +371,19 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[QB][KB], f32x16 (
     softmax_finish<T, QB, KB, DB, KT>(s, o, m_run, l_run, c_log2, p, rs);
 }
 
-// O^T += V^T P^T. V^T operand, lane l = 16g + i: dim 32*db + (l % 32);
-// elements 0..3 are keys 16t + 4h + [0,4), elements 4..7 keys
-// 16t + 8 + 4h + [0,4) (h = g/2), the key order of P^T. Each of the two
-// transposed reads has lane i address key (base + i/4), dims 4*(i%4) + [0,4)
-// of the group's 16 dims. Each V operand feeds QB MFMAs; the t-major order
-// consumes P in the order it is produced.
+// O^T += V^T P^T (operand layout at vt_operand). Each V operand feeds QB
+// MFMAs; the t-major order consumes P in the order it is produced.
 template <typename T, int D, int QB, int DB, int KT>
 __device__ __forceinline__ void pv_tile(const typename Mma<T>::vec8 (&p)[QB][KT],
                                         const uint16_t* __restrict__ vts, f32x16 (&o)[QB][DB], int lane,
                                         int hh)
 {
     typedef typename Mma<T>::vec8 vec8;
-    const int gi = lane & 15, g1 = (lane >> 4) & 1;
-    const int half = (gi & 1) * 4;
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-        const int key0 = 16 * t + 4 * hh + (gi >> 2);
-        const int key1 = key0 + 8;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const int chunk = 4 * db + 2 * g1 + ((gi & 3) >> 1);
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(vts + key0 * D + ((chunk ^ swz<D>(key0)) * 8) + half));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(vts + key1 * D + ((chunk ^ swz<D>(key1)) * 8) + half));
-            u32x4 w;
-            w[0] = __builtin_bit_cast(u32x2, lo)[0];
-            w[1] = __builtin_bit_cast(u32x2, lo)[1];
-            w[2] = __builtin_bit_cast(u32x2, hi)[0];
-            w[3] = __builtin_bit_cast(u32x2, hi)[1];
-            const vec8 a = as_vec8<vec8>(w);
+            const vec8 a = vt_operand<vec8, D>(vts, t, db, lane, hh);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) o[qb][db] = Mma<T>::run(a, p[qb][t], o[qb][db]);
         }

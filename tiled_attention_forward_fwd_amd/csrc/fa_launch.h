@@ -63,6 +63,11 @@ hipError_t launch_forward_masked(const FwdArgs& a);
 hipError_t launch_forward_hdim(const FwdArgs& a);
 hipError_t launch_forward_hdim_masked(const FwdArgs& a);
 
+// fp32 inputs and outputs (d = 64 or 128): splits K and V into bf16 hi/lo
+// parts in `workspace` (4 * B*H*Nk*d bf16 values), then one kernel.
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
+                          int Nq, int Nk, int d, bool causal, float scale, void* workspace, hipStream_t stream);
+
 // Enqueues the backward pass (delta, dK/dV and dQ kernels); arguments were
 // validated by the caller.
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
