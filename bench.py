@@ -23,6 +23,7 @@ Other modes (used to collect counters; each runs a few launches only):
     --copy-calibration  a plain device-to-device copy of a known size
     --profile-decode    the split-key decode path (one query x 16384 keys, B=1 H=32)
     --profile-masked    the padding and sliding-window workloads of the sweep
+    --profile-variants  head dims 96 and 32 and fp32 inputs at the headline shape
     --sweep             medians of 50 for every configuration of the workload
                         list, with peak memory (one extra JSON object); the
                         masked rows count exactly the visible (query, key)
@@ -406,15 +407,23 @@ MASKED_WORKLOADS = [
 ]
 
 
-def profile_masked(args):
-    """Each masked workload (MASKED_WORKLOADS, in order, each causal flag): untimed calls for at
-    least half a second (the clock ramps up under load), then `steps` calls; the JSON line lists
-    the (untimed, counted) call numbers in launch order."""
+# Head dims other than 64 / 128 and fp32 inputs (--profile-variants).
+VARIANT_WORKLOADS = [
+    dict(B=4, H=16, N=4096, d=96, dtype="bf16", seed=17, flags=(0, 1)),
+    dict(B=4, H=16, N=4096, d=32, dtype="fp16", seed=18, flags=(0, 1)),
+    dict(B=4, H=16, N=4096, d=128, dtype="fp32", seed=19, flags=(0, 1)),
+]
+
+
+def profile_workloads(args, workloads, label):
+    """Each workload (in order, each causal flag): untimed calls for at least half a second (the
+    clock ramps up under load), then `steps` calls; the JSON line lists the (untimed, counted)
+    call numbers in launch order."""
     import torch
     import tiled_attention_forward_fwd_amd as fa
     dev = torch.device("cuda:0")
     calls = []
-    for cfg in MASKED_WORKLOADS:
+    for cfg in workloads:
         _, _, _, qd, kd, vd = make_inputs(cfg, dev)
         Nq = cfg.get("Nq", cfg["N"])
         qd = qd[:, :, :Nq].contiguous()
@@ -435,7 +444,7 @@ def profile_masked(args):
             torch.cuda.synchronize()
             calls.append([n_warm, args.steps])
         del qd, kd, vd
-    print(json.dumps({"profiled": "masked workloads", "workloads": MASKED_WORKLOADS, "calls": calls}))
+    print(json.dumps({"profiled": label, "workloads": workloads, "calls": calls}))
 
 
 def profile_kernels(args):
@@ -525,6 +534,8 @@ def main():
                     help="split-key decode calls only (one query x 16384 keys), for rocprofv3")
     ap.add_argument("--profile-masked", action="store_true",
                     help="padding and sliding-window workloads only, for rocprofv3")
+    ap.add_argument("--profile-variants", action="store_true",
+                    help="head dims 96 / 32 and fp32 inputs at B4 H16 N4096, for rocprofv3")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -547,7 +558,9 @@ def main():
     if args.profile_decode:
         return profile_decode(args)
     if args.profile_masked:
-        return profile_masked(args)
+        return profile_workloads(args, MASKED_WORKLOADS, "masked workloads")
+    if args.profile_variants:
+        return profile_workloads(args, VARIANT_WORKLOADS, "head-dim and fp32 workloads")
 
     out, (q, k, v) = headline(args)
     if args.backward:
