@@ -227,6 +227,18 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
            int causal, float scale, int dtype, void *stream);
 
 /*
+ * fa_bwd_qk -- the backward pass for Nq query rows against Nk keys per head
+ * (the gradients of fa_fwd_qk, same causal rule: key j is visible to row i
+ * iff j <= i). q, o, dout, dq are [B, H, Nq, d]; lse and delta [B, H, Nq];
+ * k, v, dk, dv [B, H, Nk, d]. Keys no row sees get dK = dV = 0. Other
+ * arguments as fa_bwd, which is fa_bwd_qk with Nq = Nk = N. No output
+ * (dq, dk, dv, delta) may overlap another output or an input.
+ */
+int fa_bwd_qk(const void *q, const void *k, const void *v, const void *o, const void *dout,
+              const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H, int Nq,
+              int Nk, int d, int causal, float scale, int dtype, void *stream);
+
+/*
  * fa_status_string -- human-readable text for a status code. For FA_ERR_HIP
  * and FA_ERR_INVALID_ARG it names the HIP error or the failed check of the
  * last failing call on the calling thread. The returned pointer stays valid

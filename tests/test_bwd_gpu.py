@@ -30,8 +30,10 @@ def grads_gpu(q, k, v, dout, causal):
     return dq.cpu(), dk.cpu(), dv.cpu()
 
 
-def check_bwd(B, H, N, d, dtype, causal, seed):
+def check_bwd(B, H, N, d, dtype, causal, seed, Nk=None):
     q, k, v = make_qkv(B, H, N, d, dtype, seed)
+    if Nk is not None:  # fewer or more keys than queries
+        _, k, v = make_qkv(B, H, Nk, d, dtype, seed + 3)
     dout = make_qkv(B, H, N, d, dtype, seed + 7)[0]
     scale = fa.default_scale(d)
     g = grads_gpu(q, k, v, dout, causal)
@@ -44,10 +46,11 @@ def check_bwd(B, H, N, d, dtype, causal, seed):
         # (dQ and dK of a single key) checked absolutely
         err = float(np.abs(a - b).max() / max(float(np.abs(b).max()), 1e-3))
         errs.append(err)
-    print(f"[bwd] B{B} H{H} N{N} d{d} {dtype} causal={causal} rel err dq={errs[0]:.2e} "
+    print(f"[bwd] B{B} H{H} N{N} Nk{Nk or N} d{d} {dtype} causal={causal} rel err dq={errs[0]:.2e} "
           f"dk={errs[1]:.2e} dv={errs[2]:.2e}", flush=True)
     tol = TOL[q.dtype]
     assert max(errs) <= tol, f"gradient error {max(errs):.3e} > {tol}"
+    return g
 
 
 CASES = [(1, 2, 128, 64, "fp16"), (1, 2, 128, 128, "bf16"), (2, 3, 300, 128, "bf16"),
@@ -90,3 +93,19 @@ def test_backward_headline_shape_two_heads():
                 err = float(np.abs(a - r).max() / max(float(np.abs(r).max()), 1e-3))
                 print(f"[bwd] headline head ({b},{h}) causal={causal} {name} rel err {err:.2e}", flush=True)
                 assert err <= TOL[torch.bfloat16]
+
+
+# (B, H, Nq, Nk, d, dtype): cross-attention shapes, ragged both ways, a key
+# block wholly past every causal row, and a single query
+QK_CASES = [(2, 2, 300, 1000, 128, "bf16"), (2, 2, 1000, 300, 64, "fp16"), (1, 3, 129, 700, 64, "bf16"),
+            (1, 2, 700, 129, 128, "fp16"), (1, 2, 1, 513, 128, "bf16"), (1, 1, 64, 1024, 64, "fp16")]
+
+
+@pytest.mark.parametrize("case", QK_CASES, ids=[f"B{c[0]}H{c[1]}q{c[2]}k{c[3]}d{c[4]}{c[5]}" for c in QK_CASES])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_query_and_key_lengths(case, causal):
+    B, H, Nq, Nk, d, dtype = case
+    print(f"[case] bwd {case} causal={causal}", flush=True)
+    dq, dk, dv = check_bwd(B, H, Nq, d, dtype, causal, 540 + Nq % 50, Nk=Nk)
+    if causal and Nq < Nk:  # keys past the last query row are seen by no row
+        assert torch.all(dk[:, :, Nq:] == 0) and torch.all(dv[:, :, Nq:] == 0)

@@ -26,7 +26,7 @@ FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1
 
 # Entry points declared in include/fa.h.
 EXPORTED = ("fa_fwd", "fa_fwd_qk", "fa_fwd_split_qk", "fa_split_count", "fa_split_workspace_bytes",
-            "fa_fwd_masked", "fa_fwd_split_masked", "fa_fwd_f32", "fa_f32_workspace_bytes", "fa_bwd",
+            "fa_fwd_masked", "fa_fwd_split_masked", "fa_fwd_f32", "fa_f32_workspace_bytes", "fa_bwd", "fa_bwd_qk",
             "fa_status_string", "fa_tile_counts",
             "fa_tile_counts_qk", "fa_tile_counts_masked", "fa_plan", "fa_plan_qk", "fa_plan_masked")
 
@@ -94,6 +94,9 @@ def load_library(path=LIB_PATH):
     lib.fa_split_workspace_bytes.argtypes = [ctypes.c_int] * 5
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_bwd_qk.restype = ctypes.c_int
+    lib.fa_bwd_qk.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [ctypes.c_int]
@@ -203,37 +206,48 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, causal, scale, 
                                  int(d), int(causal), float(scale), int(dtype), stream)
 
 
+def fa_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d, causal, scale, dtype, stream):
+    """Direct call of the C entry point with raw pointers (ints); returns the status."""
+    return load_library().fa_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, delta, int(B), int(H), int(Nq),
+                                    int(Nk), int(d), int(causal), float(scale), int(dtype), stream)
+
+
 def bwd(q, k, v, o, lse, dout, causal=False, scale=None, stream=None):
     """Attention backward on the GPU: returns ``(dq, dk, dv)``.
 
-    q, k, v, o, dout : CUDA (HIP) tensors ``[B, H, N, d]``, contiguous, one of
-                       float16/bfloat16; ``o`` and ``lse`` (``[B, H, N]``
-                       float32) from ``fwd`` with the same causal flag and
-                       scale. The D = rowsum(dO * O) scratch is allocated with
-                       torch.
+    q, o, dout : CUDA (HIP) tensors ``[B, H, Nq, d]``; k, v ``[B, H, Nk, d]``;
+                 contiguous, one of float16/bfloat16; ``o`` and ``lse``
+                 (``[B, H, Nq]`` float32) from ``fwd`` with the same causal
+                 flag and scale. The D = rowsum(dO * O) scratch is allocated
+                 with torch.
     """
     import torch
     ts = (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout))
     for name, t in ts:
         if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
             raise ValueError(f"{name} must be a contiguous [B, H, N, d] GPU tensor")
-        if t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError(f"{name} must match q in shape and dtype")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in dtype")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must match q in shape")
+    if k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3] or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
     code = dtype_code(q.dtype)
     if scale is None:
         scale = default_scale(d)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     with torch.cuda.device(q.device):
-        rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-                    B, H, N, d, causal, scale, code, handle)
+        rc = fa_bwd_qk(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                       B, H, N, Nk, d, causal, scale, code, handle)
     _check(rc)
     return dq, dk, dv
 

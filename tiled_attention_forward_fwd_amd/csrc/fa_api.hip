@@ -429,9 +429,9 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                                          (hipStream_t)stream));
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-           const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d,
-           int causal, float scale, int dtype, void* stream)
+int fa_bwd_qk(const void* q, const void* k, const void* v, const void* o, const void* dout,
+              const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int Nq, int Nk,
+              int d, int causal, float scale, int dtype, void* stream)
 {
     g_msg[0] = 0;
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta)
@@ -440,32 +440,37 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     for (const void* p : a16)
         if (!aligned(p, 16)) return fail(FA_ERR_INVALID_ARG, "tensors and delta must be 16-byte aligned");
     if (!aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-    const int rc = check_problem(B, H, N, N, d, causal, dtype);
+    const int rc = check_problem(B, H, Nq, Nk, d, causal, dtype);
     if (rc != FA_OK) return rc;
     if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "the backward pass takes head dim 64 or 128");
     if (!(scale > 0.f) || !isfinite(scale))
         return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
-    const size_t tb = (size_t)B * H * N * d * 2, lb = (size_t)B * H * N * 4;
-    const void* outs[] = {dq, dk, dv};
-    const void* ins[] = {q, k, v, o, dout};
-    for (const void* w : outs) {
-        for (const void* r : ins)
-            if (overlap(w, tb, r, tb)) return fail(FA_ERR_INVALID_ARG, "a gradient overlaps an input");
-        if (overlap(w, tb, lse, lb) || overlap(w, tb, delta, lb))
-            return fail(FA_ERR_INVALID_ARG, "a gradient overlaps lse or delta");
-    }
-    if (overlap(dq, tb, dk, tb) || overlap(dq, tb, dv, tb) || overlap(dk, tb, dv, tb))
-        return fail(FA_ERR_INVALID_ARG, "dq, dk and dv overlap");
-    for (const void* r : ins)
-        if (overlap(delta, lb, r, tb)) return fail(FA_ERR_INVALID_ARG, "delta overlaps an input");
-    if (overlap(delta, lb, lse, lb)) return fail(FA_ERR_INVALID_ARG, "delta overlaps lse");
-    const hipError_t e = fa::launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d,
-                                        causal != 0, scale, dtype == FA_DTYPE_BF16, (hipStream_t)stream);
-    if (e != hipSuccess) {
-        snprintf(g_msg, sizeof g_msg, "HIP error %d: %s", (int)e, hipGetErrorString(e));
-        return FA_ERR_HIP;
-    }
-    return FA_OK;
+    // query side: q, o, dout, dq [Nq rows], lse and delta [Nq]; key side: k, v, dk, dv [Nk rows]
+    const size_t qb = (size_t)B * H * Nq * d * 2, kb = (size_t)B * H * Nk * d * 2;
+    const size_t lb = (size_t)B * H * Nq * 4;
+    struct Buf {
+        const void* p;
+        size_t n;
+    };
+    const Buf ins[] = {{q, qb}, {k, kb}, {v, kb}, {o, qb}, {dout, qb}, {lse, lb}};
+    const Buf outs[] = {{dq, qb}, {dk, kb}, {dv, kb}, {delta, lb}};
+    for (const Buf& w : outs)
+        for (const Buf& r : ins)
+            if (overlap(w.p, w.n, r.p, r.n))
+                return fail(FA_ERR_INVALID_ARG, "an output (dq, dk, dv or delta) overlaps an input");
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+                return fail(FA_ERR_INVALID_ARG, "dq, dk, dv and delta overlap");
+    return hip_status(fa::launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d, causal != 0,
+                                     scale, dtype == FA_DTYPE_BF16, (hipStream_t)stream));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d,
+           int causal, float scale, int dtype, void* stream)
+{
+    return fa_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, N, d, causal, scale, dtype, stream);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,

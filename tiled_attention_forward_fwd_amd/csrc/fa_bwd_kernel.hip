@@ -29,6 +29,9 @@
 //     keys and masks only the diagonal tiles; the dQ kernel visits the
 //     forward's key-tile range (Round 4, "Causal tile-skipping"). Waves skip
 //     query or key blocks that lie wholly above the diagonal for their rows.
+//   * N_q query rows against N_k keys, with the forward's top-left causal
+//     rule (key j visible to row i iff j <= i): query-side tensors (q, dO, O,
+//     L, D, dQ) have N_q rows per head, key-side ones (K, V, dK, dV) N_k.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -117,8 +120,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kBwdWaves, 64 * kBwdW
                           amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                         const T* __restrict__ dout, const float* __restrict__ lse,
-                        const float* __restrict__ delta, T* __restrict__ dk, T* __restrict__ dv, int N,
-                        int n_kt, float scale, float c_log2)
+                        const float* __restrict__ delta, T* __restrict__ dk, T* __restrict__ dv, int Nq,
+                        int Nk, int n_kt, float scale, float c_log2)
 {
     typedef Cfg<D, kBwdWaves, 1> C;  // 64-row copies by the whole workgroup, as the forward's tiles
     typedef typename Mma<T>::vec8 vec8;
@@ -136,25 +139,25 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
-    const int64_t off = (int64_t)bh * N * D;
+    const int64_t q_off = (int64_t)bh * Nq * D, kv_off = (int64_t)bh * Nk * D;
     const int kw0 = k0 + 32 * wave;  // this wave's first key
 
-    // K rows of this wave's keys in B-operand layout (rows >= N zero); V rows
+    // K rows of this wave's keys in B-operand layout (rows >= Nk zero); V rows
     // go to LDS once and are read per MFMA (registers hold two waves per SIMD)
     int krow[1];
     vec8 kf[1][C::DS];
-    load_q<T, D, 1, C::DS>(k + off, kw0, N, l32, hh, krow, kf);
+    load_q<T, D, 1, C::DS>(k + kv_off, kw0, Nk, l32, hh, krow, kf);
 
     f32x16 dk_acc[1][C::DB], dv_acc[1][C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) dk_acc[0][db] = dv_acc[0][db] = (f32x16){};
 
-    const uint32_t head_bytes = (uint32_t)N * (D * 2), row_bytes = (uint32_t)N * 4;
-    const rsrc_t qrs = head_rsrc(q + off, head_bytes), drs = head_rsrc(dout + off, head_bytes);
-    const rsrc_t lrs = head_rsrc(lse + (int64_t)bh * N, row_bytes);
-    const rsrc_t ers = head_rsrc(delta + (int64_t)bh * N, row_bytes);
+    const uint32_t q_bytes = (uint32_t)Nq * (D * 2), row_bytes = (uint32_t)Nq * 4;
+    const rsrc_t qrs = head_rsrc(q + q_off, q_bytes), drs = head_rsrc(dout + q_off, q_bytes);
+    const rsrc_t lrs = head_rsrc(lse + (int64_t)bh * Nq, row_bytes);
+    const rsrc_t ers = head_rsrc(delta + (int64_t)bh * Nq, row_bytes);
     const uint32_t lane_off = tile_lane_offset<D>(wave, lane);
-    const rsrc_t vrs = head_rsrc(v + off, head_bytes);
+    const rsrc_t vrs = head_rsrc(v + kv_off, (uint32_t)Nk * (D * 2));
 #pragma unroll
     for (int i = 0; i < kBwdKeys / kBwdRows; ++i)
         issue_tile<D, kBwdWaves, 1>(vtile + i * TILE, vrs, k0 + i * kBwdRows, wave, lane_off);
@@ -171,9 +174,11 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
         }
     };
 
-    const int n_qt = (N + kBwdRows - 1) / kBwdRows;
-    const int t_begin = CAUSAL ? k0 / kBwdRows : 0;  // no earlier query row sees these keys
-    issue(t_begin);
+    const int n_qt = (Nq + kBwdRows - 1) / kBwdRows;
+    // no earlier query row sees these keys; with fewer queries than keys a
+    // causal key block can lie past every row (its gradients are zero)
+    const int t_begin = CAUSAL ? k0 / kBwdRows : 0;
+    if (t_begin < n_qt) issue(t_begin);
     stage_barrier();
     for (int t = t_begin; t < n_qt; ++t) {
         if (t + 1 < n_qt) issue(t + 1);
@@ -226,8 +231,8 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
         }
         stage_barrier();
     }
-    store_rows<T, D, C::DB>(dk_acc[0], scale, kw0 + l32, N, dk + off, hh);
-    store_rows<T, D, C::DB>(dv_acc[0], 1.0f, kw0 + l32, N, dv + off, hh);
+    store_rows<T, D, C::DB>(dk_acc[0], scale, kw0 + l32, Nk, dk + kv_off, hh);
+    store_rows<T, D, C::DB>(dv_acc[0], 1.0f, kw0 + l32, Nk, dv + kv_off, hh);
 }
 
 // ---------------------------------------------------------------- dQ
@@ -235,8 +240,8 @@ template <typename T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                       const T* __restrict__ dout, const float* __restrict__ lse,
-                      const float* __restrict__ delta, T* __restrict__ dq, int N, int n_qt, float scale,
-                      float c_log2)
+                      const float* __restrict__ delta, T* __restrict__ dq, int Nq, int Nk, int n_qt,
+                      float scale, float c_log2)
 {
     typedef Cfg<D, 4, 1> C;  // 128 query rows, 64-key tiles
     typedef typename Mma<T>::vec8 vec8;
@@ -248,28 +253,28 @@ void fa_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
-    const int64_t off = (int64_t)bh * N * D;
+    const int64_t q_off = (int64_t)bh * Nq * D, kv_off = (int64_t)bh * Nk * D;
 
     int qrow[1];
     vec8 qf[1][C::DS], df[1][C::DS];
-    load_q<T, D, 1, C::DS>(q + off, q0 + wave * 32, N, l32, hh, qrow, qf);
-    load_q<T, D, 1, C::DS>(dout + off, q0 + wave * 32, N, l32, hh, qrow, df);
-    const bool row_ok = qrow[0] < N;
-    const float l2 = row_ok ? lse[(int64_t)bh * N + qrow[0]] * kLog2e : 0.f;
-    const float dd = row_ok ? delta[(int64_t)bh * N + qrow[0]] : 0.f;
+    load_q<T, D, 1, C::DS>(q + q_off, q0 + wave * 32, Nq, l32, hh, qrow, qf);
+    load_q<T, D, 1, C::DS>(dout + q_off, q0 + wave * 32, Nq, l32, hh, qrow, df);
+    const bool row_ok = qrow[0] < Nq;
+    const float l2 = row_ok ? lse[(int64_t)bh * Nq + qrow[0]] * kLog2e : 0.f;
+    const float dd = row_ok ? delta[(int64_t)bh * Nq + qrow[0]] : 0.f;
 
     f32x16 dq_acc[1][C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) dq_acc[0][db] = (f32x16){};
 
-    const TileSpan span = tile_span(q0, C::BM, C::BN, N, N, CAUSAL);
+    const TileSpan span = tile_span(q0, C::BM, C::BN, Nq, Nk, CAUSAL);
     const int n_unmasked = (int)span.unmasked, n_tiles = (int)span.total;
     const int n_wave = CAUSAL ? min(n_tiles, (q0 + (wave + 1) * 32 - 1) / C::BN + 1) : n_tiles;
 
     auto kbuf = [&](int i) { return smem + (i & 1) * C::TILE; };
     auto vbuf = [&](int i) { return smem + (2 + (i & 1)) * C::TILE; };
-    const uint32_t head_bytes = (uint32_t)N * (D * 2);
-    const rsrc_t krs = head_rsrc(k + off, head_bytes), vrs = head_rsrc(v + off, head_bytes);
+    const uint32_t head_bytes = (uint32_t)Nk * (D * 2);
+    const rsrc_t krs = head_rsrc(k + kv_off, head_bytes), vrs = head_rsrc(v + kv_off, head_bytes);
     const uint32_t lane_off = tile_lane_offset<D>(wave, lane);
     issue_tile<D, 4, 1>(kbuf(0), krs, 0, wave, lane_off);
     issue_tile<D, 4, 1>(vbuf(0), vrs, 0, wave, lane_off);
@@ -283,7 +288,7 @@ void fa_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
             f32x16 s[1][C::KB], dp[1][C::KB];
             scores<T, D, 1, C::KB, C::DS>(s, kbuf(j), qf, l32, hh);
             scores<T, D, 1, C::KB, C::DS>(dp, vbuf(j), df, l32, hh);
-            if (j >= n_unmasked) mask_scores<C::KB, CAUSAL>(s[0], j * C::BN, qrow[0], N, hh);
+            if (j >= n_unmasked) mask_scores<C::KB, CAUSAL>(s[0], j * C::BN, qrow[0], Nk, hh);
             vec8 dsk[1][C::KT];
 #pragma unroll
             for (int kb = 0; kb < C::KB; ++kb) {
@@ -297,32 +302,32 @@ void fa_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
         }
         stage_barrier();
     }
-    store_rows<T, D, C::DB>(dq_acc[0], scale, qrow[0], N, dq + off, hh);
+    store_rows<T, D, C::DB>(dq_acc[0], scale, qrow[0], Nq, dq + q_off, hh);
 }
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_bwd_typed(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                            const float* lse, void* dq, void* dk, void* dv, float* delta, int BH, int N,
-                            float scale, hipStream_t stream)
+                            const float* lse, void* dq, void* dk, void* dv, float* delta, int BH, int Nq,
+                            int Nk, float scale, hipStream_t stream)
 {
-    const int64_t n_rows = (int64_t)BH * N;
+    const int64_t n_rows = (int64_t)BH * Nq;
     const float c_log2 = scale * kLog2e;
     dim3 g0((unsigned)((n_rows * (D / 8) + 255) / 256)), b0(256);
     hipLaunchKernelGGL((fa_bwd_delta_kernel<T, D>), g0, b0, 0, stream, (const T*)o, (const T*)dout, delta,
                        n_rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int n_kt = (N + kBwdKeys - 1) / kBwdKeys;
+    const int n_kt = (Nk + kBwdKeys - 1) / kBwdKeys;
     dim3 g1((unsigned)((int64_t)n_kt * BH)), b1(64 * kBwdWaves);
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, CAUSAL>), g1, b1, 0, stream, (const T*)q, (const T*)k,
-                       (const T*)v, (const T*)dout, lse, (const float*)delta, (T*)dk, (T*)dv, N, n_kt, scale,
-                       c_log2);
+                       (const T*)v, (const T*)dout, lse, (const float*)delta, (T*)dk, (T*)dv, Nq, Nk, n_kt,
+                       scale, c_log2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int n_qt = (N + 127) / 128;
+    const int n_qt = (Nq + 127) / 128;
     dim3 g2((unsigned)((int64_t)n_qt * BH)), b2(256);
     hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, CAUSAL>), g2, b2, 0, stream, (const T*)q, (const T*)k,
-                       (const T*)v, (const T*)dout, lse, (const float*)delta, (T*)dq, N, n_qt, scale,
+                       (const T*)v, (const T*)dout, lse, (const float*)delta, (T*)dq, Nq, Nk, n_qt, scale,
                        c_log2);
     return hipGetLastError();
 }
@@ -330,15 +335,15 @@ hipError_t launch_bwd_typed(const void* q, const void* k, const void* v, const v
 }  // namespace
 
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                      const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
-                      int d, bool causal, float scale, bool bf16, hipStream_t stream)
+                      const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int Nq,
+                      int Nk, int d, bool causal, float scale, bool bf16, hipStream_t stream)
 {
     const int BH = B * H;
-#define FA_BWD(T, D)                                                                                    \
-    return causal ? launch_bwd_typed<T, D, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, BH, N, scale, \
-                                                 stream)                                                \
-                  : launch_bwd_typed<T, D, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, BH, N, scale, \
-                                                  stream)
+#define FA_BWD(T, D)                                                                                   \
+    return causal ? launch_bwd_typed<T, D, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, BH, Nq, Nk, \
+                                                 scale, stream)                                        \
+                  : launch_bwd_typed<T, D, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, BH, Nq, Nk, \
+                                                  scale, stream)
     if (bf16) {
         if (d == 64) FA_BWD(__bf16, 64);
         FA_BWD(__bf16, 128);
