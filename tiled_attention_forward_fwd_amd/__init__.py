@@ -1,17 +1,20 @@
-"""Python binding of libfa, the gfx950 attention-forward library.
+"""Python binding of libfa, the gfx950 attention library (forward and backward).
 
-Argument marshalling only: every step of the forward pass runs in the HIP
-kernels of ``libfa.so``. PyTorch provides device memory and the stream.
-There is no fallback: if the library is missing or fails to load, the
-functions here raise.
+Argument marshalling only: every step of the forward and backward passes runs
+in the HIP kernels of ``libfa.so``. PyTorch provides device memory, the
+stream and the workspaces some entry points take. There is no fallback: if
+the library is missing or fails to load, the functions here raise.
 
     o, lse = fwd(q, k, v, causal=False, scale=None)
+    dq, dk, dv = bwd(q, k, v, o, lse, dout, causal=False, scale=None)
 
 q is ``[B, H, Nq, d]`` and k, v are ``[B, H, Nk, d]``; Nq may differ from Nk
-(a causal row i sees keys j <= i). ``fwd`` also takes padding lengths and
-sliding windows (``key_lens``, ``window_left``, ``window_right``). The C
-entry points are exposed under their own names (those in ``EXPORTED``) for
-callers that manage their own buffers.
+(a causal row i sees keys j <= i). d is any multiple of 8 up to 128 (the
+backward: 64 or 128); float16, bfloat16, or float32 (forward only). ``fwd``
+also takes padding lengths and sliding windows (``key_lens``,
+``window_left``, ``window_right``) and picks the split-key launch for small
+grids (``splits``). The C entry points are exposed under their own names
+(those in ``EXPORTED``) for callers that manage their own buffers.
 """
 
 import ctypes

@@ -1,7 +1,11 @@
 // fa_fwd_kernel.h -- the attention forward kernel (FlashAttention-2 form) for
-// gfx950, its epilogues, the merge of a split launch and the launch templates;
-// instantiated by fa_fwd_kernel.hip (no masks) and fa_fwd_masked.hip (padding
-// and sliding-window masks).
+// gfx950, its epilogues, the merge of a split launch and the launch templates.
+// One template covers every variant, chosen at compile time: SPLIT (the key
+// tiles of a query tile divided over several workgroups, for decode), MASKS
+// (padding lengths and sliding windows) and PADDED (head dims other than 64
+// and 128, run with the missing dims held at zero). fa_fwd_kernel.hip,
+// fa_fwd_masked.hip, fa_fwd_hdim.hip and fa_fwd_hdim_masked.hip instantiate
+// the four MASKS x PADDED combinations, each with and without SPLIT.
 //
 // Method: "How to optimise a Triton FlashAttention-2 kernel step by step with
 // a profiler" ("Where the last article left off", Round 1, Round 4): one
@@ -12,10 +16,11 @@
 // written once.
 //
 // gfx950 mapping (our design, not the pages'):
-//   * A workgroup is WAVES waves; each wave owns QB blocks of 32 whole query
-//     rows, so row reductions never leave the wave (the pages' rule that every
-//     warp must own whole rows, Round 0 / Round 1). With QB = 2 every K and V
-//     operand read from LDS feeds two MFMAs.
+//   * A workgroup is WAVES waves (4 or 8); each wave owns QB blocks of 32 whole
+//     query rows, so row reductions never leave the wave (the pages' rule that
+//     every warp must own whole rows, Round 0 / Round 1). The launches use
+//     QB = 1, which keeps two waves per SIMD; the template's QB = 2 (each K and
+//     V operand read feeding two MFMAs) needs more registers than that allows.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_{bf16,f16}: keys on the M axis, queries on N. In the
 //     32x32 accumulator each lane holds 16 keys of ONE query, and the other 16
