@@ -222,6 +222,23 @@ __device__ __forceinline__ void scores(f32x16 (&s)[QB][KB], const uint16_t* __re
     }
 }
 
+// Row-sum update with two exponentials of a row. bf16: the fp32 values, in
+// order. fp16: one v_dot2_f32_f16 of the rounded pair (the values the P.V
+// product uses); fp16 rounding changes each term by at most 2^-11 of itself,
+// so l and the logsumexp move by at most 2^-11 relative / 4.9e-4 absolute.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+template <typename T>
+__device__ __forceinline__ float pair_sum(float acc, float x0, float x1, T, T)
+{
+    return (acc + x0) + x1;
+}
+template <>
+__device__ __forceinline__ float pair_sum<_Float16>(float acc, float, float, _Float16 h0, _Float16 h1)
+{
+    const f16x2 v = {h0, h1}, one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(v, one, acc, false);
+}
+
 // The scores of the next tile fused with the exp2 work of this one: after
 // each score MFMA come the exp2 / row-sum / convert of a few elements of the
 // current tile, so the vector units work while the matrix core runs instead
@@ -246,11 +263,14 @@ __device__ __forceinline__ void scores_with_exp(f32x16 (&sn)[1][KB], const uint1
             sn[0][kb] = Mma<T>::run(a, qf[0][ds], sn[0][kb]);
             const int i = ds * KB + kb;
 #pragma unroll
-            for (int e = i * per; e < (i + 1) * per; ++e) {
-                const int eb = e >> 4, r = e & 15;
-                const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][eb][r], c_log2, -m));
-                acc += x;
-                p[0][eb * 2 + (r >> 3)][r & 7] = to_elem<T>(x);
+            for (int e = i * per; e < (i + 1) * per; e += 2) {
+                const int eb = e >> 4, r = e & 15;  // r even: r and r + 1 share a P vector
+                const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][eb][r], c_log2, -m));
+                const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][eb][r + 1], c_log2, -m));
+                const T h0 = to_elem<T>(x0), h1 = to_elem<T>(x1);
+                p[0][eb * 2 + (r >> 3)][r & 7] = h0;
+                p[0][eb * 2 + (r >> 3)][(r & 7) + 1] = h1;
+                acc = pair_sum<T>(acc, x0, x1, h0, h1);
             }
         }
     }
@@ -312,10 +332,13 @@ __device__ __forceinline__ void exp_tile(const f32x16 (&s)[QB][KB], const float 
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r], c_log2, -m_run[qb]));
-                acc += e;
-                p[qb][kb * 2 + (r >> 3)][r & 7] = to_elem<T>(e);
+            for (int r = 0; r < 16; r += 2) {
+                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r], c_log2, -m_run[qb]));
+                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r + 1], c_log2, -m_run[qb]));
+                const T h0 = to_elem<T>(e0), h1 = to_elem<T>(e1);
+                p[qb][kb * 2 + (r >> 3)][r & 7] = h0;
+                p[qb][kb * 2 + (r >> 3)][(r & 7) + 1] = h1;
+                acc = pair_sum<T>(acc, e0, e1, h0, h1);
             }
         }
         rs[qb] = acc;
