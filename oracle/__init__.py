@@ -126,10 +126,11 @@ def attention_fwd(q, k, v, causal, scale, rows=None, tile_n=0, nthreads=None, li
 
 
 def _bind_bwd(lib):
-    fn = lib.fa_oracle_bwd
+    fn = lib.fa_oracle_bwd_masked
     fn.restype = ctypes.c_int
     fn.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 5 + [
-        ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_double,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     return lib
 
 
@@ -145,12 +146,14 @@ def load_bwd(path=None):
     return _lib_bwd
 
 
-def attention_bwd(q, k, v, dout, causal, scale, nthreads=None, lib=None):
+def attention_bwd(q, k, v, dout, causal, scale, nthreads=None, lib=None, window_left=-1,
+                  window_right=-1, key_lens=None):
     """fp64 gradients of sum(dout * O) for O = attention(q, k, v) on the CPU.
 
     q, dout : ``[B, H, Nq, d]``; k, v: ``[B, H, Nk, d]`` (values in the storage
-              dtype). Returns ``(dq, dk, dv)`` as float64 numpy arrays. See the
-              header of ``fa_oracle_bwd.c`` for the definition.
+              dtype). window_left, window_right, key_lens: the masks of
+              ``attention_fwd``. Returns ``(dq, dk, dv)`` as float64 numpy
+              arrays. See the header of ``fa_oracle_bwd.c`` for the definition.
     """
     lib = lib or load_bwd()
     qf, kf, vf, df = _as_f32(q), _as_f32(k), _as_f32(v), _as_f32(dout)
@@ -160,9 +163,14 @@ def attention_bwd(q, k, v, dout, causal, scale, nthreads=None, lib=None):
     dq = np.empty((B, H, Nq, d), dtype=np.float64)
     dk = np.empty((B, H, Nk, d), dtype=np.float64)
     dv = np.empty((B, H, Nk, d), dtype=np.float64)
-    rc = lib.fa_oracle_bwd(qf.ctypes.data, kf.ctypes.data, vf.ctypes.data, df.ctypes.data, B, H,
-                           Nq, Nk, d, 1 if causal else 0, float(scale), dq.ctypes.data,
-                           dk.ctypes.data, dv.ctypes.data, int(nthreads or default_threads()))
+    kl = None if key_lens is None else np.ascontiguousarray(np.asarray(key_lens, dtype=np.int64))
+    if kl is not None:
+        assert kl.shape == (B,)
+    rc = lib.fa_oracle_bwd_masked(qf.ctypes.data, kf.ctypes.data, vf.ctypes.data, df.ctypes.data, B,
+                                  H, Nq, Nk, d, 1 if causal else 0, int(window_left),
+                                  int(window_right), None if kl is None else kl.ctypes.data,
+                                  float(scale), dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
+                                  int(nthreads or default_threads()))
     if rc != 0:
         raise RuntimeError(f"fa_oracle_bwd failed with status {rc}")
     return dq, dk, dv

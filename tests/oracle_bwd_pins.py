@@ -15,6 +15,11 @@ What pins what:
   uniform_dv           Q = 0: P is uniform over the visible keys, and dV has a
                        closed form (mean of dO, or a causal suffix sum)
   linear_in_dout       the gradients are linear in dO
+  masked_finite_differences  central differences of the masked forward oracle
+                       (padding, windows, rows that see no key)
+  masked_torch_autograd  fp64 autograd through an explicit boolean mask
+  masked_padding_is_truncation  a padding length L gives the gradients of the
+                       first L keys, bit for bit, and zero for the rest
 """
 
 import numpy as np
@@ -135,5 +140,76 @@ def linear_in_dout(bwd):
             _close(c, 2 * a - 3 * b, 1e-12, f"{name} linear in dO causal={causal}")
 
 
+# (B, H, Nq, Nk, d, causal, window_left, window_right, key_lens)
+MASKS = [(2, 1, 7, 9, 4, True, 2, -1, [9, 3]),      # causal window; padding empties rows of batch 1
+         (1, 2, 6, 8, 3, False, 1, 2, None),        # band
+         (2, 1, 5, 6, 4, False, -1, -1, [0, 4])]    # a batch with no key at all
+
+
+def masked_finite_differences(bwd):
+    rng = np.random.default_rng(7)
+    for (B, H, Nq, Nk, d, causal, wl, wr, kl) in MASKS:
+        q, k, v, dout = (_f(t) for t in _inputs(B, H, Nq, Nk, d, "fp16", 300 + Nq))
+        scale = 0.4
+        dq, dk, dv = bwd(q, k, v, dout, causal, scale, window_left=wl, window_right=wr, key_lens=kl)
+
+        def loss(q_, k_, v_):
+            o, _ = oracle.attention_fwd(q_.astype(np.float32), k_.astype(np.float32),
+                                        v_.astype(np.float32), causal, scale, window_left=wl,
+                                        window_right=wr, key_lens=kl)
+            return float(np.sum(o * dout))
+        h = 2.0 ** -10
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            for _ in range(8):
+                idx = tuple(rng.integers(0, s) for s in x.shape)
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = {"q": q, "k": k, "v": v}
+                args_m = {"q": q, "k": k, "v": v}
+                args_p[name], args_m[name] = xp, xm
+                fd = (loss(**{a + "_": b for a, b in args_p.items()}) -
+                      loss(**{a + "_": b for a, b in args_m.items()})) / (2 * h)
+                assert abs(fd - g[idx]) <= 2e-5 * max(1.0, abs(fd)), \
+                    f"masked d{name}{idx}: finite difference {fd:.8f} vs {g[idx]:.8f}"
+
+
+def masked_torch_autograd(bwd):
+    B, H, Nq, Nk, d = 2, 2, 40, 56, 16
+    q, k, v, dout = _inputs(B, H, Nq, Nk, d, "bf16", 320)
+    i = torch.arange(Nq)[:, None]
+    j = torch.arange(Nk)[None, :]
+    for causal, wl, wr, kl in [(True, 9, -1, [56, 20]), (False, 4, 7, [30, 56]), (False, -1, -1, [56, 0])]:
+        allow = torch.ones(B, 1, Nq, Nk, dtype=torch.bool)
+        if wl >= 0:
+            allow = allow & (j >= i - wl)
+        allow = allow & ((j <= i) if causal else ((j <= i + wr) if wr >= 0 else True))
+        allow = allow & (torch.arange(Nk)[None, None, None, :] < torch.tensor(kl)[:, None, None, None])
+        rows = allow.any(dim=-1, keepdim=True)  # rows that see some key
+        q64, k64, v64 = (t.to(torch.float64).requires_grad_() for t in (q, k, v))
+        s = torch.matmul(q64, k64.transpose(-1, -2).contiguous()) * 0.3
+        s = torch.where(allow, s, torch.tensor(float("-inf"), dtype=torch.float64))
+        s = torch.where(rows, s, torch.zeros((), dtype=torch.float64))  # finite softmax on empty rows
+        o = torch.matmul(torch.softmax(s, dim=-1), v64) * rows
+        o.backward(dout.to(torch.float64))
+        dq, dk, dv = bwd(q, k, v, dout, causal, 0.3, window_left=wl, window_right=wr, key_lens=kl)
+        for name, a, b in (("dq", dq, q64.grad), ("dk", dk, k64.grad), ("dv", dv, v64.grad)):
+            _close(a, b.numpy(), 1e-12, f"masked autograd {name} causal={causal} wl={wl} wr={wr}")
+
+
+def masked_padding_is_truncation(bwd):
+    B, H, Nq, Nk, d = 3, 2, 30, 40, 8
+    q, k, v, dout = _inputs(B, H, Nq, Nk, d, "fp16", 330)
+    lens = [40, 13, 1]
+    for causal in (False, True):
+        dq, dk, dv = bwd(q, k, v, dout, causal, 0.25, key_lens=lens)
+        for b, L in enumerate(lens):
+            t = bwd(q[b:b + 1], k[b:b + 1, :, :L].contiguous(), v[b:b + 1, :, :L].contiguous(),
+                    dout[b:b + 1], causal, 0.25)
+            assert np.array_equal(dq[b:b + 1], t[0]), f"dq padded to {L} causal={causal}"
+            assert np.array_equal(dk[b:b + 1, :, :L], t[1]) and np.array_equal(dv[b:b + 1, :, :L], t[2])
+            assert np.all(dk[b, :, L:] == 0) and np.all(dv[b, :, L:] == 0)
+
+
 ALL_PINS = [finite_differences, torch_autograd, dk_sums_to_zero, equal_keys_zero_dq, uniform_dv,
-            linear_in_dout]
+            linear_in_dout, masked_finite_differences, masked_torch_autograd, masked_padding_is_truncation]

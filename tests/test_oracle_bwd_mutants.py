@@ -27,6 +27,12 @@ MUTANTS = [
     ("keys_strided_by_queries", [("*kh = job->k + bh * Nk * d;", "*kh = job->k + bh * Nq * d;")]),
     ("dp_transposed_dims", [("acc += (double)doi[c] * (double)vh[j * d + c];",
                              "acc += (double)doi[c] * (double)vh[j * d + (d - 1 - c)];")]),
+    ("window_left_off_by_one", [("l = i - job->win_left;", "l = i - job->win_left + 1;")]),
+    ("window_right_off_by_one", [("h = i + job->win_right + 1;", "h = i + job->win_right;")]),
+    ("padding_ignored", [("h = job->key_lens[b];", "h = h;")]),
+    ("padding_of_first_batch", [("row_range(job, bh / job->H, i, &lo, &hi);", "row_range(job, 0, i, &lo, &hi);")]),
+    ("empty_rows_take_every_key", [("continue; /* no visible key: O_i = 0, no gradient */",
+                                    "{ lo = 0; hi = Nk; } /* mutant */")]),
 ]
 
 
