@@ -239,6 +239,19 @@ int fa_bwd_qk(const void *q, const void *k, const void *v, const void *o, const 
               int Nk, int d, int causal, float scale, int dtype, void *stream);
 
 /*
+ * fa_bwd_masked -- the backward pass of fa_fwd_masked: the same padding
+ * lengths and sliding windows (window_left, window_right, key_lens with the
+ * meaning, clamping and overlap rules of fa_fwd_masked), o and lse as that
+ * call wrote them. Keys that no row sees get dK = dV = 0; a row that sees no
+ * key (O = 0, lse = -inf) gets dQ = 0 and adds nothing elsewhere. Other
+ * arguments as fa_bwd_qk; with no mask in effect it is fa_bwd_qk.
+ */
+int fa_bwd_masked(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                  const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H, int Nq,
+                  int Nk, int d, int causal, int window_left, int window_right,
+                  const int32_t *key_lens, float scale, int dtype, void *stream);
+
+/*
  * fa_status_string -- human-readable text for a status code. For FA_ERR_HIP
  * and FA_ERR_INVALID_ARG it names the HIP error or the failed check of the
  * last failing call on the calling thread. The returned pointer stays valid

@@ -403,3 +403,18 @@ def test_fa_fwd_f32_rejects_before_any_hip_call(lib):
                    (dict(o=P[0]), fa.FA_ERR_INVALID_ARG), (dict(ws=P[2]), fa.FA_ERR_INVALID_ARG),
                    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG), (dict(Nk=0), fa.FA_ERR_INVALID_ARG)]:
         assert run(**kw) == st, kw
+
+
+def test_fa_bwd_masked_rejects_before_any_hip_call(lib):
+    p = [0x10000 * (i + 1) for i in range(10)]
+    base = dict(B=2, H=1, Nq=16, Nk=32, d=64, causal=0, wl=-1, wr=-1, kl=0xB00000, scale=0.125)
+
+    def run(**kw):
+        a = dict(base)
+        a.update(kw)
+        return fa.fa_bwd_masked(*p, a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["causal"], a["wl"],
+                                a["wr"], a["kl"], a["scale"], fa.FA_DTYPE_BF16, None)
+    for kw, st in [(dict(wl=-2), fa.FA_ERR_INVALID_ARG), (dict(kl=0xB00002), fa.FA_ERR_INVALID_ARG),
+                   (dict(kl=p[7] + 16), fa.FA_ERR_INVALID_ARG),   # key_lens inside dk
+                   (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(Nk=0), fa.FA_ERR_INVALID_ARG)]:
+        assert run(**kw) == st, kw

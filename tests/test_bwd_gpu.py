@@ -109,3 +109,52 @@ def test_backward_query_and_key_lengths(case, causal):
     dq, dk, dv = check_bwd(B, H, Nq, d, dtype, causal, 540 + Nq % 50, Nk=Nk)
     if causal and Nq < Nk:  # keys past the last query row are seen by no row
         assert torch.all(dk[:, :, Nq:] == 0) and torch.all(dv[:, :, Nq:] == 0)
+
+
+# (B, H, Nq, Nk, d, dtype, causal, window_left, window_right, key_lens): the
+# masks of fa_fwd_masked through the forward and fa_bwd_masked
+MASK_CASES = [(3, 2, 500, 500, 128, "bf16", False, -1, -1, [500, 250, 0]),
+              (1, 2, 700, 700, 128, "bf16", True, 100, -1, None),
+              (2, 2, 600, 600, 64, "fp16", False, 64, 64, None),
+              (2, 1, 600, 600, 128, "fp16", True, 50, -1, [600, 300]),
+              (2, 2, 300, 1000, 64, "bf16", False, -1, 200, [1000, 400]),
+              (1, 2, 1000, 300, 128, "fp16", True, 120, -1, [300]),
+              (8, 4, 333, 333, 128, "bf16", False, -1, -1, [333, 1, 64, 65, 300, 0, 200, 333])]
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=[f"q{c[2]}k{c[3]}d{c[4]}{c[5]}c{int(c[6])}wl{c[7]}wr{c[8]}"
+                                                  for c in MASK_CASES])
+def test_backward_masks_match_oracle(case):
+    B, H, Nq, Nk, d, dtype, causal, wl, wr, kl = case
+    print(f"[case] bwd masks {case}", flush=True)
+    q = make_qkv(B, H, Nq, d, dtype, 560 + Nq % 40)[0]
+    _, k, v = make_qkv(B, H, Nk, d, dtype, 563 + Nq % 40)
+    dout = make_qkv(B, H, Nq, d, dtype, 567 + Nq % 40)[0]
+    scale = fa.default_scale(d)
+    qd, kd, vd, dd = (t.cuda() for t in (q, k, v, dout))
+    mk = dict(window_left=wl, window_right=wr, key_lens=kl)
+    o, lse = fa.fwd(qd, kd, vd, causal=causal, splits=1, **mk)
+    g = [t.cpu() for t in fa.bwd(qd, kd, vd, o, lse, dd, causal=causal, **mk)]
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd(q, k, v, dout, causal, scale, **mk)
+    # structural zeros: rows that see no key (dQ) and keys that no row sees (dK, dV)
+    i = np.arange(Nq)[:, None]
+    j = np.arange(Nk)[None, :]
+    vis = np.ones((B, Nq, Nk), dtype=bool)
+    if wl >= 0:
+        vis &= (j >= i - wl)[None]
+    vis &= (j <= i)[None] if causal else ((j <= i + wr)[None] if wr >= 0 else True)
+    if kl is not None:
+        vis &= np.arange(Nk)[None, None, :] < np.asarray(kl)[:, None, None]
+    no_key = ~vis.any(axis=2)      # [B, Nq]
+    no_row = ~vis.any(axis=1)      # [B, Nk]
+    errs = []
+    for name, a, b in zip(("dq", "dk", "dv"), g, ref):
+        a = a.float().numpy().astype(np.float64)
+        assert np.all(np.isfinite(a)), f"{name}: non-finite"
+        errs.append(float(np.abs(a - b).max() / max(float(np.abs(b).max()), 1e-3)))
+        zero = no_key if name == "dq" else no_row
+        assert np.all(a[zero[:, None, :].repeat(H, axis=1)] == 0), f"{name}: nonzero gradient of an unseen row or key"
+    print(f"[bwd] masks {case[:7]} wl={wl} wr={wr} rel err dq={errs[0]:.2e} dk={errs[1]:.2e} "
+          f"dv={errs[2]:.2e}", flush=True)
+    assert max(errs) <= TOL[q.dtype]

@@ -29,7 +29,7 @@ FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1
 
 # Entry points declared in include/fa.h.
 EXPORTED = ("fa_fwd", "fa_fwd_qk", "fa_fwd_split_qk", "fa_split_count", "fa_split_workspace_bytes",
-            "fa_fwd_masked", "fa_fwd_split_masked", "fa_fwd_f32", "fa_f32_workspace_bytes", "fa_bwd", "fa_bwd_qk",
+            "fa_fwd_masked", "fa_fwd_split_masked", "fa_fwd_f32", "fa_f32_workspace_bytes", "fa_bwd", "fa_bwd_qk", "fa_bwd_masked",
             "fa_status_string", "fa_tile_counts",
             "fa_tile_counts_qk", "fa_tile_counts_masked", "fa_plan", "fa_plan_qk", "fa_plan_masked")
 
@@ -98,6 +98,9 @@ def load_library(path=LIB_PATH):
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_bwd_masked.restype = ctypes.c_int
+    lib.fa_bwd_masked.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 8 + [
+        ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
     lib.fa_bwd_qk.restype = ctypes.c_int
     lib.fa_bwd_qk.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
@@ -215,14 +218,24 @@ def fa_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d, causal,
                                     int(Nk), int(d), int(causal), float(scale), int(dtype), stream)
 
 
-def bwd(q, k, v, o, lse, dout, causal=False, scale=None, stream=None):
+def fa_bwd_masked(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d, causal, window_left,
+                  window_right, key_lens, scale, dtype, stream):
+    """Direct call of the C entry point with raw pointers (ints); returns the status."""
+    return load_library().fa_bwd_masked(q, k, v, o, dout, lse, dq, dk, dv, delta, int(B), int(H),
+                                        int(Nq), int(Nk), int(d), int(causal), int(window_left),
+                                        int(window_right), key_lens, float(scale), int(dtype), stream)
+
+
+def bwd(q, k, v, o, lse, dout, causal=False, scale=None, stream=None, window_left=-1, window_right=-1,
+        key_lens=None):
     """Attention backward on the GPU: returns ``(dq, dk, dv)``.
 
     q, o, dout : CUDA (HIP) tensors ``[B, H, Nq, d]``; k, v ``[B, H, Nk, d]``;
                  contiguous, one of float16/bfloat16; ``o`` and ``lse``
                  (``[B, H, Nq]`` float32) from ``fwd`` with the same causal
-                 flag and scale. The D = rowsum(dO * O) scratch is allocated
-                 with torch.
+                 flag, scale and masks. The D = rowsum(dO * O) scratch is
+                 allocated with torch.
+    window_left, window_right, key_lens : the masks of ``fwd``.
     """
     import torch
     ts = (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout))
@@ -248,9 +261,18 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, stream=None):
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     with torch.cuda.device(q.device):
-        rc = fa_bwd_qk(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-                       B, H, N, Nk, d, causal, scale, code, handle)
+        kl_ptr = None
+        if key_lens is not None:
+            if not torch.is_tensor(key_lens):
+                key_lens = torch.tensor([int(x) for x in key_lens], dtype=torch.int32, device=q.device)
+            if (key_lens.dtype != torch.int32 or not key_lens.is_cuda or key_lens.shape != (B,)
+                    or not key_lens.is_contiguous()):
+                raise ValueError("key_lens must be a contiguous int32 [B] GPU tensor")
+            kl_ptr = key_lens.data_ptr()
+        rc = fa_bwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                           B, H, N, Nk, d, causal, window_left, window_right, kl_ptr, scale, code,
+                           handle)
     _check(rc)
     return dq, dk, dv
 

@@ -157,6 +157,53 @@ double causal_area(double Nq, double Nk)
     return Nq <= Nk ? 0.5 * Nq * Nq : 0.5 * Nk * Nk + (Nq - Nk) * Nk;
 }
 
+int bwd_checked(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                void* dq, void* dk, void* dv, float* delta, int B, int H, int Nq, int Nk, int d, int causal,
+                float scale, int dtype, const fa::MaskArgs* mask, void* stream)
+{
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta)
+        return fail(FA_ERR_INVALID_ARG, "NULL tensor pointer");
+    const void* a16[] = {q, k, v, o, dout, dq, dk, dv, delta};
+    for (const void* p : a16)
+        if (!aligned(p, 16)) return fail(FA_ERR_INVALID_ARG, "tensors and delta must be 16-byte aligned");
+    if (!aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    const int rc = check_problem(B, H, Nq, Nk, d, causal, dtype);
+    if (rc != FA_OK) return rc;
+    if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "the backward pass takes head dim 64 or 128");
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    // query side: q, o, dout, dq [Nq rows], lse and delta [Nq]; key side: k, v, dk, dv [Nk rows]
+    const size_t qb = (size_t)B * H * Nq * d * 2, kb = (size_t)B * H * Nk * d * 2;
+    const size_t lb = (size_t)B * H * Nq * 4;
+    struct Buf {
+        const void* p;
+        size_t n;
+    };
+    const Buf ins[] = {{q, qb}, {k, kb}, {v, kb}, {o, qb}, {dout, qb}, {lse, lb}};
+    const Buf outs[] = {{dq, qb}, {dk, kb}, {dv, kb}, {delta, lb}};
+    for (const Buf& w : outs)
+        for (const Buf& r : ins)
+            if (overlap(w.p, w.n, r.p, r.n))
+                return fail(FA_ERR_INVALID_ARG, "an output (dq, dk, dv or delta) overlaps an input");
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+                return fail(FA_ERR_INVALID_ARG, "dq, dk, dv and delta overlap");
+    if (mask) {
+        const int rc2 = check_masks(B, H, Nq, d, mask->window_left, mask->window_right, mask->key_lens, dq,
+                                    lse, nullptr, 0);
+        if (rc2 != FA_OK) return rc2;
+        const size_t nb = (size_t)B * 4;
+        if (mask->key_lens && (overlap(mask->key_lens, nb, dk, kb) || overlap(mask->key_lens, nb, dv, kb) ||
+                               overlap(mask->key_lens, nb, delta, lb)))
+            return fail(FA_ERR_INVALID_ARG, "key_lens overlaps an output");
+        if (masks_off(causal, mask->window_left, mask->window_right, mask->key_lens)) mask = nullptr;
+    }
+    return hip_status(fa::launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d, causal != 0,
+                                     scale, dtype == FA_DTYPE_BF16, mask, (hipStream_t)stream));
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -429,41 +476,25 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                                          (hipStream_t)stream));
 }
 
+
 int fa_bwd_qk(const void* q, const void* k, const void* v, const void* o, const void* dout,
               const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int Nq, int Nk,
               int d, int causal, float scale, int dtype, void* stream)
 {
     g_msg[0] = 0;
-    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta)
-        return fail(FA_ERR_INVALID_ARG, "NULL tensor pointer");
-    const void* a16[] = {q, k, v, o, dout, dq, dk, dv, delta};
-    for (const void* p : a16)
-        if (!aligned(p, 16)) return fail(FA_ERR_INVALID_ARG, "tensors and delta must be 16-byte aligned");
-    if (!aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-    const int rc = check_problem(B, H, Nq, Nk, d, causal, dtype);
-    if (rc != FA_OK) return rc;
-    if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "the backward pass takes head dim 64 or 128");
-    if (!(scale > 0.f) || !isfinite(scale))
-        return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
-    // query side: q, o, dout, dq [Nq rows], lse and delta [Nq]; key side: k, v, dk, dv [Nk rows]
-    const size_t qb = (size_t)B * H * Nq * d * 2, kb = (size_t)B * H * Nk * d * 2;
-    const size_t lb = (size_t)B * H * Nq * 4;
-    struct Buf {
-        const void* p;
-        size_t n;
-    };
-    const Buf ins[] = {{q, qb}, {k, kb}, {v, kb}, {o, qb}, {dout, qb}, {lse, lb}};
-    const Buf outs[] = {{dq, qb}, {dk, kb}, {dv, kb}, {delta, lb}};
-    for (const Buf& w : outs)
-        for (const Buf& r : ins)
-            if (overlap(w.p, w.n, r.p, r.n))
-                return fail(FA_ERR_INVALID_ARG, "an output (dq, dk, dv or delta) overlaps an input");
-    for (int i = 0; i < 4; ++i)
-        for (int j = i + 1; j < 4; ++j)
-            if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
-                return fail(FA_ERR_INVALID_ARG, "dq, dk, dv and delta overlap");
-    return hip_status(fa::launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d, causal != 0,
-                                     scale, dtype == FA_DTYPE_BF16, (hipStream_t)stream));
+    return bwd_checked(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d, causal, scale, dtype, nullptr,
+                       stream);
+}
+
+int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int Nq, int Nk,
+                  int d, int causal, int window_left, int window_right, const int32_t* key_lens, float scale,
+                  int dtype, void* stream)
+{
+    g_msg[0] = 0;
+    const fa::MaskArgs mask{window_left, window_right, key_lens, H};
+    return bwd_checked(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d, causal, scale, dtype, &mask,
+                       stream);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -32,6 +32,12 @@
 //   * N_q query rows against N_k keys, with the forward's top-left causal
 //     rule (key j visible to row i iff j <= i): query-side tensors (q, dO, O,
 //     L, D, dQ) have N_q rows per head, key-side ones (K, V, dK, dV) N_k.
+//   * MASKS: the forward's padding lengths and sliding windows (fa_tiles.h,
+//     row_keys). The rows that see key j form one interval [i_min(j),
+//     i_max(j)]; a dK/dV workgroup visits only the query tiles whose rows see
+//     one of its keys and masks P per element, and the dQ kernel takes the
+//     forward's masked key-tile ranges. A row that sees no key (lse = -inf,
+//     O = 0) gets P = 0 everywhere, so it adds nothing.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -115,13 +121,29 @@ constexpr int kBwdWaves = 8;                // waves per dK/dV workgroup
 constexpr int kBwdKeys = 32 * kBwdWaves;     // keys per dK/dV workgroup (32 per wave)
 constexpr int kBwdRows = 64;                 // query rows per streamed tile
 
-template <typename T, int D, bool CAUSAL>
+// Rows that see key j under the masks: i_min(j) <= i <= i_max(j), none when
+// j is past the batch's key count (fa_tiles.h, row_keys, read per key).
+struct KeyRows {
+    int64_t first, last;  // empty when first > last
+};
+
+__device__ __forceinline__ KeyRows key_rows(int64_t j, bool causal, const MaskArgs& m, int64_t key_len)
+{
+    KeyRows r;
+    r.first = causal ? j : (m.window_right >= 0 ? j - m.window_right : 0);
+    if (r.first < 0) r.first = 0;
+    r.last = m.window_left >= 0 ? j + m.window_left : INT64_MAX / 4;
+    if (j >= key_len) r.last = r.first - 1;
+    return r;
+}
+
+template <typename T, int D, bool CAUSAL, bool MASKS>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kBwdWaves, 64 * kBwdWaves),
                           amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                         const T* __restrict__ dout, const float* __restrict__ lse,
                         const float* __restrict__ delta, T* __restrict__ dk, T* __restrict__ dv, int Nq,
-                        int Nk, int n_kt, float scale, float c_log2)
+                        int Nk, int n_kt, float scale, float c_log2, MaskArgs mask)
 {
     typedef Cfg<D, kBwdWaves, 1> C;  // 64-row copies by the whole workgroup, as the forward's tiles
     typedef typename Mma<T>::vec8 vec8;
@@ -134,7 +156,7 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     uint16_t* const vtile = smem + 2 * BUF;
 
     uint32_t bh, kt;
-    bwd_tile<CAUSAL>(n_kt, true, bh, kt);
+    bwd_tile<CAUSAL || MASKS>(n_kt, true, bh, kt);
     const int k0 = (int)kt * kBwdKeys;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -174,10 +196,39 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
         }
     };
 
-    const int n_qt = (Nq + kBwdRows - 1) / kBwdRows;
+    int n_qt = (Nq + kBwdRows - 1) / kBwdRows;
     // no earlier query row sees these keys; with fewer queries than keys a
     // causal key block can lie past every row (its gradients are zero)
-    const int t_begin = CAUSAL ? k0 / kBwdRows : 0;
+    int t_begin = CAUSAL ? k0 / kBwdRows : 0;
+    // masks: the rows that see a key of this block, and this lane's key's rows
+    int key_len = Nk;
+    int64_t my_first = 0, my_last = INT64_MAX / 4;
+    if (MASKS) {
+        if (mask.key_lens) key_len = min(max(mask.key_lens[bh / (uint32_t)mask.heads], 0), Nk);
+        const int k1 = min(k0 + kBwdKeys, key_len);  // one past the block's last real key
+        if (k1 <= k0) {
+            n_qt = t_begin = 0;  // padding only: no row sees these keys
+        } else {
+            const KeyRows a = key_rows(k0, CAUSAL, mask, key_len), z = key_rows(k1 - 1, CAUSAL, mask, key_len);
+            t_begin = (int)(a.first / kBwdRows);
+            const int64_t r_end = min((int64_t)Nq, z.last + 1);
+            n_qt = r_end > a.first ? (int)((r_end + kBwdRows - 1) / kBwdRows) : t_begin;
+        }
+        const KeyRows mine = key_rows(kw0 + l32, CAUSAL, mask, key_len);
+        my_first = mine.first;
+        my_last = mine.last;
+    }
+    // this wave's keys: the rows that see one of them (masks)
+    int64_t wave_first = 0, wave_last = INT64_MAX / 4;
+    if (MASKS) {
+        const int kl = min(kw0 + 31, key_len - 1);
+        if (kl < kw0) {
+            wave_last = -1;  // all of this wave's keys are padding
+        } else {
+            wave_first = key_rows(kw0, CAUSAL, mask, key_len).first;
+            wave_last = key_rows(kl, CAUSAL, mask, key_len).last;
+        }
+    }
     if (t_begin < n_qt) issue(t_begin);
     stage_barrier();
     for (int t = t_begin; t < n_qt; ++t) {
@@ -189,7 +240,8 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
 #pragma unroll
         for (int qb = 0; qb < kBwdRows / 32; ++qb) {
             const int qbase = t * kBwdRows + qb * 32;  // first query row of this block
-            if (CAUSAL && qbase + 31 < kw0) continue;  // every query of the block precedes every key
+            if (!MASKS && CAUSAL && qbase + 31 < kw0) continue;  // every query of the block precedes every key
+            if (MASKS && (qbase + 31 < wave_first || qbase > wave_last)) continue;  // no row sees these keys
             // S = Q K^T and dP = dO V^T: queries on M, this wave's keys on N
             f32x16 s = (f32x16){}, dp = (f32x16){};
             const int row = qb * 32 + l32, vrow = 32 * wave + l32;
@@ -214,7 +266,12 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * g + e;
                     float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -lq[e] * kLog2e));
-                    if (CAUSAL && kw0 + l32 > qbase + 8 * g + 4 * hh + e) p = 0.f;
+                    const int qi = qbase + 8 * g + 4 * hh + e;
+                    if (MASKS) {
+                        if (qi < my_first || qi > my_last) p = 0.f;
+                    } else if (CAUSAL && kw0 + l32 > qi) {
+                        p = 0.f;
+                    }
                     const float dsv = p * (dp[r] - dq[e]);
                     pk[r >> 3][r & 7] = to_elem<T>(p);
                     dsk[r >> 3][r & 7] = to_elem<T>(dsv);
@@ -236,19 +293,19 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
 }
 
 // ---------------------------------------------------------------- dQ
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool MASKS>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                       const T* __restrict__ dout, const float* __restrict__ lse,
                       const float* __restrict__ delta, T* __restrict__ dq, int Nq, int Nk, int n_qt,
-                      float scale, float c_log2)
+                      float scale, float c_log2, MaskArgs mask)
 {
     typedef Cfg<D, 4, 1> C;  // 128 query rows, 64-key tiles
     typedef typename Mma<T>::vec8 vec8;
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * C::TILE];
 
     uint32_t bh, qt;
-    bwd_tile<CAUSAL>(n_qt, false, bh, qt);
+    bwd_tile<CAUSAL || MASKS>(n_qt, false, bh, qt);
     const int q0 = (int)qt * C::BM;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -260,35 +317,71 @@ void fa_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
     load_q<T, D, 1, C::DS>(q + q_off, q0 + wave * 32, Nq, l32, hh, qrow, qf);
     load_q<T, D, 1, C::DS>(dout + q_off, q0 + wave * 32, Nq, l32, hh, qrow, df);
     const bool row_ok = qrow[0] < Nq;
-    const float l2 = row_ok ? lse[(int64_t)bh * Nq + qrow[0]] * kLog2e : 0.f;
+    float l2 = row_ok ? lse[(int64_t)bh * Nq + qrow[0]] * kLog2e : 0.f;
+    // a row that saw no key (masks) has lse = -inf and every score masked:
+    // any finite value gives P = 0 instead of -inf - (-inf)
+    if (MASKS && !(l2 > -INFINITY)) l2 = 0.f;
     const float dd = row_ok ? delta[(int64_t)bh * Nq + qrow[0]] : 0.f;
 
     f32x16 dq_acc[1][C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) dq_acc[0][db] = (f32x16){};
 
-    const TileSpan span = tile_span(q0, C::BM, C::BN, Nq, Nk, CAUSAL);
-    const int n_unmasked = (int)span.unmasked, n_tiles = (int)span.total;
-    const int n_wave = CAUSAL ? min(n_tiles, (q0 + (wave + 1) * 32 - 1) / C::BN + 1) : n_tiles;
+    // key tiles [t0, t1), of which [u_lo, u_hi) need no mask (the forward's split)
+    int t0 = 0, t1, u_lo = 0, u_hi, w_lo = 0, n_wave;
+    int row_lo = 0, row_hi = 0, key_len = Nk;
+    if (MASKS) {
+        if (mask.key_lens) key_len = min(max(mask.key_lens[bh / (uint32_t)mask.heads], 0), Nk);
+        const MaskedSpan ms = masked_span(q0, C::BM, C::BN, Nq, Nk, CAUSAL, mask.window_left,
+                                          mask.window_right, key_len);
+        t0 = (int)ms.first;
+        t1 = (int)ms.end;
+        u_lo = (int)ms.unmasked_begin;
+        u_hi = (int)ms.unmasked_end;
+        const int r0 = q0 + wave * 32;
+        if (r0 >= Nq) {
+            w_lo = n_wave = t0;
+        } else {
+            const MaskedSpan ws = masked_span(r0, 32, C::BN, Nq, Nk, CAUSAL, mask.window_left, mask.window_right,
+                                              key_len);
+            w_lo = max(t0, (int)ws.first);
+            n_wave = min(t1, (int)ws.end);
+        }
+        const RowKeys rk = row_keys(qrow[0], Nk, CAUSAL, mask.window_left, mask.window_right, key_len);
+        row_lo = (int)rk.lo;
+        row_hi = (int)rk.hi;
+    } else {
+        const TileSpan span = tile_span(q0, C::BM, C::BN, Nq, Nk, CAUSAL);
+        u_hi = (int)span.unmasked;
+        t1 = (int)span.total;
+        n_wave = CAUSAL ? min(t1, (q0 + (wave + 1) * 32 - 1) / C::BN + 1) : t1;
+    }
 
     auto kbuf = [&](int i) { return smem + (i & 1) * C::TILE; };
     auto vbuf = [&](int i) { return smem + (2 + (i & 1)) * C::TILE; };
     const uint32_t head_bytes = (uint32_t)Nk * (D * 2);
     const rsrc_t krs = head_rsrc(k + kv_off, head_bytes), vrs = head_rsrc(v + kv_off, head_bytes);
     const uint32_t lane_off = tile_lane_offset<D>(wave, lane);
-    issue_tile<D, 4, 1>(kbuf(0), krs, 0, wave, lane_off);
-    issue_tile<D, 4, 1>(vbuf(0), vrs, 0, wave, lane_off);
+    if (t0 < t1) {
+        issue_tile<D, 4, 1>(kbuf(t0), krs, t0 * C::BN, wave, lane_off);
+        issue_tile<D, 4, 1>(vbuf(t0), vrs, t0 * C::BN, wave, lane_off);
+    }
     stage_barrier();
-    for (int j = 0; j < n_tiles; ++j) {
-        if (j + 1 < n_tiles) {
+    for (int j = t0; j < t1; ++j) {
+        if (j + 1 < t1) {
             issue_tile<D, 4, 1>(kbuf(j + 1), krs, (j + 1) * C::BN, wave, lane_off);
             issue_tile<D, 4, 1>(vbuf(j + 1), vrs, (j + 1) * C::BN, wave, lane_off);
         }
-        if (j < n_wave) {
+        if (j < n_wave && j >= w_lo) {
             f32x16 s[1][C::KB], dp[1][C::KB];
             scores<T, D, 1, C::KB, C::DS>(s, kbuf(j), qf, l32, hh);
             scores<T, D, 1, C::KB, C::DS>(dp, vbuf(j), df, l32, hh);
-            if (j >= n_unmasked) mask_scores<C::KB, CAUSAL>(s[0], j * C::BN, qrow[0], Nk, hh);
+            if (j < u_lo || j >= u_hi) {
+                if (MASKS)
+                    mask_range<C::KB>(s[0], j * C::BN, row_lo, row_hi, hh);
+                else
+                    mask_scores<C::KB, CAUSAL>(s[0], j * C::BN, qrow[0], Nk, hh);
+            }
             vec8 dsk[1][C::KT];
 #pragma unroll
             for (int kb = 0; kb < C::KB; ++kb) {
@@ -305,10 +398,10 @@ void fa_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
     store_rows<T, D, C::DB>(dq_acc[0], scale, qrow[0], Nq, dq + q_off, hh);
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool MASKS>
 hipError_t launch_bwd_typed(const void* q, const void* k, const void* v, const void* o, const void* dout,
                             const float* lse, void* dq, void* dk, void* dv, float* delta, int BH, int Nq,
-                            int Nk, float scale, hipStream_t stream)
+                            int Nk, float scale, const MaskArgs& mask, hipStream_t stream)
 {
     const int64_t n_rows = (int64_t)BH * Nq;
     const float c_log2 = scale * kLog2e;
@@ -319,16 +412,16 @@ hipError_t launch_bwd_typed(const void* q, const void* k, const void* v, const v
     if (e != hipSuccess) return e;
     const int n_kt = (Nk + kBwdKeys - 1) / kBwdKeys;
     dim3 g1((unsigned)((int64_t)n_kt * BH)), b1(64 * kBwdWaves);
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, CAUSAL>), g1, b1, 0, stream, (const T*)q, (const T*)k,
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, CAUSAL, MASKS>), g1, b1, 0, stream, (const T*)q, (const T*)k,
                        (const T*)v, (const T*)dout, lse, (const float*)delta, (T*)dk, (T*)dv, Nq, Nk, n_kt,
-                       scale, c_log2);
+                       scale, c_log2, mask);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_qt = (Nq + 127) / 128;
     dim3 g2((unsigned)((int64_t)n_qt * BH)), b2(256);
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, CAUSAL>), g2, b2, 0, stream, (const T*)q, (const T*)k,
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, CAUSAL, MASKS>), g2, b2, 0, stream, (const T*)q, (const T*)k,
                        (const T*)v, (const T*)dout, lse, (const float*)delta, (T*)dq, Nq, Nk, n_qt, scale,
-                       c_log2);
+                       c_log2, mask);
     return hipGetLastError();
 }
 
@@ -336,14 +429,21 @@ hipError_t launch_bwd_typed(const void* q, const void* k, const void* v, const v
 
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int Nq,
-                      int Nk, int d, bool causal, float scale, bool bf16, hipStream_t stream)
+                      int Nk, int d, bool causal, float scale, bool bf16, const MaskArgs* mask,
+                      hipStream_t stream)
 {
     const int BH = B * H;
-#define FA_BWD(T, D)                                                                                   \
-    return causal ? launch_bwd_typed<T, D, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, BH, Nq, Nk, \
-                                                 scale, stream)                                        \
-                  : launch_bwd_typed<T, D, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, BH, Nq, Nk, \
-                                                  scale, stream)
+    const MaskArgs none{-1, -1, nullptr, H};
+#define FA_BWD_M(T, D, C)                                                                              \
+    return mask ? launch_bwd_typed<T, D, C, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, BH, Nq, Nk, \
+                                                  scale, *mask, stream)                                \
+                : launch_bwd_typed<T, D, C, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, BH, Nq, Nk,\
+                                                   scale, none, stream)
+#define FA_BWD(T, D)                \
+    do {                            \
+        if (causal) FA_BWD_M(T, D, true); \
+        FA_BWD_M(T, D, false);      \
+    } while (0)
     if (bf16) {
         if (d == 64) FA_BWD(__bf16, 64);
         FA_BWD(__bf16, 128);
@@ -351,6 +451,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
     if (d == 64) FA_BWD(_Float16, 64);
     FA_BWD(_Float16, 128);
 #undef FA_BWD
+#undef FA_BWD_M
 }
 
 }  // namespace fa

@@ -69,9 +69,10 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           int Nq, int Nk, int d, bool causal, float scale, void* workspace, hipStream_t stream);
 
 // Enqueues the backward pass (delta, dK/dV and dQ kernels); arguments were
-// validated by the caller.
+// validated by the caller. mask: padding / window masks, or nullptr.
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int Nq,
-                      int Nk, int d, bool causal, float scale, bool bf16, hipStream_t stream);
+                      int Nk, int d, bool causal, float scale, bool bf16, const MaskArgs* mask,
+                      hipStream_t stream);
 
 }  // namespace fa
