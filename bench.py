@@ -141,13 +141,12 @@ def power_and_clock(step, seconds=2.0):
     return result if "socket_power_w" in result else None
 
 
-def backward_leg(reps=10):
-    """The backward pass at the headline shape, after the timed region: fa.bwd (its three kernels)
-    back to back between HIP events, non-causal and causal, with TFLOP/s in the FlashAttention-2
-    convention (2.5x the forward's 4*B*H*N*N*d, halved for causal)."""
+def time_backward(cfg, reps=10):
+    """fa.bwd (its three kernels) back to back between HIP events on one configuration,
+    non-causal and causal, with TFLOP/s in the FlashAttention-2 convention (2.5x the forward's
+    4*B*H*N*N*d, halved for causal; d is the tensors' head dim)."""
     import torch
     import tiled_attention_forward_fwd_amd as fa
-    cfg = HEADLINE
     dev = torch.device("cuda:0")
     _, _, _, qd, kd, vd = make_inputs(cfg, dev)
     from fa_inputs import make_qkv
@@ -170,8 +169,16 @@ def backward_leg(reps=10):
         res["causal" if causal else "noncausal"] = {
             "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
             "frac_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    return res
+
+
+def backward_leg(reps=10):
+    """The backward pass after the timed region: the headline shape, and the same shape at head
+    dim 96 (the d = 128 kernels run padded; FLOPs counted at d = 96)."""
+    res = time_backward(HEADLINE, reps)
     res["what"] = ("fa.bwd (delta, dK/dV, dQ kernels) at B=4 H=16 N=4096 d=128 bf16, FLOPs = 2.5x "
                    "the forward's; the kernels execute 1.4x that (S and dP are recomputed for dQ)")
+    res["d96"] = time_backward(dict(HEADLINE, d=96), reps)
     return res
 
 

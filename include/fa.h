@@ -41,7 +41,7 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1, /* NULL/misaligned/overlapping pointer, bad size, dtype or scale */
     FA_ERR_UNSUPPORTED = 2, /* well-formed but not built: a head dim that is not a multiple of
-                               8 from 8 to 128 (backward: not 64 or 128) */
+                               8 from 8 to 128 (fp32 inputs: not 64 or 128) */
     FA_ERR_HIP = 3          /* the HIP runtime reported an error (see fa_status_string) */
 } fa_status;
 
@@ -218,9 +218,10 @@ int fa_fwd_f32(const float *q, const float *k, const float *v, float *o, float *
  *   delta            : device, [B, H, N] fp32, 16-byte aligned, owned by the
  *                      caller: scratch that receives D (libfa allocates
  *                      nothing).
- * Other arguments as fa_fwd, except that d must be 64 or 128. Three kernels
- * are enqueued on `stream`; nothing uses atomics, so results are
- * deterministic.
+ * Other arguments as fa_fwd, d included (a multiple of 8 from 8 to 128;
+ * below 128 other than 64 the d = 64 or 128 kernels run with the missing
+ * dims held at zero). Three kernels are enqueued on `stream`; nothing uses
+ * atomics, so results are deterministic.
  */
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
            const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H, int N, int d,

@@ -381,9 +381,13 @@ def test_plan_other_head_dims(lib, d):
     assert fa.fa_split_workspace_bytes(1, 4, 3, d, 5) == 5 * 4 * 3 * (D + 1) * 4
 
 
-def test_backward_keeps_head_dims_64_and_128(lib):
+@pytest.mark.parametrize("d", [0, 4, 100, 127, 136, 256])
+def test_backward_rejects_head_dims_it_does_not_build(lib, d):
+    # the backward takes the forward's head dims: multiples of 8 from 8 to 128
     args = [P[0], P[1], P[2], P[3], P[4], 0x60000, 0x70000, 0x80000, 0x90000, 0xa0000]
-    assert fa.fa_bwd(*args, 1, 1, 16, 96, 0, 0.1, fa.FA_DTYPE_BF16, None) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd(*args, 1, 1, 16, d, 0, 0.1, fa.FA_DTYPE_BF16, None) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_masked(*args, 1, 1, 16, 16, d, 1, 4, -1, None, 0.1, fa.FA_DTYPE_F16,
+                            None) == fa.FA_ERR_UNSUPPORTED
 
 
 def test_fa_fwd_f32_rejects_before_any_hip_call(lib):
@@ -416,5 +420,5 @@ def test_fa_bwd_masked_rejects_before_any_hip_call(lib):
                                 a["wr"], a["kl"], a["scale"], fa.FA_DTYPE_BF16, None)
     for kw, st in [(dict(wl=-2), fa.FA_ERR_INVALID_ARG), (dict(kl=0xB00002), fa.FA_ERR_INVALID_ARG),
                    (dict(kl=p[7] + 16), fa.FA_ERR_INVALID_ARG),   # key_lens inside dk
-                   (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(Nk=0), fa.FA_ERR_INVALID_ARG)]:
+                   (dict(d=100), fa.FA_ERR_UNSUPPORTED), (dict(Nk=0), fa.FA_ERR_INVALID_ARG)]:
         assert run(**kw) == st, kw

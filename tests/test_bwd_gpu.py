@@ -158,3 +158,72 @@ def test_backward_masks_match_oracle(case):
     print(f"[bwd] masks {case[:7]} wl={wl} wr={wr} rel err dq={errs[0]:.2e} dk={errs[1]:.2e} "
           f"dv={errs[2]:.2e}", flush=True)
     assert max(errs) <= TOL[q.dtype]
+
+
+# head dims other than 64 and 128 (a multiple of 8 up to 128): the d = 64 or
+# d = 128 kernels with the missing dims held at zero
+HDIM_CASES = [(2, 2, 300, 300, 8, "bf16"), (1, 3, 257, 257, 32, "fp16"), (2, 2, 333, 333, 40, "bf16"),
+              (1, 2, 300, 300, 72, "fp16"), (2, 2, 500, 500, 96, "bf16"), (1, 2, 129, 129, 120, "fp16"),
+              (2, 2, 300, 1000, 96, "bf16"), (1, 2, 700, 129, 48, "fp16")]
+
+
+@pytest.mark.parametrize("case", HDIM_CASES, ids=[f"q{c[2]}k{c[3]}d{c[4]}{c[5]}" for c in HDIM_CASES])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_head_dims_match_oracle(case, causal):
+    B, H, Nq, Nk, d, dtype = case
+    print(f"[case] bwd head dim {case} causal={causal}", flush=True)
+    check_bwd(B, H, Nq, d, dtype, causal, 580 + d, Nk=None if Nk == Nq else Nk)
+
+
+@pytest.mark.parametrize("d,D", [(96, 128), (40, 64), (120, 128), (8, 64)])
+def test_backward_head_dim_equals_the_native_kernel_on_zero_padded_inputs(d, D):
+    # same tiles, same LDS contents and the same MFMA sums: bit for bit, and
+    # the native kernel's gradients past d are zero
+    B, H, N = 2, 3, 333
+    q, k, v = (t.cuda() for t in make_qkv(B, H, N, d, "bf16", 600 + d))
+    dout = make_qkv(B, H, N, d, "bf16", 607 + d)[0].cuda()
+    pad = lambda t: torch.nn.functional.pad(t, (0, D - d)).contiguous()
+    sc = fa.default_scale(d)  # the padded calls take d's scale, not D's
+    for causal in (False, True):
+        o, lse = fa.fwd(q, k, v, causal=causal, scale=sc, splits=1)
+        g = fa.bwd(q, k, v, o, lse, dout, causal=causal, scale=sc)
+        o_n, lse_n = fa.fwd(pad(q), pad(k), pad(v), causal=causal, scale=sc, splits=1)
+        g_n = fa.bwd(pad(q), pad(k), pad(v), o_n, lse_n, pad(dout), causal=causal, scale=sc)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv"), g, g_n):
+            assert torch.equal(a, b[..., :d]), (d, causal, name)
+            assert torch.all(b[..., d:] == 0), (d, causal, name)
+
+
+def test_backward_head_dim_masks_and_guard_regions():
+    # masks at d = 96 through the C entry point, each output followed by a NaN
+    # guard that no store may touch
+    B, H, Nq, Nk, d = 2, 2, 600, 600, 96
+    q = make_qkv(B, H, Nq, d, "fp16", 620)[0]
+    _, k, v = make_qkv(B, H, Nk, d, "fp16", 621)
+    dout = make_qkv(B, H, Nq, d, "fp16", 622)[0]
+    scale = fa.default_scale(d)
+    mk = dict(window_left=50, window_right=-1, key_lens=[600, 300])
+    qd, kd, vd, dd = (t.cuda() for t in (q, k, v, dout))
+    o, lse = fa.fwd(qd, kd, vd, causal=True, splits=1, **mk)
+    outs = []
+    for t in (qd, kd, vd):
+        base = torch.full((t.numel() + 4096,), float("nan"), dtype=t.dtype, device="cuda")
+        outs.append((base, base[:t.numel()].view(t.shape)))
+    delta = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+    kl = torch.tensor(mk["key_lens"], dtype=torch.int32, device="cuda")
+    rc = fa.fa_bwd_masked(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), dd.data_ptr(),
+                          lse.data_ptr(), outs[0][1].data_ptr(), outs[1][1].data_ptr(), outs[2][1].data_ptr(),
+                          delta.data_ptr(), B, H, Nq, Nk, d, 1, 50, -1, kl.data_ptr(), scale,
+                          fa.dtype_code(q.dtype), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == fa.FA_OK, fa.fa_status_string(rc)
+    ref = oracle.attention_bwd(q, k, v, dout, True, scale, **mk)
+    for name, (base, g), r in zip(("dq", "dk", "dv"), outs, ref):
+        assert torch.isnan(base[g.numel():]).all(), f"{name}: write past the output"
+        a = g.cpu().float().numpy().astype(np.float64)
+        err = float(np.abs(a - r).max() / max(float(np.abs(r).max()), 1e-3))
+        print(f"[bwd] d96 masks {name} rel err {err:.2e}", flush=True)
+        assert err <= TOL[torch.float16]
+    # keys past a batch's length get zero gradients
+    assert torch.all(outs[1][1][1, :, 300:] == 0) and torch.all(outs[2][1][1, :, 300:] == 0)

@@ -9,8 +9,8 @@ the library is missing or fails to load, the functions here raise.
     dq, dk, dv = bwd(q, k, v, o, lse, dout, causal=False, scale=None)
 
 q is ``[B, H, Nq, d]`` and k, v are ``[B, H, Nk, d]``; Nq may differ from Nk
-(a causal row i sees keys j <= i). d is any multiple of 8 up to 128 (the
-backward: 64 or 128); float16, bfloat16, or float32 (forward only). ``fwd``
+(a causal row i sees keys j <= i). d is any multiple of 8 up to 128 (fp32:
+64 or 128); float16, bfloat16, or float32 (forward only). ``fwd``
 also takes padding lengths and sliding windows (``key_lens``,
 ``window_left``, ``window_right``) and picks the split-key launch for small
 grids (``splits``). The C entry points are exposed under their own names

@@ -169,7 +169,6 @@ int bwd_checked(const void* q, const void* k, const void* v, const void* o, cons
     if (!aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
     const int rc = check_problem(B, H, Nq, Nk, d, causal, dtype);
     if (rc != FA_OK) return rc;
-    if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "the backward pass takes head dim 64 or 128");
     if (!(scale > 0.f) || !isfinite(scale))
         return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
     // query side: q, o, dout, dq [Nq rows], lse and delta [Nq]; key side: k, v, dk, dv [Nk rows]

@@ -2,8 +2,9 @@
 // kernels. The forward launches are split over four sources by variant
 // (fa_fwd_kernel.hip: no masks, head dim 64 or 128; fa_fwd_masked.hip: masks;
 // fa_fwd_hdim.hip and fa_fwd_hdim_masked.hip: other head dims), all built
-// from the kernel template in fa_fwd_kernel.h; fa_bwd_kernel.hip holds the
-// backward pass. Not installed; the public header is include/fa.h.
+// from the kernel template in fa_fwd_kernel.h. The backward pass is in
+// fa_bwd_kernel.h, launched from fa_bwd_kernel.hip (head dim 64 or 128) and
+// fa_bwd_hdim.hip (other head dims). Not installed; the public header is include/fa.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -69,10 +70,15 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           int Nq, int Nk, int d, bool causal, float scale, void* workspace, hipStream_t stream);
 
 // Enqueues the backward pass (delta, dK/dV and dQ kernels); arguments were
-// validated by the caller. mask: padding / window masks, or nullptr.
+// validated by the caller. mask: padding / window masks, or nullptr. d: 64 or
+// 128, or a multiple of 8 below 128 (launch_bwd_hdim, run padded).
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int Nq,
                       int Nk, int d, bool causal, float scale, bool bf16, const MaskArgs* mask,
                       hipStream_t stream);
+hipError_t launch_bwd_hdim(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int Nq,
+                           int Nk, int d, bool causal, float scale, bool bf16, const MaskArgs* mask,
+                           hipStream_t stream);
 
 }  // namespace fa
