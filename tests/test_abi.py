@@ -161,6 +161,13 @@ def test_plan_picks_workgroup_shape(lib):
     assert (causal["block_m"], causal["threads"], causal["workgroups"]) == (128, 256, 2048)
     small = fa.fa_plan(2, 4, 1000, 64, 0, fa.FA_DTYPE_F16)
     assert (small["block_m"], small["threads"], small["workgroups"]) == (128, 256, 64)
+    # at most 128 query rows: 128-row workgroups whatever the grid, so that
+    # no workgroup holds a CU's waves for one block of rows
+    for nq in (1, 16, 128):
+        few = fa.fa_plan_qk(64, 32, nq, 8192, 128, 0, fa.FA_DTYPE_BF16)
+        assert (few["block_m"], few["threads"], few["workgroups"]) == (128, 256, 64 * 32)
+    more = fa.fa_plan_qk(64, 32, 129, 8192, 128, 0, fa.FA_DTYPE_BF16)
+    assert (more["block_m"], more["threads"], more["workgroups"]) == (256, 512, 64 * 32)
 
 
 # ---- Nq != Nk (fa_fwd_qk, fa_tile_counts_qk, fa_plan_qk)
@@ -353,15 +360,28 @@ def test_fa_fwd_split_masked_rejects_before_any_hip_call(lib):
 
 
 def test_split_count_suggestion(lib):
-    # decode grids get 8 chunks, a full grid gets none, short keys stay direct
-    assert fa.fa_split_count(1, 32, 1, 16384, 128, 0) == 8
-    assert fa.fa_split_count(4, 32, 1, 16384, 128, 0) == 8
+    # decode grids are split to about 512 workgroups, a full grid is not, short
+    # key sequences stay direct
+    assert fa.fa_split_count(1, 32, 1, 16384, 128, 0) == 16
+    assert fa.fa_split_count(1, 32, 1, 1024, 128, 0) == 8     # chunks of two key tiles
+    assert fa.fa_split_count(4, 32, 1, 2048, 128, 0) == 4
+    assert fa.fa_split_count(4, 32, 1, 16384, 128, 0) == 8    # long caches: 8 chunks
+    assert fa.fa_split_count(16, 32, 1, 2048, 128, 0) == 1    # a large grid of short caches
+    assert fa.fa_split_count(16, 32, 1, 8192, 128, 0) == 2
+    assert fa.fa_split_count(2, 32, 128, 8192, 128, 0) == 4   # full query tiles: about 256 workgroups
+    assert fa.fa_split_count(2, 32, 128, 1024, 128, 0) == 2   # ... with chunks of 8 key tiles
+    assert fa.fa_split_count(8, 32, 128, 8192, 128, 0) == 1
     assert fa.fa_split_count(4, 16, 4096, 4096, 128, 0) == 1
     assert fa.fa_split_count(1, 1, 1, 512, 64, 0) == 1
+    assert fa.fa_split_count(1, 1, 1, 960, 64, 0) == 1       # under 16 key tiles
     assert fa.fa_split_count(0, 1, 1, 512, 64, 0) == 0  # invalid
-    for B, H, Nq, Nk in [(1, 1, 1, 100000), (2, 8, 300, 5000), (16, 32, 1, 2048), (1, 64, 129, 65536)]:
+    for B, H, Nq, Nk in [(1, 1, 1, 100000), (2, 8, 300, 5000), (16, 32, 1, 2048), (1, 64, 129, 65536),
+                         (1, 1, 32, 1024), (3, 5, 33, 7777), (64, 32, 1, 8192)]:
         s = fa.fa_split_count(B, H, Nq, Nk, 128, 0)
-        assert 1 <= s <= max(1, -(-Nk // 64) // 16)
+        n_kt = -(-Nk // 64)
+        assert 1 <= s <= max(1, n_kt // 2)
+        if min(Nq, 128) > 32:
+            assert s <= max(1, n_kt // 8)
 
 
 # ---- head dims other than 64 and 128 (run padded by the d = 64 / 128 kernels)

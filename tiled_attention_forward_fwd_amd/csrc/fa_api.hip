@@ -374,22 +374,36 @@ int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* l
 int fa_split_count(int B, int H, int Nq, int Nk, int d, int causal)
 {
     if (check_problem(B, H, Nq, Nk, d, causal, FA_DTYPE_BF16) != FA_OK) return 0;
-    // Measured on MI355X for one to 128 query rows against 4096 to 65536
-    // keys: the best split gives the grid about 256 to 1024 workgroups and
-    // every chunk at least 16 key tiles (a shorter chunk spends too much of
-    // its time filling its pipeline). Short key sequences stay on the direct
-    // path, which needs no merge. The smallest grids take at least 8 chunks:
-    // equal cache lengths run as fast with 8 as with 2 to 4, and caches of
-    // different lengths (padding) need the extra chunks to balance.
+    // Measured on MI355X (bf16, d = 64 and 128, B*H from 32 to 2048, 1 to
+    // 128 query rows, 512 to 16384 keys; every split count timed).
+    //  * Under 16 key tiles the merge costs more than the split gains.
+    //  * Up to 32 query rows a workgroup has one computing wave and streams
+    //    K/V: about 512 workgroups keep HBM busy, and chunks as short as two
+    //    key tiles still pay. Small grids with long caches take 8 chunks,
+    //    which also balances caches of different lengths (padding); grids
+    //    past 128 tiles take 2 chunks from 64 key tiles on.
+    //  * With more query rows every chunk writes a partial of that many rows
+    //    and the workgroups compute more: about 256 workgroups, chunks of at
+    //    least 8 key tiles.
     const int64_t rows = fa::split_rows_per_tile();
+    const int64_t rq = Nq < rows ? Nq : rows;
     const int64_t wgs = (int64_t)B * H * (((int64_t)Nq + rows - 1) / rows);
     const int64_t n_kt = ((int64_t)Nk + 63) / 64;
-    int64_t s = (256 + wgs - 1) / wgs;
-    if (wgs <= 128 && s < 8)
-        s = 8;
-    else if (wgs < 512 && s < 4)
-        s = 4;
-    if (s > n_kt / 16) s = n_kt / 16;
+    if (n_kt < 16) return 1;
+    int64_t s;
+    if (rq <= 32) {
+        if (wgs <= 128) {
+            s = (512 + wgs - 1) / wgs;
+            const int64_t long_cache = n_kt / 16 < 8 ? n_kt / 16 : 8;
+            if (s < long_cache) s = long_cache;
+        } else {
+            s = n_kt >= 64 ? 2 : 1;
+        }
+        if (s > n_kt / 2) s = n_kt / 2;
+    } else {
+        s = (256 + wgs - 1) / wgs;
+        if (s > n_kt / 8) s = n_kt / 8;
+    }
     return (int)(s < 1 ? 1 : s);
 }
 

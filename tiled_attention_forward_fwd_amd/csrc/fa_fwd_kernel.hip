@@ -11,14 +11,17 @@ namespace fa {
 // and, the chip being power-limited under this load, raises the clock it
 // holds; they are used for non-causal problems whose grid still gives every
 // CU a workgroup. Causal problems keep 128-row workgroups (less work above
-// the diagonal), as do small grids.
+// the diagonal), as do small grids and problems of at most 128 query rows: a
+// 256-row workgroup would leave at least half its waves without rows while
+// holding a whole CU's waves (one workgroup per CU instead of two, so half
+// the K/V copies in flight; decode-like shapes, measured 25-40% slower).
 Shape pick_shape(int B, int H, int n_queries, int d, bool causal)
 {
     (void)d;
     Shape sh;
     sh.waves = 4;
     sh.rows_per_wave = 32;
-    if (!causal) {
+    if (!causal && n_queries > 128) {
         const int64_t wg256 = (int64_t)B * H * ((n_queries + 255) / 256);
         if (wg256 >= 256) sh.waves = 8;
     }
