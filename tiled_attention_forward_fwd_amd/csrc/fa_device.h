@@ -239,42 +239,92 @@ __device__ __forceinline__ float pair_sum<_Float16>(float acc, float, float, _Fl
     return __builtin_amdgcn_fdot2(v, one, acc, false);
 }
 
+// exp2 / row-sum / convert of the score pair (e, e + 1) of one query row (e
+// even; element e of the tile is accumulator block e / 16, row e % 16), into
+// the P^T operand vector that holds it.
+template <typename T, int KB, int KT>
+__device__ __forceinline__ void exp_pair(const f32x16 (&s)[KB], int e, float m, float c_log2,
+                                         typename Mma<T>::vec8 (&p)[KT], float& acc)
+{
+    const int eb = e >> 4, r = e & 15;  // r even: r and r + 1 share a P vector
+    const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[eb][r], c_log2, -m));
+    const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[eb][r + 1], c_log2, -m));
+    const T h0 = to_elem<T>(x0), h1 = to_elem<T>(x1);
+    p[eb * 2 + (r >> 3)][r & 7] = h0;
+    p[eb * 2 + (r >> 3)][(r & 7) + 1] = h1;
+    acc = pair_sum<T>(acc, x0, x1, h0, h1);
+}
+
+// Pairs [E0/2, E1/2) of a tile's scores spread evenly over N_MFMA slots;
+// slot i gets the pairs [i*n/N_MFMA, (i+1)*n/N_MFMA).
+// BS (block sums): the row sum goes into one partial sum per 32-key block
+// (acc[e / 16]), each added in element order, and a tile's row sum is
+// acc[0] + acc[1] + ...; otherwise every element goes into acc[0] in order.
+template <typename T, int KB, int KT, int E0, int E1, int N_MFMA, bool BS>
+__device__ __forceinline__ void exp_slot(int i, const f32x16 (&s)[KB], float m, float c_log2,
+                                         typename Mma<T>::vec8 (&p)[KT], float (&acc)[KB])
+{
+    constexpr int n = (E1 - E0) / 2;
+    static_assert(E0 % 2 == 0 && E1 % 2 == 0, "pairs");
+#pragma unroll
+    for (int q = i * n / N_MFMA; q < (i + 1) * n / N_MFMA; ++q)
+        exp_pair<T, KB, KT>(s, E0 + 2 * q, m, c_log2, p, acc[BS ? (E0 + 2 * q) >> 4 : 0]);
+}
+
+template <int KB>
+__device__ __forceinline__ float block_sums(const float (&acc)[KB])
+{
+    float r = acc[0];
+#pragma unroll
+    for (int kb = 1; kb < KB; ++kb) r += acc[kb];
+    return r;
+}
+
 // The scores of the next tile fused with the exp2 work of this one: after
 // each score MFMA come the exp2 / row-sum / convert of a few elements of the
-// current tile, so the vector units work while the matrix core runs instead
-// of after it (the two streams are independent). One 32-row block (QB = 1).
-template <typename T, int D, int KB, int DS, int KT>
+// current tile (those in [E0, E1)), so the vector units work while the
+// matrix core runs instead of after it (the two streams are independent).
+// One 32-row block (QB = 1).
+template <typename T, int D, int KB, int DS, int KT, int E0, int E1, bool BS>
 __device__ __forceinline__ void scores_with_exp(f32x16 (&sn)[1][KB], const uint16_t* __restrict__ ks,
                                                 const typename Mma<T>::vec8 (&qf)[1][DS], int l32, int hh,
                                                 const f32x16 (&sc)[1][KB], float m, float c_log2,
                                                 typename Mma<T>::vec8 (&p)[1][KT], float (&rs)[1])
 {
     typedef typename Mma<T>::vec8 vec8;
-    constexpr int n_mfma = KB * DS, n_el = KB * 16, per = n_el / n_mfma;
-    static_assert(per * n_mfma == n_el && per % 2 == 0, "exp work per MFMA");
+    constexpr int n_mfma = KB * DS;
+    constexpr int b0 = BS ? E0 >> 4 : 0, b1 = BS ? (E1 + 15) >> 4 : 1;  // partial sums in use
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) sn[0][kb] = (f32x16){};
-    float acc = 0.f;
+    float acc[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) acc[kb] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const vec8 a = k_operand<vec8, D>(ks, kb * 32 + l32, ds, hh);
             sn[0][kb] = Mma<T>::run(a, qf[0][ds], sn[0][kb]);
-            const int i = ds * KB + kb;
-#pragma unroll
-            for (int e = i * per; e < (i + 1) * per; e += 2) {
-                const int eb = e >> 4, r = e & 15;  // r even: r and r + 1 share a P vector
-                const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][eb][r], c_log2, -m));
-                const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][eb][r + 1], c_log2, -m));
-                const T h0 = to_elem<T>(x0), h1 = to_elem<T>(x1);
-                p[0][eb * 2 + (r >> 3)][r & 7] = h0;
-                p[0][eb * 2 + (r >> 3)][(r & 7) + 1] = h1;
-                acc = pair_sum<T>(acc, x0, x1, h0, h1);
-            }
+            exp_slot<T, KB, KT, E0, E1, n_mfma, BS>(ds * KB + kb, sc[0], m, c_log2, p[0], acc);
         }
     }
-    rs[0] = acc;
+    float r = acc[b0];
+#pragma unroll
+    for (int kb = b0 + 1; kb < b1; ++kb) r += acc[kb];
+    rs[0] = r;
+}
+
+// exp2 work on the elements [E0, E1) of one tile without MFMAs between (a
+// range within one 32-key block).
+template <typename T, int KB, int KT, int E0, int E1>
+__device__ __forceinline__ float exp_range(const f32x16 (&s)[KB], float m, float c_log2,
+                                           typename Mma<T>::vec8 (&p)[KT])
+{
+    static_assert(E0 >> 4 == (E1 - 1) >> 4, "one block");
+    float acc = 0.f;
+#pragma unroll
+    for (int e = E0; e < E1; e += 2) exp_pair<T, KB, KT>(s, e, m, c_log2, p, acc);
+    return acc;
 }
 
 // Diagonal / ragged tiles: keys past N, and for causal attention keys after
@@ -322,26 +372,21 @@ __device__ __forceinline__ float row_max_log2(const f32x16 (&s)[KB], float c_log
 
 // P = 2^(s * c - m) of one tile, rounded to the input type after the fp32
 // value has been added to the lane's partial row sum (Round 4, "The P cast").
-template <typename T, int QB, int KB, int KT>
+template <typename T, int QB, int KB, int KT, bool BS>
 __device__ __forceinline__ void exp_tile(const f32x16 (&s)[QB][KB], const float (&m_run)[QB], float c_log2,
                                          typename Mma<T>::vec8 (&p)[QB][KT], float (&rs)[QB])
 {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        float acc = 0.f;
+        float acc[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
+            acc[kb] = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r], c_log2, -m_run[qb]));
-                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r + 1], c_log2, -m_run[qb]));
-                const T h0 = to_elem<T>(e0), h1 = to_elem<T>(e1);
-                p[qb][kb * 2 + (r >> 3)][r & 7] = h0;
-                p[qb][kb * 2 + (r >> 3)][(r & 7) + 1] = h1;
-                acc = pair_sum<T>(acc, e0, e1, h0, h1);
-            }
+            for (int r = 0; r < 16; r += 2)
+                exp_pair<T, KB, KT>(s[qb], kb * 16 + r, m_run[qb], c_log2, p[qb], acc[BS ? kb : 0]);
         }
-        rs[qb] = acc;
+        rs[qb] = BS ? block_sums<KB>(acc) : acc[0];
     }
 }
 
@@ -359,7 +404,7 @@ __device__ __forceinline__ void exp_tile(const f32x16 (&s)[QB][KB], const float 
 // online softmax). The branch is wave-uniform.
 constexpr float kLaneSumBound = 4096.0f;
 
-template <typename T, int QB, int KB, int DB, int KT>
+template <typename T, int QB, int KB, int DB, int KT, bool BS>
 __device__ __forceinline__ void softmax_finish(const f32x16 (&s)[QB][KB], f32x16 (&o)[QB][DB],
                                                float (&m_run)[QB], float (&l_run)[QB], float c_log2,
                                                typename Mma<T>::vec8 (&p)[QB][KT], float (&rs)[QB])
@@ -378,20 +423,20 @@ __device__ __forceinline__ void softmax_finish(const f32x16 (&s)[QB][KB], f32x16
 #pragma unroll
             for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
         }
-        exp_tile<T, QB, KB, KT>(s, m_run, c_log2, p, rs);
+        exp_tile<T, QB, KB, KT, BS>(s, m_run, c_log2, p, rs);
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
 }
 
-template <typename T, int QB, int KB, int DB, int KT>
+template <typename T, int QB, int KB, int DB, int KT, bool BS>
 __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[QB][KB], f32x16 (&o)[QB][DB],
                                              float (&m_run)[QB], float (&l_run)[QB], float c_log2,
                                              typename Mma<T>::vec8 (&p)[QB][KT])
 {
     float rs[QB];
-    exp_tile<T, QB, KB, KT>(s, m_run, c_log2, p, rs);
-    softmax_finish<T, QB, KB, DB, KT>(s, o, m_run, l_run, c_log2, p, rs);
+    exp_tile<T, QB, KB, KT, BS>(s, m_run, c_log2, p, rs);
+    softmax_finish<T, QB, KB, DB, KT, BS>(s, o, m_run, l_run, c_log2, p, rs);
 }
 
 // O^T += V^T P^T (operand layout at vt_operand). Each V operand feeds QB
@@ -413,13 +458,39 @@ __device__ __forceinline__ void pv_tile(const typename Mma<T>::vec8 (&p)[QB][KT]
     }
 }
 
-template <typename T, int D, int QB, int KB, int DB, int KT>
+// O^T += V^T P^T of this tile with the exp2 work of the elements [E0, E1)
+// of the next tile's scores sn between the MFMAs (into pn, row sum in rs).
+template <typename T, int D, int DB, int KT, int KB, int E0, int E1>
+__device__ __forceinline__ void pv_with_exp(const typename Mma<T>::vec8 (&p)[1][KT],
+                                            const uint16_t* __restrict__ vts, f32x16 (&o)[1][DB], int lane, int hh,
+                                            const f32x16 (&sn)[1][KB], float m, float c_log2,
+                                            typename Mma<T>::vec8 (&pn)[1][KT], float& rs)
+{
+    typedef typename Mma<T>::vec8 vec8;
+    static_assert(E0 >> 4 == (E1 - 1) >> 4, "one block");
+    constexpr int n_mfma = KT * DB;
+    float acc[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) acc[kb] = 0.f;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const vec8 a = vt_operand<vec8, D>(vts, t, db, lane, hh);
+            o[0][db] = Mma<T>::run(a, p[0][t], o[0][db]);
+            exp_slot<T, KB, KT, E0, E1, n_mfma, true>(t * DB + db, sn[0], m, c_log2, pn[0], acc);
+        }
+    }
+    rs = acc[E0 >> 4];
+}
+
+template <typename T, int D, int QB, int KB, int DB, int KT, bool BS>
 __device__ __forceinline__ void softmax_pv(const f32x16 (&s)[QB][KB], const uint16_t* __restrict__ vts,
                                            f32x16 (&o)[QB][DB], float (&m_run)[QB],
                                            float (&l_run)[QB], float c_log2, int lane, int hh)
 {
     typename Mma<T>::vec8 p[QB][KT];
-    softmax_tile<T, QB, KB, DB, KT>(s, o, m_run, l_run, c_log2, p);
+    softmax_tile<T, QB, KB, DB, KT, BS>(s, o, m_run, l_run, c_log2, p);
     pv_tile<T, D, QB, DB, KT>(p, vts, o, lane, hh);
 }
 
@@ -459,6 +530,20 @@ __device__ __forceinline__ void order_pv_block()
 #pragma unroll
     for (int i = 0; i < lead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
 }
+
+// Keeps the computation of x where it is written: an empty asm statement that
+// takes x in registers and may change it. Without it the compiler sinks the
+// exp work of a mixed block past the end of the block (into the next tile's
+// step), where it no longer runs between MFMAs.
+template <typename V>
+__device__ __forceinline__ void pin_regs(V& x)
+{
+    u32x4 w = __builtin_bit_cast(u32x4, x);
+    asm volatile("" : "+v"(w));
+    x = __builtin_bit_cast(V, w);
+}
+
+__device__ __forceinline__ void pin_reg(float& x) { asm volatile("" : "+v"(x)); }
 
 // Q fragments: B operand of S^T = K Q^T, query qrow[qb] = row0 + 32*qb +
 // (lane % 32), dims 16*ds + 8*hh + [0, 8). Rows past N are zero (their

@@ -330,6 +330,22 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     // vector work between them runs meanwhile. Measured +2.5% for the 8-wave
     // shapes and +3% for 4-wave d=128; 4-wave d=64 ran 1-2% slower with it.
     constexpr bool kPrioMixed = WAVES == 8 || D == 128;
+    // d=64 without masks splits the exp work of a tile in two halves by its
+    // 32-key blocks: the second block's goes between the next tile's score
+    // MFMAs as above, the first block's between the MFMAs of the previous
+    // tile's P.V, so both MFMA blocks carry vector work. The lazy-max test
+    // still sees the whole tile before any of its P enters P.V. Measured +3%
+    // at B4 H16 N4096 d=64 non-causal, causal unchanged; at d=128 the same
+    // split ran 5% slower in every instruction order tried. (With masks a
+    // wave can start at a tile whose scores it never computed, which this
+    // order would leave unmasked.)
+    constexpr bool kSplitExp = kFuseExp && !MASKS && D == 64;
+    // Row sums of a tile: d=64 adds one partial sum per 32-key block, in
+    // element order, and then the blocks (the split above produces them
+    // apart); d=128 adds all 64 scores in element order. Every path of a
+    // kernel (fused or not, first tile, rescaled tile) uses the same order, so
+    // the masked and unmasked kernels of one head dim agree bit for bit.
+    constexpr bool kBS = D == 64;
 
     int qrow[QB];
     vec8 qf[QB][C::DS];
@@ -432,6 +448,10 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     };
 
     f32x16 sa[QB][C::KB], sb[QB][C::KB];
+    // kSplitExp: P of the tile whose scores are in sa / sb (first block
+    // filled one step ahead) and the first block's partial row sum
+    vec8 pa[QB][C::KT], pb[QB][C::KT];
+    float ra = 0.f, rb = 0.f;
     if (MASKS) {
         // a wave's extra leading tile is masked without its scores having been
         // computed: give the registers a defined value
@@ -452,34 +472,72 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
         if (jb + 1 < je) issue(kbuf(jb + 1), krs, (jb + 1) * C::BN);
         stage_barrier();
         // every wave processes an unmasked tile of a direct launch
-        if ((!SPLIT && (!MASKS || (jb >= u_lo && jb < u_hi))) || wave_sees(jb))
+        if ((!SPLIT && (!MASKS || (jb >= u_lo && jb < u_hi))) || wave_sees(jb)) {
             scores<T, D, QB, C::KB, C::DS>(sa, kbuf(jb), qf, l32, hh);
+            if constexpr (kSplitExp) {
+                if (jb >= u_hi) apply_mask(sa[0], jb, 0);
+                ra = exp_range<T, C::KB, C::KT, 0, 16>(sa[0], m_run[0], c_log2, pa[0]);
+            }
+        }
         stage_barrier();  // K_jb's buffer is refilled in the first iteration
     }
 
     // One tile that has a successor: sc holds the scores of tile j; sn
     // receives those of tile j+1.
-    auto step = [&](auto masked, int j, f32x16 (&sc)[QB][C::KB], f32x16 (&sn)[QB][C::KB]) {
+    auto step = [&](auto masked, int j, f32x16 (&sc)[QB][C::KB], f32x16 (&sn)[QB][C::KB], vec8 (&pc)[QB][C::KT],
+                    vec8 (&pn)[QB][C::KT], float& rc, float& rn) {
         // M: the tile gets the mask; G: per-wave limits apply (masked tiles,
         // and every tile of a split launch)
         constexpr bool M = decltype(masked)::value, G = M || SPLIT;
         if (j + 2 < je) issue(kbuf(j), krs, (j + 2) * C::BN);
         issue(vbuf(j + 1), vrs, (j + 1) * C::BN);
-        if (kFuseExp) {
+        if (kSplitExp) {
+            // sc is masked and its first block's P is in pc (rc): they were
+            // made with the previous tile's P.V (or before the loop)
+            if (!G || wave_sees(j)) {
+                float rs[QB];
+                if (!G || wave_sees(j + 1)) {
+                    if constexpr (kPrioMixed) __builtin_amdgcn_s_setprio(1);
+                    scores_with_exp<T, D, C::KB, C::DS, C::KT, 16, 32, kBS>(sn, kbuf(j + 1), qf, l32, hh, sc,
+                                                                            m_run[0], c_log2, pc, rs);
+                    order_scores_block<D, WAVES, QB>();
+                    pin_regs(pc[0][2]);
+                    pin_regs(pc[0][3]);
+                    pin_reg(rs[0]);
+                    if constexpr (kPrioMixed) __builtin_amdgcn_s_setprio(0);
+                } else {
+                    rs[0] = exp_range<T, C::KB, C::KT, 16, 32>(sc[0], m_run[0], c_log2, pc[0]);
+                }
+                rs[0] = rc + rs[0];
+                softmax_finish<T, QB, C::KB, C::DB, C::KT, kBS>(sc, oacc, m_run, l_run, c_log2, pc, rs);
+                if (!G || wave_sees(j + 1)) {
+                    if (M || j + 1 >= u_hi) apply_mask(sn[0], j + 1, 0);
+                    pv_with_exp<T, D, C::DB, C::KT, C::KB, 0, 16>(pc, vbuf(j), oacc, lane, hh, sn, m_run[0], c_log2,
+                                                                  pn, rn);
+                    order_pv_block<D, WAVES, QB>();
+                    pin_regs(pn[0][0]);
+                    pin_regs(pn[0][1]);
+                    pin_reg(rn);
+                } else {
+                    pv_tile<T, D, QB, C::DB, C::KT>(pc, vbuf(j), oacc, lane, hh);
+                    order_pv_block<D, WAVES, QB>();
+                }
+            }
+        } else if (kFuseExp) {
             if (!G || wave_sees(j)) {
                 if (M) apply_mask(sc[0], j, 0);
                 vec8 p[QB][C::KT];
                 float rs[QB];
                 if (!G || wave_sees(j + 1)) {
                     if constexpr (kPrioMixed) __builtin_amdgcn_s_setprio(1);
-                    scores_with_exp<T, D, C::KB, C::DS, C::KT>(sn, kbuf(j + 1), qf, l32, hh, sc, m_run[0],
-                                                               c_log2, p, rs);
+                    scores_with_exp<T, D, C::KB, C::DS, C::KT, 0, C::KB * 16, kBS>(sn, kbuf(j + 1), qf, l32, hh,
+                                                                                   sc, m_run[0], c_log2, p, rs);
                     order_scores_block<D, WAVES, QB>();
                     if constexpr (kPrioMixed) __builtin_amdgcn_s_setprio(0);
                 } else {
-                    exp_tile<T, QB, C::KB, C::KT>(sc, m_run, c_log2, p, rs);
+                    exp_tile<T, QB, C::KB, C::KT, kBS>(sc, m_run, c_log2, p, rs);
                 }
-                softmax_finish<T, QB, C::KB, C::DB, C::KT>(sc, oacc, m_run, l_run, c_log2, p, rs);
+                softmax_finish<T, QB, C::KB, C::DB, C::KT, kBS>(sc, oacc, m_run, l_run, c_log2, p, rs);
                 pv_tile<T, D, QB, C::DB, C::KT>(p, vbuf(j), oacc, lane, hh);
                 order_pv_block<D, WAVES, QB>();
             }
@@ -492,7 +550,7 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
                     if (M) apply_mask(sc[qb], j, qb);
-                softmax_pv<T, D, QB, C::KB, C::DB, C::KT>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
+                softmax_pv<T, D, QB, C::KB, C::DB, C::KT, kBS>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
                 order_pv_block<D, WAVES, QB>();
             }
         }
@@ -506,55 +564,69 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     // only: the left window edge, one step at a time), then tiles up to u_hi
     // that need no mask, then the masked rest; those loops are unrolled by two
     // so the score registers alternate.
-    auto last_step = [&](auto masked, int j, f32x16 (&sc)[QB][C::KB]) {
+    auto last_step = [&](auto masked, int j, f32x16 (&sc)[QB][C::KB], vec8 (&pc)[QB][C::KT], float rc) {
         constexpr bool M = decltype(masked)::value, G = M || SPLIT;
-        if (!G || wave_sees(j)) {
+        if (kSplitExp) {
+            if (!G || wave_sees(j)) {
+                float rs[QB];
+                rs[0] = rc + exp_range<T, C::KB, C::KT, 16, 32>(sc[0], m_run[0], c_log2, pc[0]);
+                softmax_finish<T, QB, C::KB, C::DB, C::KT, kBS>(sc, oacc, m_run, l_run, c_log2, pc, rs);
+                pv_tile<T, D, QB, C::DB, C::KT>(pc, vbuf(j), oacc, lane, hh);
+                order_pv_block<D, WAVES, QB>();
+            }
+        } else if (!G || wave_sees(j)) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
                 if (M) apply_mask(sc[qb], j, qb);
-            softmax_pv<T, D, QB, C::KB, C::DB, C::KT>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
+            softmax_pv<T, D, QB, C::KB, C::DB, C::KT, kBS>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
             order_pv_block<D, WAVES, QB>();
         }
     };
     auto shift_scores = [&]() {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+        for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
             for (int kb = 0; kb < C::KB; ++kb) sa[qb][kb] = sb[qb][kb];
+            if (kSplitExp) {
+#pragma unroll
+                for (int t = 0; t < C::KT; ++t) pa[qb][t] = pb[qb][t];
+            }
+        }
+        ra = rb;
     };
     const int n_lead = je - 1;
     int j = jb;
     if (MASKS) {
         const int a_end = min(u_lo, n_lead);
         for (; j < a_end; ++j) {
-            step(masked_t(), j, sa, sb);
+            step(masked_t(), j, sa, sb, pa, pb, ra, rb);
             shift_scores();
         }
     }
     const int n_u = min(u_hi, n_lead);
     for (; j + 2 <= n_u; j += 2) {
-        step(unmasked_t(), j, sa, sb);
-        step(unmasked_t(), j + 1, sb, sa);
+        step(unmasked_t(), j, sa, sb, pa, pb, ra, rb);
+        step(unmasked_t(), j + 1, sb, sa, pb, pa, rb, ra);
     }
     if (j < n_u) {
-        step(unmasked_t(), j, sa, sb);
+        step(unmasked_t(), j, sa, sb, pa, pb, ra, rb);
         ++j;
         shift_scores();
     }
     for (; j + 2 <= n_lead; j += 2) {
-        step(masked_t(), j, sa, sb);
-        step(masked_t(), j + 1, sb, sa);
+        step(masked_t(), j, sa, sb, pa, pb, ra, rb);
+        step(masked_t(), j + 1, sb, sa, pb, pa, rb, ra);
     }
     if (j < n_lead) {
-        step(masked_t(), j, sa, sb);
+        step(masked_t(), j, sa, sb, pa, pb, ra, rb);
         ++j;
         shift_scores();
     }
     if (j < je) {
         if (j >= u_lo && j < u_hi)
-            last_step(unmasked_t(), j, sa);
+            last_step(unmasked_t(), j, sa, pa, ra);
         else
-            last_step(masked_t(), j, sa);
+            last_step(masked_t(), j, sa, pa, ra);
     }
 
     if (SPLIT) {
