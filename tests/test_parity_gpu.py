@@ -137,6 +137,24 @@ def test_scores_that_drift_along_the_keys(d, dtype, direction):
         check(q, k, v, causal, label=f"{direction} keys d{d} {dtype}")
 
 
+@pytest.mark.parametrize("B,H", [(1, 4), (8, 16)], ids=["4-wave", "8-wave"])
+def test_max_jumps_in_the_second_key_block(B, H):
+    # d = 64 computes a tile's exponentials in two halves (its two 32-key
+    # blocks, the first one step earlier); keys 40 + 200 i have 6x the norm,
+    # so the running max jumps inside a tile's second block, after the first
+    # block's P was taken against the old max. Both workgroup shapes (the
+    # 8-wave one needs at least 256 workgroups of 256 rows).
+    N = 1100
+    q, k, v = make_qkv(B, H, N, 64, "bf16", 61)
+    k = k.float()
+    k[:, :, 40::200] *= 6.0
+    k = k.to(torch.bfloat16)
+    plan = fa.fa_plan(B, H, N, 64, 0, fa.FA_DTYPE_BF16)
+    assert plan["threads"] == (512 if B * H >= 128 else 256)
+    for causal in (False, True):
+        check(q, k, v, causal, label=f"jumps in the second key block B{B} H{H}")
+
+
 def qk_inputs(B, H, Nq, Nk, d, dtype, seed, q_scale=1.0):
     q = make_qkv(B, H, Nq, d, dtype, seed, q_scale=q_scale)[0]
     _, k, v = make_qkv(B, H, Nk, d, dtype, seed + 1)
