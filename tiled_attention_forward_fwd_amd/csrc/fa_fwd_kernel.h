@@ -324,12 +324,6 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     // (scores_with_exp). The 4-wave d=128 shape keeps them apart in its split,
     // masked and padded variants, which run out of registers fused.
     constexpr bool kFuseExp = QB == 1 && !(D == 128 && WAVES == 4 && (SPLIT || MASKS || PADDED));
-    // While a wave runs that mixed block it gets issue priority over the other
-    // wave of its SIMD, whose next instructions are then mostly P.V MFMAs: the
-    // matrix core keeps taking the mixed block's MFMAs as they come up and the
-    // vector work between them runs meanwhile. Measured +2.5% for the 8-wave
-    // shapes and +3% for 4-wave d=128; 4-wave d=64 ran 1-2% slower with it.
-    constexpr bool kPrioMixed = WAVES == 8 || D == 128;
     // d=64 without masks splits the exp work of a tile in two halves by its
     // 32-key blocks: the second block's goes between the next tile's score
     // MFMAs as above, the first block's between the MFMAs of the previous
@@ -340,6 +334,13 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     // wave can start at a tile whose scores it never computed, which this
     // order would leave unmasked.)
     constexpr bool kSplitExp = kFuseExp && !MASKS && D == 64;
+    // While a wave runs a mixed score/exp block it gets issue priority over the
+    // other wave of its SIMD, whose next instructions are then mostly P.V
+    // MFMAs: the matrix core keeps taking the mixed block's MFMAs as they come
+    // up and the vector work between them runs meanwhile. Measured +2.5% for
+    // the 8-wave shapes, +3% for 4-wave d=128 and +1.5% for 4-wave d=64 with
+    // the split above; 4-wave d=64 without the split ran 1-2% slower with it.
+    constexpr bool kPrioMixed = WAVES == 8 || D == 128 || kSplitExp;
     // Row sums of a tile: d=64 adds one partial sum per 32-key block, in
     // element order, and then the blocks (the split above produces them
     // apart); d=128 adds all 64 scores in element order. Every path of a
