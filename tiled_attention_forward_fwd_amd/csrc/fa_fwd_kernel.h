@@ -492,7 +492,7 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
         constexpr bool M = decltype(masked)::value, G = M || SPLIT;
         if (j + 2 < je) issue(kbuf(j), krs, (j + 2) * C::BN);
         issue(vbuf(j + 1), vrs, (j + 1) * C::BN);
-        if (kSplitExp) {
+        if constexpr (kSplitExp) {
             // sc is masked and its first block's P is in pc (rc): they were
             // made with the previous tile's P.V (or before the loop)
             if (!G || wave_sees(j)) {
@@ -524,7 +524,7 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
                     order_pv_block<D, WAVES, QB>();
                 }
             }
-        } else if (kFuseExp) {
+        } else if constexpr (kFuseExp) {
             if (!G || wave_sees(j)) {
                 if (M) apply_mask(sc[0], j, 0);
                 vec8 p[QB][C::KT];
@@ -567,7 +567,7 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     // so the score registers alternate.
     auto last_step = [&](auto masked, int j, f32x16 (&sc)[QB][C::KB], vec8 (&pc)[QB][C::KT], float rc) {
         constexpr bool M = decltype(masked)::value, G = M || SPLIT;
-        if (kSplitExp) {
+        if constexpr (kSplitExp) {
             if (!G || wave_sees(j)) {
                 float rs[QB];
                 rs[0] = rc + exp_range<T, C::KB, C::KT, 16, 32>(sc[0], m_run[0], c_log2, pc[0]);
@@ -588,7 +588,7 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
         for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
             for (int kb = 0; kb < C::KB; ++kb) sa[qb][kb] = sb[qb][kb];
-            if (kSplitExp) {
+            if constexpr (kSplitExp) {
 #pragma unroll
                 for (int t = 0; t < C::KT; ++t) pa[qb][t] = pb[qb][t];
             }
