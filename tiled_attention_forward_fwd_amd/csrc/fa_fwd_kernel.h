@@ -52,7 +52,11 @@
 //     are in flight meanwhile; one barrier per tile. The last tile runs
 //     without a successor, so no score MFMA is wasted. The copies go through
 //     a buffer descriptor bounded to the head, so the rows of a ragged last
-//     tile past N arrive as zeros (and are masked).
+//     tile past N arrive as zeros (and are masked). A wave raises its issue
+//     priority while it runs that mixed score/exp block, so that the other
+//     wave of its SIMD, then mostly in P.V MFMAs, fills the matrix core
+//     around it. d=64 without masks splits the exp work of a tile by its two
+//     32-key blocks over the score block and the previous tile's P.V block.
 //   * exp2 with the softmax scale and log2(e) folded into one constant
 //     (Round 4, "exp2"); the running max is kept in log2 units. The max is
 //     updated lazily: a tile's P is taken against the running max and the
