@@ -180,6 +180,43 @@ __device__ __forceinline__ void store_outputs(const f32x16 (&oacc)[QB][DB], cons
     }
 }
 
+// Epilogue through LDS: each wave writes its 32 normalised rows to its own
+// LDS region (rows D + 8 elements apart, 16-byte aligned), then reads them
+// back a row per 16 lanes and stores 16 contiguous bytes per lane, so every
+// store instruction writes four whole rows instead of 16 bytes of 32 rows.
+// The caller has passed a barrier after its last LDS read of K and V.
+template <typename T, int D, int DB>
+__device__ __forceinline__ void store_outputs_staged(const f32x16 (&oacc)[1][DB], const float (&m_run)[1],
+                                                     const float (&l_run)[1], const int (&qrow)[1], int row0,
+                                                     int n_rows, T* __restrict__ oh, float* __restrict__ lseh,
+                                                     int hh, int lane, uint16_t* __restrict__ stage)
+{
+    constexpr int RS = D + 8;  // LDS row stride in elements
+    const float l_tot = swap_halves_sum(l_run[0]);
+    const float inv = 1.0f / l_tot;
+    const int l32 = lane & 31;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            T vals[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) vals[t] = to_elem<T>(oacc[0][db][4 * g + t] * inv);
+            *(u32x2*)(stage + l32 * RS + db * 32 + 8 * g + 4 * hh) = __builtin_bit_cast(u32x2, vals);
+        }
+    }
+    constexpr int CPR = D / 8;             // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;          // rows per read instruction
+    const int rr = lane / CPR, cc = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+        const int r = i * RPI + rr;
+        const u32x4 x = *(const u32x4*)(stage + r * RS + cc * 8);
+        if (row0 + r < n_rows) *(u32x4*)(oh + (int64_t)(row0 + r) * D + cc * 8) = x;
+    }
+    if (qrow[0] < n_rows && hh == 0) lseh[qrow[0]] = (m_run[0] + log2f(l_tot)) * 0.69314718055994531f;
+}
+
 // SPLIT: the key tiles of a query tile are divided into n_splits contiguous
 // chunks, one workgroup each, and every workgroup writes the normalised
 // partial output of its chunk (fp32) and the chunk's logsumexp to a
@@ -300,7 +337,9 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 {
     typedef Cfg<D, WAVES, QB> C;
     typedef typename Mma<T>::vec8 vec8;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * C::TILE];
+    constexpr bool kStaged = QB == 1 && !MASKS && !PADDED && !SPLIT;
+    constexpr int kSmem = kStaged && WAVES * 32 * (D + 8) > 4 * C::TILE ? WAVES * 32 * (D + 8) : 4 * C::TILE;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
 
     uint32_t bh, qt, split = 0;
     if (SPLIT) {
@@ -637,6 +676,10 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     if (SPLIT) {
         const int64_t slot = ((int64_t)split * (gridDim.x / ((uint32_t)n_splits * (uint32_t)n_qt)) + bh) * Nq;
         store_partials<D, QB, C::DB>(oacc, m_run, l_run, qrow, Nq, ws_o + slot * D, ws_lse + slot, hh);
+    } else if constexpr (kStaged) {
+        __syncthreads();  // every wave is past its last read of K and V
+        store_outputs_staged<T, D, C::DB>(oacc, m_run, l_run, qrow, q0 + wave * 32, Nq, o + q_off,
+                                          lse + (int64_t)bh * Nq, hh, lane, smem + wave * 32 * (D + 8));
     } else {
         store_outputs<T, D, QB, C::DB, MASKS, PADDED>(oacc, m_run, l_run, qrow, Nq, o + q_off,
                                                       lse + (int64_t)bh * Nq, hh, dm);

@@ -31,7 +31,14 @@ Shape pick_shape(int B, int H, int n_queries, int d, bool causal)
 }
 
 int block_n(int) { return 64; }
-int lds_bytes(int d) { return 4 * 64 * kernel_dim(d) * 2; }
+int lds_bytes(int d, int waves, bool staged)
+{
+    // two K and two V tiles; the epilogue of the launches without masks,
+    // padding or split stages each wave's 32 output rows (D + 8 elements apart)
+    // through the same memory
+    const int D = kernel_dim(d), tiles = 4 * 64 * D * 2, stage = waves * 32 * (D + 8) * 2;
+    return staged && stage > tiles ? stage : tiles;
+}
 int split_rows_per_tile() { return 128; }
 
 hipError_t launch_forward(const FwdArgs& a)
