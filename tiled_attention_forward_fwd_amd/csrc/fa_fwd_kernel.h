@@ -338,7 +338,12 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     typedef Cfg<D, WAVES, QB> C;
     typedef typename Mma<T>::vec8 vec8;
     constexpr bool kStaged = QB == 1 && !MASKS && !PADDED && !SPLIT;
-    constexpr int kSmem = kStaged && WAVES * 32 * (D + 8) > 4 * C::TILE ? WAVES * 32 * (D + 8) : 4 * C::TILE;
+    // kQlds: the 8-wave launches without masks, padding or split copy their Q
+    // tile into LDS with the same whole-row copies as K and V and read the
+    // operand from there, instead of 16-byte register loads from 32 rows.
+    constexpr bool kQlds = kStaged && WAVES == 8;
+    constexpr int kTilesQ = 4 * C::TILE + (kQlds ? C::BM * D : 0);
+    constexpr int kSmem = kStaged && WAVES * 32 * (D + 8) > kTilesQ ? WAVES * 32 * (D + 8) : kTilesQ;
     __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
 
     uint32_t bh, qt, split = 0;
@@ -395,8 +400,10 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     vec8 qf[QB][C::DS];
     if (PADDED)
         load_q_padded<T, D, QB, C::DS>(q + q_off, dm, q0 + wave * QB * 32, Nq, l32, hh, qrow, qf);
-    else
+    else if (!kQlds)
         load_q<T, D, QB, C::DS>(q + q_off, q0 + wave * QB * 32, Nq, l32, hh, qrow, qf);
+    else
+        qrow[0] = q0 + wave * 32 + l32;
 
     // key tiles [t0, t1) of the query tile, of which [u_lo, u_hi) need no mask
     int t0 = 0, t1, u_lo = 0, u_hi;
@@ -511,10 +518,20 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 #pragma unroll
             for (int kb = 0; kb < C::KB; ++kb) sa[qb][kb] = (f32x16){};
     } else {
+        if constexpr (kQlds) {
+            const rsrc_t qrs = head_rsrc(q + q_off, (uint32_t)Nq * (uint32_t)(D * 2));
+#pragma unroll
+            for (int r = 0; r < C::BM; r += C::BN) issue(smem + 4 * C::TILE + r * D, qrs, q0 + r);
+        }
         issue(kbuf(jb), krs, jb * C::BN);
         issue(vbuf(jb), vrs, jb * C::BN);
         if (jb + 1 < je) issue(kbuf(jb + 1), krs, (jb + 1) * C::BN);
         stage_barrier();
+        if constexpr (kQlds) {
+#pragma unroll
+            for (int ds = 0; ds < C::DS; ++ds)
+                qf[0][ds] = k_operand<vec8, D>(smem + 4 * C::TILE, wave * 32 + l32, ds, hh);
+        }
         // every wave processes an unmasked tile of a direct launch
         if ((!SPLIT && (!MASKS || (jb >= u_lo && jb < u_hi))) || wave_sees(jb)) {
             scores<T, D, QB, C::KB, C::DS>(sa, kbuf(jb), qf, l32, hh);
