@@ -185,7 +185,8 @@ __device__ __forceinline__ void store_outputs(const f32x16 (&oacc)[QB][DB], cons
 // back a row per 16 lanes and stores 16 contiguous bytes per lane, so every
 // store instruction writes four whole rows instead of 16 bytes of 32 rows.
 // The caller has passed a barrier after its last LDS read of K and V.
-template <typename T, int D, int DB>
+// EMPTY: rows may have seen no key (masks): O = 0 and lse = -inf there.
+template <typename T, int D, int DB, bool EMPTY>
 __device__ __forceinline__ void store_outputs_staged(const f32x16 (&oacc)[1][DB], const float (&m_run)[1],
                                                      const float (&l_run)[1], const int (&qrow)[1], int row0,
                                                      int n_rows, T* __restrict__ oh, float* __restrict__ lseh,
@@ -193,7 +194,8 @@ __device__ __forceinline__ void store_outputs_staged(const f32x16 (&oacc)[1][DB]
 {
     constexpr int RS = D + 8;  // LDS row stride in elements
     const float l_tot = swap_halves_sum(l_run[0]);
-    const float inv = 1.0f / l_tot;
+    const bool seen = !EMPTY || l_tot > 0.f;
+    const float inv = seen ? 1.0f / l_tot : 0.f;
     const int l32 = lane & 31;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -214,7 +216,8 @@ __device__ __forceinline__ void store_outputs_staged(const f32x16 (&oacc)[1][DB]
         const u32x4 x = *(const u32x4*)(stage + r * RS + cc * 8);
         if (row0 + r < n_rows) *(u32x4*)(oh + (int64_t)(row0 + r) * D + cc * 8) = x;
     }
-    if (qrow[0] < n_rows && hh == 0) lseh[qrow[0]] = (m_run[0] + log2f(l_tot)) * 0.69314718055994531f;
+    if (qrow[0] < n_rows && hh == 0)
+        lseh[qrow[0]] = seen ? (m_run[0] + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
 }
 
 // SPLIT: the key tiles of a query tile are divided into n_splits contiguous
@@ -337,11 +340,11 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 {
     typedef Cfg<D, WAVES, QB> C;
     typedef typename Mma<T>::vec8 vec8;
-    constexpr bool kStaged = QB == 1 && !MASKS && !PADDED && !SPLIT;
+    constexpr bool kStaged = QB == 1 && !PADDED && !SPLIT;
     // kQlds: the 8-wave launches without masks, padding or split copy their Q
     // tile into LDS with the same whole-row copies as K and V and read the
     // operand from there, instead of 16-byte register loads from 32 rows.
-    constexpr bool kQlds = kStaged && WAVES == 8;
+    constexpr bool kQlds = kStaged && !MASKS && WAVES == 8;
     constexpr int kTilesQ = 4 * C::TILE + (kQlds ? C::BM * D : 0);
     constexpr int kSmem = kStaged && WAVES * 32 * (D + 8) > kTilesQ ? WAVES * 32 * (D + 8) : kTilesQ;
     __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
@@ -695,7 +698,7 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
         store_partials<D, QB, C::DB>(oacc, m_run, l_run, qrow, Nq, ws_o + slot * D, ws_lse + slot, hh);
     } else if constexpr (kStaged) {
         __syncthreads();  // every wave is past its last read of K and V
-        store_outputs_staged<T, D, C::DB>(oacc, m_run, l_run, qrow, q0 + wave * 32, Nq, o + q_off,
+        store_outputs_staged<T, D, C::DB, MASKS>(oacc, m_run, l_run, qrow, q0 + wave * 32, Nq, o + q_off,
                                           lse + (int64_t)bh * Nq, hh, lane, smem + wave * 32 * (D + 8));
     } else {
         store_outputs<T, D, QB, C::DB, MASKS, PADDED>(oacc, m_run, l_run, qrow, Nq, o + q_off,

@@ -54,9 +54,9 @@ Shape pick_shape(int B, int H, int n_queries, int d, bool causal);
 // of 128 keeps 4 waves.
 Shape pick_shape_masked(int B, int H, int n_queries, int d, bool causal);
 int block_n(int d);
-// LDS per workgroup; staged: the launch stages its output through LDS (no
-// masks, padding or split).
-int lds_bytes(int d, int waves, bool staged);
+// LDS per workgroup; stage_out: the launch stages its output through LDS (no
+// padding or split); q_tile: it also copies its Q tile there (8 waves, no masks).
+int lds_bytes(int d, int waves, bool stage_out, bool q_tile);
 int split_rows_per_tile();
 
 // Enqueues the forward pass (one kernel, or the split kernel and the merge).
