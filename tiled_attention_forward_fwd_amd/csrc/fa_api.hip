@@ -259,7 +259,7 @@ int fa_plan_qk(int B, int H, int Nq, int Nk, int d, int causal, int dtype, fa_pl
     plan->block_m = bm;
     plan->block_n = bn;
     plan->threads = sh.threads;
-    plan->lds_bytes = fa::lds_bytes(d, sh.waves, d == fa::kernel_dim(d), d == fa::kernel_dim(d) && sh.waves == 8);
+    plan->lds_bytes = fa::lds_bytes(d, sh.waves, d >= 64, d == fa::kernel_dim(d) && sh.waves == 8);
     plan->workgroups = bh * ((Nq + bm - 1) / bm);
     plan->pairs_visited = bh * counts[1];
     // every visited pair costs S = Q K^T and P V, masked pairs included, at
@@ -333,7 +333,7 @@ int fa_plan_masked(int B, int H, int Nq, int Nk, int d, int causal, int window_l
     plan->block_n = bn;
     plan->threads = sh.threads;
     plan->lds_bytes =
-        fa::lds_bytes(d, sh.waves, d == fa::kernel_dim(d), off && d == fa::kernel_dim(d) && sh.waves == 8);
+        fa::lds_bytes(d, sh.waves, d >= 64, off && d == fa::kernel_dim(d) && sh.waves == 8);
     plan->workgroups = (int64_t)B * H * ((Nq + bm - 1) / bm);
     plan->pairs_visited = (int64_t)(tiles * H);
     plan->mfma_flops = 4.0 * fa::kernel_dim(d) * (double)bm * bn * (double)plan->pairs_visited;

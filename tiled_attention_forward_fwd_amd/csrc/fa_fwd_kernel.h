@@ -186,11 +186,13 @@ __device__ __forceinline__ void store_outputs(const f32x16 (&oacc)[QB][DB], cons
 // store instruction writes four whole rows instead of 16 bytes of 32 rows.
 // The caller has passed a barrier after its last LDS read of K and V.
 // EMPTY: rows may have seen no key (masks): O = 0 and lse = -inf there.
-template <typename T, int D, int DB, bool EMPTY>
+// PADDED: rows are dm elements apart in memory and only dims below dm are
+// written (dm a multiple of 8, so rows stay 16-byte aligned).
+template <typename T, int D, int DB, bool EMPTY, bool PADDED>
 __device__ __forceinline__ void store_outputs_staged(const f32x16 (&oacc)[1][DB], const float (&m_run)[1],
                                                      const float (&l_run)[1], const int (&qrow)[1], int row0,
                                                      int n_rows, T* __restrict__ oh, float* __restrict__ lseh,
-                                                     int hh, int lane, uint16_t* __restrict__ stage)
+                                                     int hh, int lane, uint16_t* __restrict__ stage, int dm)
 {
     constexpr int RS = D + 8;  // LDS row stride in elements
     const float l_tot = swap_halves_sum(l_run[0]);
@@ -214,7 +216,8 @@ __device__ __forceinline__ void store_outputs_staged(const f32x16 (&oacc)[1][DB]
     for (int i = 0; i < 32 / RPI; ++i) {
         const int r = i * RPI + rr;
         const u32x4 x = *(const u32x4*)(stage + r * RS + cc * 8);
-        if (row0 + r < n_rows) *(u32x4*)(oh + (int64_t)(row0 + r) * D + cc * 8) = x;
+        const int stride = PADDED ? dm : D;
+        if (row0 + r < n_rows && (!PADDED || cc * 8 < dm)) *(u32x4*)(oh + (int64_t)(row0 + r) * stride + cc * 8) = x;
     }
     if (qrow[0] < n_rows && hh == 0)
         lseh[qrow[0]] = seen ? (m_run[0] + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
@@ -340,11 +343,13 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 {
     typedef Cfg<D, WAVES, QB> C;
     typedef typename Mma<T>::vec8 vec8;
-    constexpr bool kStaged = QB == 1 && !PADDED && !SPLIT;
+    // kStaged: the epilogue goes through LDS (store_outputs_staged); padded head
+    // dims below 64 measured 1% slower with it and keep the direct stores.
+    constexpr bool kStaged = QB == 1 && !SPLIT && !(PADDED && D == 64);
     // kQlds: the 8-wave launches without masks, padding or split copy their Q
     // tile into LDS with the same whole-row copies as K and V and read the
     // operand from there, instead of 16-byte register loads from 32 rows.
-    constexpr bool kQlds = kStaged && !MASKS && WAVES == 8;
+    constexpr bool kQlds = kStaged && !MASKS && !PADDED && WAVES == 8;
     constexpr int kTilesQ = 4 * C::TILE + (kQlds ? C::BM * D : 0);
     constexpr int kSmem = kStaged && WAVES * 32 * (D + 8) > kTilesQ ? WAVES * 32 * (D + 8) : kTilesQ;
     __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
@@ -698,8 +703,9 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
         store_partials<D, QB, C::DB>(oacc, m_run, l_run, qrow, Nq, ws_o + slot * D, ws_lse + slot, hh);
     } else if constexpr (kStaged) {
         __syncthreads();  // every wave is past its last read of K and V
-        store_outputs_staged<T, D, C::DB, MASKS>(oacc, m_run, l_run, qrow, q0 + wave * 32, Nq, o + q_off,
-                                          lse + (int64_t)bh * Nq, hh, lane, smem + wave * 32 * (D + 8));
+        store_outputs_staged<T, D, C::DB, MASKS, PADDED>(oacc, m_run, l_run, qrow, q0 + wave * 32, Nq, o + q_off,
+                                                         lse + (int64_t)bh * Nq, hh, lane, smem + wave * 32 * (D + 8),
+                                                         dm);
     } else {
         store_outputs<T, D, QB, C::DB, MASKS, PADDED>(oacc, m_run, l_run, qrow, Nq, o + q_off,
                                                       lse + (int64_t)bh * Nq, hh, dm);

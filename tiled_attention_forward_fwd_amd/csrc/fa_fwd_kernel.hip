@@ -34,8 +34,9 @@ int block_n(int) { return 64; }
 int lds_bytes(int d, int waves, bool stage_out, bool q_tile)
 {
     // two K and two V tiles (plus the Q tile of the 8-wave launches without
-    // masks, padding or split); the launches without padding or split stage
-    // each wave's 32 output rows (D + 8 elements apart) through the same memory
+    // masks, padding or split); the launches without split (and head dim at
+    // least 64) stage each wave's 32 output rows (D + 8 elements apart)
+    // through the same memory
     const int D = kernel_dim(d);
     const int tiles = 4 * 64 * D * 2 + (q_tile ? 256 * D * 2 : 0);
     const int stage = waves * 32 * (D + 8) * 2;

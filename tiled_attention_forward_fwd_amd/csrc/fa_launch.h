@@ -55,7 +55,8 @@ Shape pick_shape(int B, int H, int n_queries, int d, bool causal);
 Shape pick_shape_masked(int B, int H, int n_queries, int d, bool causal);
 int block_n(int d);
 // LDS per workgroup; stage_out: the launch stages its output through LDS (no
-// padding or split); q_tile: it also copies its Q tile there (8 waves, no masks).
+// split, head dim at least 64); q_tile: it also copies its Q tile there (8
+// waves, no masks or padding).
 int lds_bytes(int d, int waves, bool stage_out, bool q_tile);
 int split_rows_per_tile();
 
