@@ -170,6 +170,24 @@ def test_plan_picks_workgroup_shape(lib):
     assert (more["block_m"], more["threads"], more["workgroups"]) == (256, 512, 64 * 32)
 
 
+def test_plan_lds_bytes(lib):
+    # two K and two V tiles of 64 rows; the 8-wave launches without masks or
+    # padding also hold their 256-row Q tile; the staged epilogue (32 rows of
+    # D + 8 elements per wave) needs more than the tiles only for 8-wave
+    # launches that hold no Q tile
+    big = fa.fa_plan(4, 16, 4096, 128, 0, fa.FA_DTYPE_BF16)
+    assert big["lds_bytes"] == 4 * 64 * 128 * 2 + 256 * 128 * 2
+    assert fa.fa_plan(4, 16, 4096, 128, 1, fa.FA_DTYPE_BF16)["lds_bytes"] == 4 * 64 * 128 * 2
+    assert fa.fa_plan(4, 16, 4096, 64, 0, fa.FA_DTYPE_BF16)["lds_bytes"] == 4 * 64 * 64 * 2 + 256 * 64 * 2
+    # padded d = 96 runs the d = 128 kernel: no Q tile, staged epilogue
+    assert fa.fa_plan(4, 16, 4096, 96, 0, fa.FA_DTYPE_BF16)["lds_bytes"] == 8 * 32 * 136 * 2
+    # padded d = 32: neither
+    assert fa.fa_plan(4, 16, 4096, 32, 0, fa.FA_DTYPE_F16)["lds_bytes"] == 4 * 64 * 64 * 2
+    # masks: staged epilogue, no Q tile
+    m = fa.fa_plan_masked(4, 16, 4096, 4096, 64, 0, 100, -1, None, fa.FA_DTYPE_BF16)
+    assert m["threads"] == 512 and m["lds_bytes"] == 8 * 32 * 72 * 2
+
+
 # ---- Nq != Nk (fa_fwd_qk, fa_tile_counts_qk, fa_plan_qk)
 
 def call_qk(**kw):
