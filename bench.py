@@ -25,9 +25,10 @@ Other modes (used to collect counters; each runs a few launches only):
     --profile-masked    the padding and sliding-window workloads of the sweep
     --profile-variants  head dims 96 and 32 and fp32 inputs at the headline shape
     --sweep             medians of 50 for every configuration of the workload
-                        list, with peak memory (one extra JSON object); the
-                        masked rows count exactly the visible (query, key)
-                        pairs (fa_plan_masked)
+                        list, with each configuration's own peak memory and
+                        the fp64 oracle's rate on a row sample of it (one
+                        extra JSON object); the masked rows count exactly the
+                        visible (query, key) pairs (fa_plan_masked)
 """
 
 import argparse
@@ -207,6 +208,50 @@ def gemm_ceiling(seconds=1.0):
             "what": "bf16 8192x8192x8192 GEMM, torch.matmul (hipBLASLt), N(0,1) operands, median of 20"}
 
 
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_rate(cfg, q, k, v, causal, flop_budget=4.0e10):
+    """The fp64 oracle on a row sample of one sweep configuration: every
+    stride-th query row (all heads), the stride chosen so that the sample
+    holds about `flop_budget` visited-key FLOPs. Returns the rate over the
+    sample's exact visited-key FLOPs and what the sample was."""
+    import oracle
+    import tiled_attention_forward_fwd_amd as fa
+    B, H, Nk, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+    Nq = q.shape[2]
+    wl, wr, kls = cfg.get("wl", -1), cfg.get("wr", -1), cfg.get("key_lens")
+
+    def keys_seen(i, kl):
+        hi = min(i + 1, Nk) if causal else (min(i + wr + 1, Nk) if wr >= 0 else Nk)
+        hi = min(hi, kl)
+        lo = max(0, i - wl) if wl >= 0 else 0
+        return max(0, hi - lo)
+
+    lens = kls if kls is not None else [Nk] * B
+    total = 4.0 * H * d * sum(keys_seen(i, kl) for kl in lens for i in range(Nq))
+    stride = max(1, int(-(-total // flop_budget)))
+    rows = list(range(0, Nq, stride))
+    flops = 4.0 * H * d * sum(keys_seen(i, kl) for kl in lens for i in rows)
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.attention_fwd(q, k, v, causal, fa.default_scale(d), rows=rows, nthreads=threads,
+                         window_left=wl, window_right=wr, key_lens=kls)
+    dt = time.perf_counter() - t0
+    return {"gflops": flops / dt / 1e9, "seconds": dt, "threads": threads,
+            "sample": ("all query rows" if stride == 1 else f"every {stride}th query row")
+                      + f" ({len(rows)} of {Nq}, all heads), {flops / 1e9:.2f} G visited-key FLOPs"}
+
+
 def cpu_baseline(cfg, q, k, v, stride):
     """The fp64 oracle on a bounded row sample of the workload (host cores)."""
     import oracle
@@ -225,6 +270,7 @@ def cpu_baseline(cfg, q, k, v, stride):
     # the same convention as the GPU: the causal pass counts half of the full rows' keys
     conv = 4.0 * cfg["B"] * cfg["H"] * len(rows) * N * cfg["d"] * 1.5
     return {"value": conv / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": (f"B={cfg['B']} H={cfg['H']} N={N} d={cfg['d']} {cfg['dtype']}: "
                        + ("all query rows" if stride == 1 else f"every {stride}th query row")
                        + f" ({len(rows)} rows per head, all heads), one "
@@ -328,7 +374,12 @@ def headline(args):
 
 
 def sweep(args):
-    """Medians of 50 (after a separate warmup) for each configuration, with peak memory."""
+    """Medians of 50 (after a separate warmup) for each configuration, with peak memory and
+    the fp64 oracle's rate on the host for the same configuration.
+
+    peak_mem_bytes is the peak device allocation during the configuration's timed calls
+    (statistics reset after its warmup) minus what was allocated before its inputs were
+    created, i.e. its own inputs, outputs and workspace."""
     import torch
     import tiled_attention_forward_fwd_amd as fa
     dev = torch.device("cuda:0")
@@ -356,10 +407,13 @@ def sweep(args):
         dict(B=4, H=16, N=4096, d=64, dtype="fp32", seed=20, flags=(0, 1)),
     ] + MASKED_WORKLOADS
     for cfg in configs:
-        _, _, _, qd, kd, vd = make_inputs(cfg, dev)
+        torch.cuda.synchronize()
+        base_mem = torch.cuda.memory_allocated(dev)  # what earlier configurations still hold
+        qh, kh, vh, qd, kd, vd = make_inputs(cfg, dev)
         B, H, Nk, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
         Nq = cfg.get("Nq", Nk)
         qd = qd[:, :, :Nq].contiguous()
+        qh = qh[:, :, :Nq].contiguous()
         code = fa.FA_DTYPE_BF16 if cfg["dtype"] == "bf16" else fa.FA_DTYPE_F16
         wl, wr, kls = cfg.get("wl", -1), cfg.get("wr", -1), cfg.get("key_lens")
         masked = wl != -1 or wr != -1 or kls is not None
@@ -381,7 +435,9 @@ def sweep(args):
                 plan = fa.fa_plan_masked(B, H, Nq, Nk, d, causal, wl, wr, kls, code)
             else:
                 plan = fa.fa_plan_qk(B, H, Nq, Nk, d, causal, code)
+            peak = torch.cuda.max_memory_allocated(dev) - base_mem
             med = statistics.median(ts)
+            cpu = oracle_rate(cfg, qh, kh, vh, bool(causal)) if args.sweep_oracle else None
             rows.append({"B": B, "H": H, "Nq": Nq, "N": Nk, "d": d,
                          "dtype": cfg["dtype"], "q_scale": cfg.get("q_scale", 1.0),
                          **({"window_left": wl, "window_right": wr, "key_lens": kls} if masked else {}),
@@ -391,9 +447,12 @@ def sweep(args):
                          "frac_peak": plan["algo_flops"] / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                          "hbm_gbs_compulsory": plan["algo_bytes"] / (med * 1e-3) / 1e9,
                          "frac_hbm": plan["algo_bytes"] / (med * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                         "peak_mem_bytes": torch.cuda.max_memory_allocated(dev)})
+                         "peak_mem_bytes": peak,
+                         "cpu_oracle": cpu,
+                         "gpu_over_oracle": (None if cpu is None else
+                                             plan["algo_flops"] / (med * 1e-3) / (cpu["gflops"] * 1e9))})
             print(json.dumps({"sweep_row": rows[-1]}), flush=True)
-        del qd, kd, vd
+        del qd, kd, vd, out, lse, ws, fn
         torch.cuda.empty_cache()
     return rows
 
@@ -535,6 +594,8 @@ def main():
     ap.add_argument("--no-gemm-ceiling", dest="gemm_ceiling", action="store_false",
                     help="skip the hipBLASLt GEMM reference run (context for the roofline)")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--no-sweep-oracle", dest="sweep_oracle", action="store_false",
+                    help="skip the per-configuration oracle timing of --sweep")
     ap.add_argument("--profile-kernels", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--profile-decode", action="store_true",
