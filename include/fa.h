@@ -302,9 +302,14 @@ typedef struct {
     int lds_bytes;          /* LDS per workgroup */
     int64_t workgroups;     /* grid size */
     int64_t pairs_visited;  /* visited (query tile, key tile) pairs, all heads */
-    double mfma_flops;      /* FLOPs the matrix cores execute: 4*D per (row, key)
-                               of every visited tile pair, masked ones included,
-                               D the kernel's head dim (64 or 128) */
+    double mfma_flops;      /* FLOPs the matrix cores execute, D the kernel's
+                               head dim (64 or 128): 2*32*64*D for each block of
+                               32 query rows x 64 keys of which a wave computes
+                               S = Q K^T, and as much for each it computes P V.
+                               Every visited tile pair counts, masked ones too,
+                               except that in a causal tile a wave skips the key
+                               tiles past its own rows (and under masks the
+                               tiles its rows do not see) */
     double algo_flops;      /* 4*d per (query, key) pair of the visible region:
                                4*B*H*Nq*Nk*d non-causal; causal counts the area
                                below the diagonal, Nq*Nq/2 for Nq <= Nk and

@@ -134,7 +134,62 @@ def test_plan_flops_match_printed_counts(lib):
     # algorithm's FLOPs; causal adds the masked part of the diagonal tiles
     assert nc["mfma_flops"] == nc["algo_flops"]
     assert c["mfma_flops"] > c["algo_flops"]
-    assert c["mfma_flops"] == 4 * 64 * c["block_m"] * c["block_n"] * c["pairs_visited"]
+    # waves skip the diagonal key tiles past their own rows, so the executed
+    # work is below the visited tile pairs' full count
+    assert c["mfma_flops"] < 4 * 64 * c["block_m"] * c["block_n"] * c["pairs_visited"]
+    assert c["mfma_flops"] == _walked_mfma_flops(4, 8, 4096, 4096, 64, 1, c["threads"] // 64)
+
+
+def _walked_mfma_flops(B, H, Nq, Nk, D, causal, waves):
+    """The forward kernel's step loop walked one step at a time (no masks, no
+    split): each wave counts the 32 x 64 blocks whose S = Q K^T and whose P V
+    it computes. Restates the kernel's control flow, not the plan's interval
+    arithmetic."""
+    BM, BN = 32 * waves, 64  # every unmasked, unpadded direct launch fuses the exp work
+    blocks = 0
+    for q0 in range(0, Nq, BM):
+        full_end = (Nk // BN) * BN
+        if causal:
+            un_end = min((q0 // BN) * BN, full_end)
+            m_end = min(q0 + BM, Nq, Nk)
+        else:
+            un_end, m_end = full_end, Nk
+        u_hi = un_end // BN
+        je = u_hi + -(-(m_end - un_end) // BN)
+        for w in range(waves):
+            n_wave = min(je, (q0 + (w + 1) * 32 - 1) // BN + 1) if causal else je
+            sees = lambda t: t < n_wave  # noqa: E731
+            blocks += 1  # the first tile's scores, before the loop
+            for j in range(0, je - 1):
+                G = j >= u_hi  # masked step: per-wave limits apply
+                if not G or sees(j):
+                    blocks += 1 if (not G or sees(j + 1)) else 0  # scores of tile j+1
+                    blocks += 1  # P V of tile j
+            j = je - 1
+            blocks += 1 if (j < u_hi or sees(j)) else 0  # the last tile's P V
+    return blocks * 2 * 32 * 64 * D * B * H
+
+
+@pytest.mark.parametrize("Nq,Nk", [(4096, 4096), (1000, 1000), (300, 1000), (1000, 300), (129, 64),
+                                   (1, 16384), (4097, 4097)])
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("d", [64, 128])
+def test_plan_mfma_flops_follow_the_kernel_loop(lib, Nq, Nk, causal, d):
+    for B, H in ((1, 2), (8, 16)):  # both workgroup shapes
+        p = fa.fa_plan_qk(B, H, Nq, Nk, d, causal, fa.FA_DTYPE_BF16)
+        assert p["mfma_flops"] == _walked_mfma_flops(B, H, Nq, Nk, d, causal, p["threads"] // 64)
+        assert p["mfma_flops"] >= p["algo_flops"] * (1.0 if not causal else 0.999)
+
+
+def test_plan_mfma_flops_of_the_headline_causal_launch(lib):
+    # B4 H16 N4096 d128 causal: 4-wave workgroups of 128 rows; in query tile
+    # i, waves 0-1 compute 2i+1 key tiles and waves 2-3 compute 2i+2, i.e.
+    # 8i+6 blocks of 32 rows x 64 keys per workgroup for each of S and P V:
+    # 64 heads x sum_i (8i+6) x 2 x 2*32*64*128 FLOPs = 279.17 G
+    c = fa.fa_plan(4, 16, 4096, 128, 1, fa.FA_DTYPE_BF16)
+    per_head = sum(8 * i + 6 for i in range(32))
+    assert c["mfma_flops"] == 64 * per_head * 2 * 2 * 32 * 64 * 128
+    assert abs(c["mfma_flops"] - 279.17e9) < 0.01e9
 
 
 def test_plan_flop_convention_matches_t4_table(lib):
@@ -320,7 +375,14 @@ def test_plan_masked_counts_visible_pairs_and_keys(lib):
         tiles = sum(fa.fa_tile_counts_masked(Nq, Nk, plan["block_m"], 64, causal, wl, wr,
                                              Nk if kls is None else kls[b])[1] for b in range(B))
         assert plan["pairs_visited"] == H * tiles
-        assert plan["mfma_flops"] == 4 * d * plan["block_m"] * 64 * plan["pairs_visited"]
+        # every visible pair is computed (at the kernel's head dim, here d);
+        # no wave computes more than every visited tile pair plus the one
+        # leading tile a wave whose range starts inside the query tile takes
+        waves = plan["threads"] // 64
+        assert plan["mfma_flops"] >= plan["algo_flops"]
+        n_qt = -(-Nq // plan["block_m"])
+        assert plan["mfma_flops"] <= 4 * d * plan["block_m"] * 64 * plan["pairs_visited"] + \
+            B * H * n_qt * waves * 2 * 2 * 32 * 64 * d
 
 
 def test_plan_masked_shape(lib):

@@ -10,6 +10,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "fa.h"
 #include "fa_launch.h"
 #include "fa_tiles.h"
@@ -157,6 +159,82 @@ double causal_area(double Nq, double Nk)
     return Nq <= Nk ? 0.5 * Nq * Nq : 0.5 * Nk * Nk + (Nq - Nk) * Nk;
 }
 
+// Number of j in [a, b) that lie in [u0, u1) or in [w0, w1).
+int64_t count_in_union(int64_t a, int64_t b, int64_t u0, int64_t u1, int64_t w0, int64_t w1)
+{
+    auto len = [a, b](int64_t lo, int64_t hi) {
+        lo = lo > a ? lo : a;
+        hi = hi < b ? hi : b;
+        return hi > lo ? hi - lo : 0;
+    };
+    const int64_t both = len(u0 > w0 ? u0 : w0, u1 < w1 ? u1 : w1);
+    return len(u0, u1) + len(w0, w1) - both;
+}
+
+// Masks of a plan (host values); key_len is the batch's key count.
+struct PlanMasks {
+    int64_t window_left, window_right, key_len;
+};
+
+// Blocks of 32 query rows x 64 keys for which the waves of the query tile at
+// q0 execute S = Q K^T, plus those for which they execute P V, in a direct
+// (unsplit) launch, following the forward kernel's loop (fa_fwd_kernel.h):
+//  * the tile's key tiles are [jb, je), of which U = [u_lo, u_hi) run the
+//    unmasked step, where every wave computes; in the other steps a wave
+//    computes only the tiles W = [w_lo, n_wave) its own rows see;
+//  * the scores of the first tile are computed before the loop, those of tile
+//    j+1 in step j, and the P V of tile j in step j (the last tile in a step
+//    of its own);
+//  * a wave that fuses the exp work with the next scores computes the scores
+//    of j+1 only in a step in which it computes tile j.
+int64_t wave_blocks(int64_t q0, int waves, int64_t Nq, int64_t Nk, bool causal, const PlanMasks* m, int D,
+                    bool padded)
+{
+    const int64_t BM = 32 * waves, BN = fa::block_n(D);
+    int64_t jb, je, u_lo, u_hi;
+    if (m) {
+        const fa::MaskedSpan ms =
+            fa::masked_span(q0, BM, BN, Nq, Nk, causal, m->window_left, m->window_right, m->key_len);
+        jb = ms.first;
+        je = ms.end;
+        u_lo = ms.unmasked_begin;
+        u_hi = ms.unmasked_end;
+        if (jb == je) return 0;
+    } else {
+        const fa::TileSpan sp = fa::tile_span(q0, BM, BN, Nq, Nk, causal);
+        jb = 0;
+        je = sp.total;
+        u_lo = 0;
+        u_hi = sp.unmasked;
+    }
+    const bool fused = fa::fuses_exp(D, waves, false, m != nullptr, padded);
+    int64_t blocks = 0;
+    for (int w = 0; w < waves; ++w) {
+        int64_t n_wave = causal ? std::min(je, (q0 + (w + 1) * 32 - 1) / BN + 1) : je;
+        int64_t w_lo = jb;
+        if (m) {
+            const int64_t r0 = q0 + w * 32;
+            if (r0 >= Nq) {
+                n_wave = jb;
+            } else {
+                const fa::MaskedSpan ws = fa::masked_span(r0, 32, BN, Nq, Nk, causal, m->window_left,
+                                                          m->window_right, m->key_len);
+                w_lo = std::max(jb, ws.first - (fused ? 1 : 0));
+                n_wave = std::min(je, ws.end);
+            }
+        }
+        const bool pre = (!m || (jb >= u_lo && jb < u_hi)) || (jb >= w_lo && jb < n_wave);
+        const int64_t s_steps = fused ? count_in_union(jb, je - 1, u_lo, u_hi, w_lo, n_wave - 1)
+                                      : count_in_union(jb, je - 1, u_lo, u_hi, w_lo - 1, n_wave - 1);
+        const int64_t pv = count_in_union(jb, je, u_lo, u_hi, w_lo, n_wave);
+        blocks += (pre ? 1 : 0) + s_steps + pv;
+    }
+    return blocks;
+}
+
+// FLOPs of one 32 x 64 block of S = Q K^T or of P V at the kernel's head dim.
+double block_flops(int d) { return 2.0 * 32 * 64 * fa::kernel_dim(d); }
+
 int bwd_checked(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                 void* dq, void* dk, void* dv, float* delta, int B, int H, int Nq, int Nk, int d, int causal,
                 float scale, int dtype, const fa::MaskArgs* mask, void* stream)
@@ -262,9 +340,13 @@ int fa_plan_qk(int B, int H, int Nq, int Nk, int d, int causal, int dtype, fa_pl
     plan->lds_bytes = fa::lds_bytes(d, sh.waves, d >= 64, d == fa::kernel_dim(d) && sh.waves == 8);
     plan->workgroups = bh * ((Nq + bm - 1) / bm);
     plan->pairs_visited = bh * counts[1];
-    // every visited pair costs S = Q K^T and P V, masked pairs included, at
-    // the kernel's head dim
-    plan->mfma_flops = 4.0 * fa::kernel_dim(d) * (double)bm * bn * (double)plan->pairs_visited;
+    // S = Q K^T and P V of every 32-row block a wave computes (waves skip the
+    // causal tiles past their own rows), at the kernel's head dim
+    const bool padded = d != fa::kernel_dim(d);
+    int64_t blocks = 0;
+    for (int64_t q0 = 0; q0 < Nq; q0 += bm)
+        blocks += wave_blocks(q0, sh.waves, Nq, Nk, causal != 0, nullptr, fa::kernel_dim(d), padded);
+    plan->mfma_flops = block_flops(d) * (double)blocks * (double)bh;
     const double pairs = causal ? causal_area(Nq, Nk) : (double)Nq * (double)Nk;
     plan->algo_flops = 4.0 * (double)bh * pairs * d;
     plan->algo_bytes = 4.0 * (double)bh * ((double)Nq + Nk) * d + 4.0 * (double)bh * Nq;
@@ -309,7 +391,8 @@ int fa_plan_masked(int B, int H, int Nq, int Nk, int d, int causal, int window_l
     const fa::Shape sh = off ? fa::pick_shape(B, H, Nq, d, causal != 0)
                              : fa::pick_shape_masked(B, H, Nq, d, causal != 0);
     const int bm = sh.block_m, bn = fa::block_n(d);
-    double pairs = 0, tiles = 0, keys_read = 0;
+    double pairs = 0, tiles = 0, keys_read = 0, blocks = 0;
+    const bool padded = d != fa::kernel_dim(d);
     for (int b = 0; b < B; ++b) {
         const int64_t kl = key_lens ? key_lens[b] : Nk;
         int64_t counts[4];
@@ -318,6 +401,10 @@ int fa_plan_masked(int B, int H, int Nq, int Nk, int d, int causal, int window_l
         else
             fa_tile_counts_masked(Nq, Nk, bm, bn, causal, window_left, window_right, kl, counts);
         tiles += (double)counts[1];
+        const PlanMasks pm{window_left, window_right, kl};
+        for (int64_t q0 = 0; q0 < Nq; q0 += bm)
+            blocks += (double)wave_blocks(q0, sh.waves, Nq, Nk, causal != 0, off ? nullptr : &pm,
+                                          fa::kernel_dim(d), padded);
         // visible (query, key) pairs, and the keys some row sees (the union
         // of the rows' ranges; lo and hi never decrease with the row)
         int64_t reach = 0;
@@ -336,7 +423,7 @@ int fa_plan_masked(int B, int H, int Nq, int Nk, int d, int causal, int window_l
         fa::lds_bytes(d, sh.waves, d >= 64, off && d == fa::kernel_dim(d) && sh.waves == 8);
     plan->workgroups = (int64_t)B * H * ((Nq + bm - 1) / bm);
     plan->pairs_visited = (int64_t)(tiles * H);
-    plan->mfma_flops = 4.0 * fa::kernel_dim(d) * (double)bm * bn * (double)plan->pairs_visited;
+    plan->mfma_flops = block_flops(d) * blocks * H;
     plan->algo_flops = 4.0 * H * pairs * d;
     plan->algo_bytes = 4.0 * H * ((double)B * Nq + keys_read) * d + 4.0 * (double)B * H * Nq;
     return FA_OK;

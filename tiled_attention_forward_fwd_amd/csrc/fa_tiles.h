@@ -21,6 +21,16 @@
 
 namespace fa {
 
+// Whether a forward kernel variant interleaves the exp2 work of tile j with
+// the score MFMAs of tile j+1. Every 32-row variant does, except the 4-wave
+// head-dim-128 kernels with a split, masks or padding, which run out of
+// registers fused. The kernel and the host's count of executed MFMA work
+// (fa_plan) both take it from here.
+FA_HD constexpr bool fuses_exp(int D, int waves, bool split, bool masks, bool padded)
+{
+    return !(D == 128 && waves == 4 && (split || masks || padded));
+}
+
 struct KeyRange {
     int64_t unmasked_end;  // keys [0, unmasked_end) need no mask; a multiple of block_n
     int64_t masked_end;    // keys [unmasked_end, masked_end) are visited with the mask
