@@ -255,24 +255,18 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, stream=None, window_lef
     code = dtype_code(q.dtype)
     if scale is None:
         scale = default_scale(d)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    delta = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    with torch.cuda.device(q.device):
+    sobj = _launch_stream(stream, q.device)
+    with torch.cuda.device(q.device), torch.cuda.stream(sobj):
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
         kl_ptr = None
         if key_lens is not None:
-            if not torch.is_tensor(key_lens):
-                key_lens = torch.tensor([int(x) for x in key_lens], dtype=torch.int32, device=q.device)
-            if (key_lens.dtype != torch.int32 or not key_lens.is_cuda or key_lens.shape != (B,)
-                    or not key_lens.is_contiguous()):
-                raise ValueError("key_lens must be a contiguous int32 [B] GPU tensor")
+            key_lens = _device_key_lens(key_lens, B, q.device)
             kl_ptr = key_lens.data_ptr()
         rc = fa_bwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
                            B, H, N, Nk, d, causal, window_left, window_right, kl_ptr, scale, code,
-                           handle)
+                           sobj.cuda_stream)
     _check(rc)
     return dq, dk, dv
 
@@ -306,6 +300,30 @@ def fa_plan(B, H, N, d, causal, dtype):
     return plan.as_dict()
 
 
+def _launch_stream(stream, device):
+    """The torch stream object the kernels go on (torch's current stream when
+    `stream` is None; a raw hipStream_t handle is wrapped). Every temporary a
+    call allocates (outputs, workspaces, the delta scratch, the device copy of
+    key_lens) is allocated and filled while this stream is current, so the
+    caching allocator orders its reuse after the kernels that read it."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _device_key_lens(key_lens, B, device):
+    import torch
+    if not torch.is_tensor(key_lens):
+        key_lens = torch.tensor([int(x) for x in key_lens], dtype=torch.int32, device=device)
+    if (key_lens.dtype != torch.int32 or not key_lens.is_cuda or key_lens.shape != (B,)
+            or not key_lens.is_contiguous()):
+        raise ValueError("key_lens must be a contiguous int32 [B] GPU tensor")
+    return key_lens
+
+
 def dtype_code(torch_dtype):
     import torch
     if torch_dtype == torch.bfloat16:
@@ -330,26 +348,24 @@ def _fwd_f32(q, k, v, causal, scale, out, lse, stream, workspace, splits, window
     Nk = k.shape[2]
     if scale is None:
         scale = default_scale(d)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
-    need = fa_f32_workspace_bytes(B, H, Nk, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16) // 2, device=q.device, dtype=torch.bfloat16)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    if ws_bytes < need or not workspace.is_contiguous():
-        raise ValueError(f"workspace must be a contiguous tensor of at least {need} bytes")
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    with torch.cuda.device(q.device):
+    sobj = _launch_stream(stream, q.device)
+    with torch.cuda.device(q.device), torch.cuda.stream(sobj):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+        if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous tensor like q")
+        if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+        need = fa_f32_workspace_bytes(B, H, Nk, d)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16) // 2, device=q.device, dtype=torch.bfloat16)
+        ws_bytes = workspace.numel() * workspace.element_size()
+        if ws_bytes < need or not workspace.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous tensor of at least {need} bytes")
         rc = fa_fwd_f32(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
-                        N, Nk, d, causal, scale, workspace.data_ptr(), ws_bytes, handle)
+                        N, Nk, d, causal, scale, workspace.data_ptr(), ws_bytes, sobj.cuda_stream)
     _check(rc)
     return out, lse
 
@@ -396,29 +412,24 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None, spli
     code = dtype_code(q.dtype)
     if scale is None:
         scale = default_scale(d)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     if splits is None:
         splits = fa_split_count(B, H, N, Nk, d, causal) or 1
     masked = key_lens is not None or window_left != -1 or window_right != -1
-    kl_ptr = None
-    if key_lens is not None:
-        if not torch.is_tensor(key_lens):
-            key_lens = torch.tensor([int(x) for x in key_lens], dtype=torch.int32, device=q.device)
-        if (key_lens.dtype != torch.int32 or not key_lens.is_cuda or key_lens.shape != (B,)
-                or not key_lens.is_contiguous()):
-            raise ValueError("key_lens must be a contiguous int32 [B] GPU tensor")
-        kl_ptr = key_lens.data_ptr()
-    with torch.cuda.device(q.device):
+    sobj = _launch_stream(stream, q.device)
+    handle = sobj.cuda_stream
+    with torch.cuda.device(q.device), torch.cuda.stream(sobj):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+        if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous tensor like q")
+        if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+        kl_ptr = None
+        if key_lens is not None:
+            key_lens = _device_key_lens(key_lens, B, q.device)
+            kl_ptr = key_lens.data_ptr()
         if masked:
             if splits == 1:
                 rc = fa_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
