@@ -136,6 +136,28 @@ int fa_fwd_split_qk(const void *q, const void *k, const void *v, void *o, float 
                     void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * fa_fwd_split_qk_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): fa_fwd_split_qk without the workspace arguments. The partial
+ * results go to a scratch array of the library's own, FA_NOALLOC_SCRATCH_BYTES
+ * of device memory on each GPU the call runs on, which that GPU holds until
+ * the process ends. The call allocates nothing and frees nothing: on the
+ * first call on a device (the current device) it looks up the array's
+ * address there and keeps it. Arguments, results and ordering as
+ * fa_fwd_split_qk. Returns FA_ERR_UNSUPPORTED, before any HIP call, when
+ * fa_split_workspace_bytes(B, H, Nq, d, n_splits) exceeds
+ * FA_NOALLOC_SCRATCH_BYTES (then call fa_fwd_split_qk with a workspace).
+ * Every call on one GPU uses the same array and overwrites it: calls that can
+ * overlap in time on one GPU (on different streams, or from several threads)
+ * race and give wrong results; order them on one stream. Each call writes
+ * every scratch entry it reads, so nothing needs clearing between calls.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+int fa_fwd_split_qk_noalloc(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                            int H, int Nq, int Nk, int d, int causal, float scale, int dtype,
+                            int n_splits, void *stream);
+
+/*
  * Padding masks and sliding windows. "How to optimise a Triton
  * FlashAttention-2 kernel step by step with a profiler", section "Future
  * articles", names them as the case where a query row can be left with no

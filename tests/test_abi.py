@@ -522,3 +522,24 @@ def test_fa_bwd_masked_rejects_before_any_hip_call(lib):
                    (dict(kl=p[7] + 16), fa.FA_ERR_INVALID_ARG),   # key_lens inside dk
                    (dict(d=100), fa.FA_ERR_UNSUPPORTED), (dict(Nk=0), fa.FA_ERR_INVALID_ARG)]:
         assert run(**kw) == st, kw
+
+
+def test_noalloc_split_rejects_before_any_hip_call(lib):
+    # the static scratch holds FA_NOALLOC_SCRATCH_BYTES (16 MiB); a problem
+    # whose split workspace is larger is refused before any HIP call, as are
+    # the usual argument errors (fake, non-overlapping device addresses)
+    B, H, Nq, Nk, d = 16, 32, 128, 8192, 128
+    assert fa.fa_split_workspace_bytes(B, H, Nq, d, 64) > fa.NOALLOC_SCRATCH_BYTES
+    p = [(i + 1) << 36 for i in range(5)]
+    rc = fa.fa_fwd_split_qk_noalloc(*p, B, H, Nq, Nk, d, 0, 0.088, fa.FA_DTYPE_BF16, 64, None)
+    assert rc == fa.FA_ERR_UNSUPPORTED and "static scratch" in fa.fa_status_string(rc)
+    assert fa.fa_fwd_split_qk_noalloc(*p, B, H, Nq, Nk, d, 0, 0.088, fa.FA_DTYPE_BF16, 0, None) == \
+        fa.FA_ERR_INVALID_ARG
+    assert fa.fa_fwd_split_qk_noalloc(*p, B, H, Nq, Nk, d, 0, 0.088, fa.FA_DTYPE_BF16, 129, None) == \
+        fa.FA_ERR_INVALID_ARG
+    p16 = list(p)
+    p16[1] += 8  # k not 16-byte aligned
+    assert fa.fa_fwd_split_qk_noalloc(*p16, 1, 1, 1, 1024, 64, 0, 0.125, fa.FA_DTYPE_BF16, 2, None) == \
+        fa.FA_ERR_INVALID_ARG
+    assert fa.fa_fwd_split_qk_noalloc(*p, 1, 1, 1, 1024, 100, 0, 0.1, fa.FA_DTYPE_BF16, 2, None) == \
+        fa.FA_ERR_UNSUPPORTED

@@ -1,0 +1,65 @@
+"""GPU test of fa_fwd_split_qk_noalloc: the split-key decode launch with the
+library's static scratch instead of a caller workspace, through the C ABI,
+against fa_fwd_split_qk with a torch workspace on the same inputs (and the
+oracle), on two calls in a row, the second with a smaller problem."""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_attention_forward_fwd_amd as fa
+from fa_inputs import make_qkv
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {torch.float16: 4e-3, torch.bfloat16: 3.2e-2}
+
+
+def _inputs(B, H, Nq, Nk, d, dtype, seed):
+    q = make_qkv(B, H, Nq, d, dtype, seed)[0]
+    _, k, v = make_qkv(B, H, Nk, d, dtype, seed + 1)
+    return q, k, v
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def test_noalloc_split_matches_the_workspace_launch():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    fa.load_library()
+    stream = torch.cuda.current_stream().cuda_stream
+    # (B, H, Nq, Nk, d, dtype, causal): a decode batch, then a smaller problem
+    # of another head dim whose scratch use is a prefix of the first one's
+    cases = [(4, 16, 3, 8192, 128, "bf16", 0), (1, 4, 100, 2500, 64, "fp16", 1)]
+    for B, H, Nq, Nk, d, dtype, causal in cases:
+        print(f"[case] noalloc B={B} H={H} Nq={Nq} Nk={Nk} d={d} {dtype} causal={causal}", flush=True)
+        q, k, v = _inputs(B, H, Nq, Nk, d, dtype, 95 + d)
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        code = fa.dtype_code(q.dtype)
+        scale = fa.default_scale(d)
+        splits = fa.fa_split_count(B, H, Nq, Nk, d, causal)
+        assert splits > 1
+        need = fa.fa_split_workspace_bytes(B, H, Nq, d, splits)
+        assert need <= fa.NOALLOC_SCRATCH_BYTES
+        ws = torch.empty(need // 4, device="cuda", dtype=torch.float32)
+        o_ref, l_ref = torch.empty_like(qd), torch.empty((B, H, Nq), device="cuda")
+        o, lse = torch.full_like(qd, float("nan")), torch.full((B, H, Nq), float("nan"), device="cuda")
+        rc = fa.fa_fwd_split_qk(_ptr(qd), _ptr(kd), _ptr(vd), _ptr(o_ref), _ptr(l_ref), B, H, Nq, Nk, d, causal,
+                                scale, code, splits, _ptr(ws), need, stream)
+        assert rc == fa.FA_OK, fa.fa_status_string(rc)
+        rc = fa.fa_fwd_split_qk_noalloc(_ptr(qd), _ptr(kd), _ptr(vd), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, causal,
+                                        scale, code, splits, stream)
+        assert rc == fa.FA_OK, fa.fa_status_string(rc)
+        torch.cuda.synchronize()
+        # the same kernels on the same inputs: bit-identical outputs
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+        o64, l64 = oracle.attention_fwd(q, k, v, bool(causal), scale)
+        err_o = float(np.abs(o.cpu().double().numpy() - o64).max())
+        err_l = float((np.abs(lse.cpu().double().numpy() - l64) / np.maximum(1.0, np.abs(l64))).max())
+        print(f"[parity] noalloc max|dO|={err_o:.3e} max rel dlse={err_l:.3e}", flush=True)
+        assert err_o <= TOL_O[q.dtype] and err_l <= 1e-3
+

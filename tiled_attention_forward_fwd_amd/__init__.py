@@ -28,7 +28,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1
 
 # Entry points declared in include/fa.h.
-EXPORTED = ("fa_fwd", "fa_fwd_qk", "fa_fwd_split_qk", "fa_split_count", "fa_split_workspace_bytes",
+EXPORTED = ("fa_fwd", "fa_fwd_qk", "fa_fwd_split_qk", "fa_fwd_split_qk_noalloc", "fa_split_count",
+            "fa_split_workspace_bytes",
             "fa_fwd_masked", "fa_fwd_split_masked", "fa_fwd_f32", "fa_f32_workspace_bytes", "fa_bwd", "fa_bwd_qk", "fa_bwd_masked",
             "fa_status_string", "fa_tile_counts",
             "fa_tile_counts_qk", "fa_tile_counts_masked", "fa_plan", "fa_plan_qk", "fa_plan_masked")
@@ -72,6 +73,9 @@ def load_library(path=LIB_PATH):
     lib.fa_fwd_split_qk.restype = ctypes.c_int
     lib.fa_fwd_split_qk.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.fa_fwd_split_qk_noalloc.restype = ctypes.c_int
+    lib.fa_fwd_split_qk_noalloc.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.fa_fwd_masked.restype = ctypes.c_int
     lib.fa_fwd_masked.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 8 + [
         ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
@@ -148,6 +152,17 @@ def fa_fwd_split_qk(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, n_sp
     return load_library().fa_fwd_split_qk(q, k, v, o, lse, int(B), int(H), int(Nq), int(Nk), int(d),
                                           int(causal), float(scale), int(dtype), int(n_splits),
                                           workspace, int(workspace_bytes), stream)
+
+
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024  # FA_NOALLOC_SCRATCH_BYTES of include/fa.h
+
+
+def fa_fwd_split_qk_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, n_splits, stream):
+    """Direct call of the C entry point with raw pointers (ints); returns the status.
+    The split partials go to the library's static scratch (no allocation)."""
+    return load_library().fa_fwd_split_qk_noalloc(q, k, v, o, lse, int(B), int(H), int(Nq), int(Nk),
+                                                  int(d), int(causal), float(scale), int(dtype),
+                                                  int(n_splits), stream)
 
 
 def fa_fwd_masked(q, k, v, o, lse, B, H, Nq, Nk, d, causal, window_left, window_right, key_lens,

@@ -11,10 +11,19 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_launch.h"
 #include "fa_tiles.h"
+
+// The split workspace of fa_fwd_split_qk_noalloc: a scratch array of the
+// library's own, one copy on each GPU (at its own address there), allocated
+// with the code object and held until the process ends. Host code never
+// passes `scratch` itself to a kernel (in host code the name stands for a
+// host-side shadow): it looks up the device address on each GPU once
+// (noalloc_scratch) and passes that.
+static __device__ __align__(256) float scratch[FA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace {
 
@@ -157,6 +166,31 @@ int hip_status(hipError_t e)
 double causal_area(double Nq, double Nk)
 {
     return Nq <= Nk ? 0.5 * Nq * Nq : 0.5 * Nk * Nk + (Nq - Nk) * Nk;
+}
+
+// Device address of `scratch` on the current device, looked up with
+// hipGetSymbolAddress on the first call there (with that device current) and
+// kept per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices];
+
+int noalloc_scratch(void** addr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_UNSUPPORTED, "device index past the scratch table (64)");
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (!p) return fail(FA_ERR_HIP, "hipGetSymbolAddress returned no address for the scratch array");
+        g_scratch_addr[dev] = p;
+    }
+    *addr = g_scratch_addr[dev];
+    return FA_OK;
 }
 
 // Number of j in [a, b) that lie in [u0, u1) or in [w0, w1).
@@ -514,6 +548,31 @@ int fa_fwd_split_qk(const void* q, const void* k, const void* v, void* o, float*
     a.split = true;
     a.n_splits = n_splits;
     a.workspace = (float*)workspace;
+    return hip_status(fa::launch_forward(a));
+}
+
+int fa_fwd_split_qk_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                            int Nq, int Nk, int d, int causal, float scale, int dtype, int n_splits, void* stream)
+{
+    g_msg[0] = 0;
+    int rc = check_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype);
+    if (rc != FA_OK) return rc;
+    if (n_splits < 1 || n_splits > (Nk + 63) / 64)
+        return fail(FA_ERR_INVALID_ARG, "n_splits must be between 1 and ceil(Nk / 64)");
+    if ((int64_t)B * H * ((Nq + 127) / 128) * n_splits > (int64_t)UINT32_MAX)
+        return fail(FA_ERR_INVALID_ARG, "B*H*ceil(Nq/128)*n_splits exceeds the grid limit");
+    const int64_t need = fa_split_workspace_bytes(B, H, Nq, d, n_splits);
+    if (need > (int64_t)FA_NOALLOC_SCRATCH_BYTES)
+        return fail(FA_ERR_UNSUPPORTED,
+                    "the split workspace (n_splits*B*H*Nq*(D+1)*4 bytes) exceeds the static scratch "
+                    "(FA_NOALLOC_SCRATCH_BYTES = 16 MiB); use fa_fwd_split_qk with a workspace");
+    void* ws = nullptr;
+    rc = noalloc_scratch(&ws);
+    if (rc != FA_OK) return rc;
+    fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, stream);
+    a.split = true;
+    a.n_splits = n_splits;
+    a.workspace = (float*)ws;
     return hip_status(fa::launch_forward(a));
 }
 
