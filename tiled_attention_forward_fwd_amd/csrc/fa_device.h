@@ -239,39 +239,6 @@ __device__ __forceinline__ float pair_sum<_Float16>(float acc, float, float, _Fl
     return __builtin_amdgcn_fdot2(v, one, acc, false);
 }
 
-// bf16 inputs keep a second running sum, of the rounded P that enter P.V,
-// and O is normalised by it (the logsumexp still takes the sum of the fp32
-// P): numerator and denominator then weigh each key alike, so the rounding
-// of a key that carries most of a row's weight cancels in O / l. With the
-// lazily updated max (softmax_finish) that key's P is rarely 1 and its
-// rounding is up to 2^-8 of itself; normalised by the fp32 sum it would move
-// a dominated output by up to one bf16 ulp. fp16 sums the rounded P for both
-// (pair_sum), so its l already is that sum.
-template <typename T>
-struct SumsRounded : std::false_type {};
-template <>
-struct SumsRounded<__bf16> : std::true_type {};
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// The share of P.V slot `db` (one of the DB MFMAs of a k-step) in that sum:
-// the four pairs of the k-step's rounded P vector are spread evenly over its
-// DB MFMAs, one v_dot2c_f32_bf16 with (1, 1) per pair (exact products, fp32
-// sums). Nothing for fp16.
-template <typename T, int DB>
-__device__ __forceinline__ void add_rounded_slot(const typename Mma<T>::vec8& p, int db, float& acc)
-{
-    if constexpr (SumsRounded<T>::value) {
-        static_assert(DB == 2 || DB == 4, "pairs per slot");
-        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-        for (int i = db * 4 / DB; i < (db + 1) * 4 / DB; ++i) {
-            const bf16x2 pair = {p[2 * i], p[2 * i + 1]};
-            acc = __builtin_amdgcn_fdot2_f32_bf16(pair, one, acc, false);
-        }
-    }
-}
-
 // exp2 / row-sum / convert of the score pair (e, e + 1) of one query row (e
 // even; element e of the tile is accumulator block e / 16, row e % 16), into
 // the P^T operand vector that holds it.
@@ -426,26 +393,36 @@ __device__ __forceinline__ void exp_tile(const f32x16 (&s)[QB][KB], const float 
 // Online softmax with a lazily updated max. The exponentials of a tile are
 // taken against the running max m of the earlier tiles; the row max of the
 // tile itself is only needed when that makes some P large. The test is on the
-// lane's partial row sum (32 of the tile's 64 keys), which bounds every P of
-// the lane: while it stays <= 2^12 the tile is accepted as it is. P <= 2^12
-// is far inside the fp16/bf16 range, the accumulators cannot overflow, and
-// O / l and m + log2(l) are unchanged because O and l carry the same factor.
+// lane's partial row sum rs (32 of the tile's 64 keys), which bounds every P
+// of the lane. The tile is accepted as it is while
+//   * rs <= 2^12: P <= 2^12 is far inside the fp16/bf16 range, the
+//     accumulators cannot overflow, and O / l and m + log2(l) are unchanged
+//     because O and l carry the same factor; and
+//   * rs <= 4 l, l the lane's running sum of the earlier tiles: no key of the
+//     tile then carries more than 4/5 of the lane's sum so far. A key that
+//     outweighs the rest of its row is accepted only while it sits at the
+//     running max, where its P is 1 and rounds to the input type exactly; at
+//     P = 2^k (0 < k <= 12) its rounding (up to 2^-8 of itself for bf16)
+//     would move a row dominated by it by up to one output ulp.
 // Otherwise (always on the first tile, where m is still the initial -1e30,
-// and when the scores grew by more than about 2^12 over m) the wave takes the
-// true row max, rescales O and l by alpha = 2^(m_old - m_new) and recomputes
-// the tile's P (the update of "Programming an attention kernel in Triton",
-// online softmax). The branch is wave-uniform.
+// when the scores grew by more than about 2^12 over m, and when a tile's keys
+// outweigh the row so far) the wave takes the true row max, rescales O and l
+// by alpha = 2^(m_old - m_new) and recomputes the tile's P (the update of
+// "Programming an attention kernel in Triton", online softmax). The branch is
+// wave-uniform. On iid N(0,1) inputs the second rule adds almost no refresh
+// beyond the first tile's.
 constexpr float kLaneSumBound = 4096.0f;
+constexpr float kLaneSumGrowth = 4.0f;
 
 template <typename T, int QB, int KB, int DB, int KT, bool BS>
 __device__ __forceinline__ void softmax_finish(const f32x16 (&s)[QB][KB], f32x16 (&o)[QB][DB],
-                                               float (&m_run)[QB], float (&l_run)[QB], float (&lr_run)[QB],
-                                               float c_log2, typename Mma<T>::vec8 (&p)[QB][KT],
-                                               float (&rs)[QB])
+                                               float (&m_run)[QB], float (&l_run)[QB], float c_log2,
+                                               typename Mma<T>::vec8 (&p)[QB][KT], float (&rs)[QB])
 {
     bool bad = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) bad = bad || !(rs[qb] <= kLaneSumBound);
+    for (int qb = 0; qb < QB; ++qb)
+        bad = bad || !(rs[qb] <= kLaneSumBound) || rs[qb] > kLaneSumGrowth * l_run[qb];
     if (__builtin_amdgcn_ballot_w64(bad)) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
@@ -454,7 +431,6 @@ __device__ __forceinline__ void softmax_finish(const f32x16 (&s)[QB][KB], f32x16
             const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
             m_run[qb] = m_new;
             l_run[qb] *= alpha;
-            if constexpr (SumsRounded<T>::value) lr_run[qb] *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
         }
@@ -466,17 +442,16 @@ __device__ __forceinline__ void softmax_finish(const f32x16 (&s)[QB][KB], f32x16
 
 template <typename T, int QB, int KB, int DB, int KT, bool BS>
 __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[QB][KB], f32x16 (&o)[QB][DB],
-                                             float (&m_run)[QB], float (&l_run)[QB], float (&lr_run)[QB],
-                                             float c_log2, typename Mma<T>::vec8 (&p)[QB][KT])
+                                             float (&m_run)[QB], float (&l_run)[QB], float c_log2,
+                                             typename Mma<T>::vec8 (&p)[QB][KT])
 {
     float rs[QB];
     exp_tile<T, QB, KB, KT, BS>(s, m_run, c_log2, p, rs);
-    softmax_finish<T, QB, KB, DB, KT, BS>(s, o, m_run, l_run, lr_run, c_log2, p, rs);
+    softmax_finish<T, QB, KB, DB, KT, BS>(s, o, m_run, l_run, c_log2, p, rs);
 }
 
 // O^T += V^T P^T (operand layout at vt_operand). Each V operand feeds QB
-// MFMAs; the t-major order consumes P in the order it is produced. (The
-// backward's products of the same shape use this form.)
+// MFMAs; the t-major order consumes P in the order it is produced.
 template <typename T, int D, int QB, int DB, int KT>
 __device__ __forceinline__ void pv_tile(const typename Mma<T>::vec8 (&p)[QB][KT],
                                         const uint16_t* __restrict__ vts, f32x16 (&o)[QB][DB], int lane,
@@ -494,35 +469,13 @@ __device__ __forceinline__ void pv_tile(const typename Mma<T>::vec8 (&p)[QB][KT]
     }
 }
 
-// The forward's P.V of a tile: as above, and for bf16 the rounded P also go
-// into lr (add_rounded_slot), between the MFMAs.
-template <typename T, int D, int QB, int DB, int KT>
-__device__ __forceinline__ void pv_tile(const typename Mma<T>::vec8 (&p)[QB][KT],
-                                        const uint16_t* __restrict__ vts, f32x16 (&o)[QB][DB], int lane,
-                                        int hh, float (&lr)[QB])
-{
-    typedef typename Mma<T>::vec8 vec8;
-#pragma unroll
-    for (int t = 0; t < KT; ++t) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const vec8 a = vt_operand<vec8, D>(vts, t, db, lane, hh);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                o[qb][db] = Mma<T>::run(a, p[qb][t], o[qb][db]);
-                add_rounded_slot<T, DB>(p[qb][t], db, lr[qb]);
-            }
-        }
-    }
-}
-
 // O^T += V^T P^T of this tile with the exp2 work of the elements [E0, E1)
 // of the next tile's scores sn between the MFMAs (into pn, row sum in rs).
 template <typename T, int D, int DB, int KT, int KB, int E0, int E1>
 __device__ __forceinline__ void pv_with_exp(const typename Mma<T>::vec8 (&p)[1][KT],
                                             const uint16_t* __restrict__ vts, f32x16 (&o)[1][DB], int lane, int hh,
                                             const f32x16 (&sn)[1][KB], float m, float c_log2,
-                                            typename Mma<T>::vec8 (&pn)[1][KT], float& rs, float (&lr)[1])
+                                            typename Mma<T>::vec8 (&pn)[1][KT], float& rs)
 {
     typedef typename Mma<T>::vec8 vec8;
     static_assert(E0 >> 4 == (E1 - 1) >> 4, "one block");
@@ -536,7 +489,6 @@ __device__ __forceinline__ void pv_with_exp(const typename Mma<T>::vec8 (&p)[1][
         for (int db = 0; db < DB; ++db) {
             const vec8 a = vt_operand<vec8, D>(vts, t, db, lane, hh);
             o[0][db] = Mma<T>::run(a, p[0][t], o[0][db]);
-            add_rounded_slot<T, DB>(p[0][t], db, lr[0]);
             exp_slot<T, KB, KT, E0, E1, n_mfma, true>(t * DB + db, sn[0], m, c_log2, pn[0], acc);
         }
     }
@@ -545,12 +497,12 @@ __device__ __forceinline__ void pv_with_exp(const typename Mma<T>::vec8 (&p)[1][
 
 template <typename T, int D, int QB, int KB, int DB, int KT, bool BS>
 __device__ __forceinline__ void softmax_pv(const f32x16 (&s)[QB][KB], const uint16_t* __restrict__ vts,
-                                           f32x16 (&o)[QB][DB], float (&m_run)[QB], float (&l_run)[QB],
-                                           float (&lr_run)[QB], float c_log2, int lane, int hh)
+                                           f32x16 (&o)[QB][DB], float (&m_run)[QB],
+                                           float (&l_run)[QB], float c_log2, int lane, int hh)
 {
     typename Mma<T>::vec8 p[QB][KT];
-    softmax_tile<T, QB, KB, DB, KT, BS>(s, o, m_run, l_run, lr_run, c_log2, p);
-    pv_tile<T, D, QB, DB, KT>(p, vts, o, lane, hh, lr_run);
+    softmax_tile<T, QB, KB, DB, KT, BS>(s, o, m_run, l_run, c_log2, p);
+    pv_tile<T, D, QB, DB, KT>(p, vts, o, lane, hh);
 }
 
 // Instruction order of a pipelined tile. The scores of the next tile are
@@ -574,10 +526,7 @@ __device__ __forceinline__ void order_scores_block()
     for (int i = 0; i < lead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
 }
 
-// VALU: vector instructions placed after each MFMA group (the rounded row
-// sums of bf16, add_rounded_slot), which would otherwise drift to the start
-// of the next block, ahead of its MFMAs.
-template <int D, int WAVES, int QB, int VALU = 0>
+template <int D, int WAVES, int QB>
 __device__ __forceinline__ void order_pv_block()
 {
     typedef Cfg<D, WAVES, QB> C;
@@ -587,14 +536,10 @@ __device__ __forceinline__ void order_pv_block()
 #pragma unroll
     for (int i = 0; i < n_ops - lead; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
-        if constexpr (VALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
 #pragma unroll
-    for (int i = 0; i < lead; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
-        if constexpr (VALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
-    }
+    for (int i = 0; i < lead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
 }
 
 // Keeps the computation of x where it is written: an empty asm statement that

@@ -146,26 +146,22 @@ __device__ __forceinline__ void padded_batch_tile(int n_qt, int heads, const int
     qt = j / (uint32_t)heads;
 }
 
-// Epilogue: O = O_acc / ln in the input type, lse = (m + log2 l) * ln 2,
-// where l is the running sum of the fp32 P and ln the sum that normalises O
-// (the rounded P for bf16, SumsRounded; l itself for fp16).
+// Epilogue: O = O_acc / l in the input type, lse = (m + log2 l) * ln 2.
 // EMPTY: rows may have seen no key (masks); such a row has l = 0 and gets
 // O = 0 and lse = -inf.
 // PADDED: rows are dm elements apart and only dims below dm are written.
 template <typename T, int D, int QB, int DB, bool EMPTY, bool PADDED>
 __device__ __forceinline__ void store_outputs(const f32x16 (&oacc)[QB][DB], const float (&m_run)[QB],
-                                              const float (&l_run)[QB], const float (&ln_run)[QB],
-                                              const int (&qrow)[QB], int n_rows, T* __restrict__ oh,
-                                              float* __restrict__ lseh, int hh, int dm)
+                                              const float (&l_run)[QB], const int (&qrow)[QB], int n_rows,
+                                              T* __restrict__ oh, float* __restrict__ lseh, int hh, int dm)
 {
     const int stride = PADDED ? dm : D;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float l_tot = swap_halves_sum(l_run[qb]);
-        const float ln_tot = swap_halves_sum(ln_run[qb]);
         if (qrow[qb] < n_rows) {
             const bool seen = !EMPTY || l_tot > 0.f;
-            const float inv = seen ? 1.0f / ln_tot : 0.f;
+            const float inv = seen ? 1.0f / l_tot : 0.f;
             T* orow = oh + (int64_t)qrow[qb] * stride;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
@@ -194,16 +190,14 @@ __device__ __forceinline__ void store_outputs(const f32x16 (&oacc)[QB][DB], cons
 // written (dm a multiple of 8, so rows stay 16-byte aligned).
 template <typename T, int D, int DB, bool EMPTY, bool PADDED>
 __device__ __forceinline__ void store_outputs_staged(const f32x16 (&oacc)[1][DB], const float (&m_run)[1],
-                                                     const float (&l_run)[1], const float (&ln_run)[1],
-                                                     const int (&qrow)[1], int row0, int n_rows,
-                                                     T* __restrict__ oh, float* __restrict__ lseh, int hh,
-                                                     int lane, uint16_t* __restrict__ stage, int dm)
+                                                     const float (&l_run)[1], const int (&qrow)[1], int row0,
+                                                     int n_rows, T* __restrict__ oh, float* __restrict__ lseh,
+                                                     int hh, int lane, uint16_t* __restrict__ stage, int dm)
 {
     constexpr int RS = D + 8;  // LDS row stride in elements
     const float l_tot = swap_halves_sum(l_run[0]);
-    const float ln_tot = swap_halves_sum(ln_run[0]);
     const bool seen = !EMPTY || l_tot > 0.f;
-    const float inv = seen ? 1.0f / ln_tot : 0.f;
+    const float inv = seen ? 1.0f / l_tot : 0.f;
     const int l32 = lane & 31;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -241,17 +235,15 @@ __device__ __forceinline__ void store_outputs_staged(const f32x16 (&oacc)[1][DB]
 // and lse = -inf, which gives it weight zero in the merge.
 template <int D, int QB, int DB>
 __device__ __forceinline__ void store_partials(const f32x16 (&oacc)[QB][DB], const float (&m_run)[QB],
-                                               const float (&l_run)[QB], const float (&ln_run)[QB],
-                                               const int (&qrow)[QB], int n_rows, float* __restrict__ ws_o,
-                                               float* __restrict__ ws_lse, int hh)
+                                               const float (&l_run)[QB], const int (&qrow)[QB], int n_rows,
+                                               float* __restrict__ ws_o, float* __restrict__ ws_lse, int hh)
 {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float l_tot = swap_halves_sum(l_run[qb]);
-        const float ln_tot = swap_halves_sum(ln_run[qb]);
         if (qrow[qb] < n_rows) {
             const bool seen = l_tot > 0.f;
-            const float inv = seen ? 1.0f / ln_tot : 0.f;
+            const float inv = seen ? 1.0f / l_tot : 0.f;
             float* orow = ws_o + (int64_t)qrow[qb] * D;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
@@ -411,9 +403,6 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     // kernel (fused or not, first tile, rescaled tile) uses the same order, so
     // the masked and unmasked kernels of one head dim agree bit for bit.
     constexpr bool kBS = D == 64;
-    // vector instructions per P.V MFMA in a block without exp work: the
-    // rounded row sums of bf16 (add_rounded_slot), 4 / DB pairs per MFMA
-    constexpr int kPvValu = SumsRounded<T>::value ? 4 / C::DB * QB : 0;
 
     int qrow[QB];
     vec8 qf[QB][C::DS];
@@ -449,26 +438,14 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     }
 
     f32x16 oacc[QB][C::DB];
-    // l_run: sum of the fp32 P (the logsumexp); lr_run: bf16 only, sum of the
-    // rounded P that enter P.V, which normalises O (SumsRounded)
-    float m_run[QB], l_run[QB], lr_run[QB];
+    float m_run[QB], l_run[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) oacc[qb][db] = (f32x16){};
         m_run[qb] = -1e30f;
         l_run[qb] = 0.f;
-        lr_run[qb] = 0.f;
     }
-    // Ends a P.V block: the rounded row sums it adds are complete here (pin_reg),
-    // so the compiler keeps them between its MFMAs instead of sinking them past
-    // the loop branch into the next block, ahead of that block's MFMAs.
-    auto pin_sums = [&]() {
-        if constexpr (SumsRounded<T>::value) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) pin_reg(lr_run[qb]);
-        }
-    };
 
     // LDS: K tiles in buffers 0/1, V tiles in buffers 2/3. Iteration j reads
     // K_{j+1} (scores of the next tile) and V_j (P.V of this tile) while the
@@ -581,7 +558,10 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
         // M: the tile gets the mask; G: per-wave limits apply (masked tiles,
         // and every tile of a split launch)
         constexpr bool M = decltype(masked)::value, G = M || SPLIT;
-        if (j + 2 < je) issue(kbuf(j), krs, (j + 2) * C::BN);
+        // K_{j+2} is copied even past the last tile: the copy stays inside the
+        // head (the descriptor reads zeros past it) and nothing reads that
+        // buffer afterwards, and the step has no branch before its MFMAs.
+        issue(kbuf(j), krs, (j + 2) * C::BN);
         issue(vbuf(j + 1), vrs, (j + 1) * C::BN);
         if constexpr (kSplitExp) {
             // sc is masked and its first block's P is in pc (rc): they were
@@ -601,20 +581,18 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
                     rs[0] = exp_range<T, C::KB, C::KT, 16, 32>(sc[0], m_run[0], c_log2, pc[0]);
                 }
                 rs[0] = rc + rs[0];
-                softmax_finish<T, QB, C::KB, C::DB, C::KT, kBS>(sc, oacc, m_run, l_run, lr_run, c_log2, pc, rs);
+                softmax_finish<T, QB, C::KB, C::DB, C::KT, kBS>(sc, oacc, m_run, l_run, c_log2, pc, rs);
                 if (!G || wave_sees(j + 1)) {
                     if (M || j + 1 >= u_hi) apply_mask(sn[0], j + 1, 0);
                     pv_with_exp<T, D, C::DB, C::KT, C::KB, 0, 16>(pc, vbuf(j), oacc, lane, hh, sn, m_run[0], c_log2,
-                                                                  pn, rn, lr_run);
+                                                                  pn, rn);
                     order_pv_block<D, WAVES, QB>();
                     pin_regs(pn[0][0]);
                     pin_regs(pn[0][1]);
                     pin_reg(rn);
-                    pin_sums();
                 } else {
-                    pv_tile<T, D, QB, C::DB, C::KT>(pc, vbuf(j), oacc, lane, hh, lr_run);
-                    order_pv_block<D, WAVES, QB, kPvValu>();
-                    pin_sums();
+                    pv_tile<T, D, QB, C::DB, C::KT>(pc, vbuf(j), oacc, lane, hh);
+                    order_pv_block<D, WAVES, QB>();
                 }
             }
         } else if constexpr (kFuseExp) {
@@ -631,10 +609,9 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
                 } else {
                     exp_tile<T, QB, C::KB, C::KT, kBS>(sc, m_run, c_log2, p, rs);
                 }
-                softmax_finish<T, QB, C::KB, C::DB, C::KT, kBS>(sc, oacc, m_run, l_run, lr_run, c_log2, p, rs);
-                pv_tile<T, D, QB, C::DB, C::KT>(p, vbuf(j), oacc, lane, hh, lr_run);
-                order_pv_block<D, WAVES, QB, kPvValu>();
-                pin_sums();
+                softmax_finish<T, QB, C::KB, C::DB, C::KT, kBS>(sc, oacc, m_run, l_run, c_log2, p, rs);
+                pv_tile<T, D, QB, C::DB, C::KT>(p, vbuf(j), oacc, lane, hh);
+                order_pv_block<D, WAVES, QB>();
             }
         } else {
             if (!G || wave_sees(j + 1)) {
@@ -645,10 +622,8 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
                     if (M) apply_mask(sc[qb], j, qb);
-                softmax_pv<T, D, QB, C::KB, C::DB, C::KT, kBS>(sc, vbuf(j), oacc, m_run, l_run, lr_run, c_log2,
-                                                               lane, hh);
-                order_pv_block<D, WAVES, QB, kPvValu>();
-                pin_sums();
+                softmax_pv<T, D, QB, C::KB, C::DB, C::KT, kBS>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
+                order_pv_block<D, WAVES, QB>();
             }
         }
         stage_barrier();
@@ -667,19 +642,16 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
             if (!G || wave_sees(j)) {
                 float rs[QB];
                 rs[0] = rc + exp_range<T, C::KB, C::KT, 16, 32>(sc[0], m_run[0], c_log2, pc[0]);
-                softmax_finish<T, QB, C::KB, C::DB, C::KT, kBS>(sc, oacc, m_run, l_run, lr_run, c_log2, pc, rs);
-                pv_tile<T, D, QB, C::DB, C::KT>(pc, vbuf(j), oacc, lane, hh, lr_run);
-                order_pv_block<D, WAVES, QB, kPvValu>();
-                pin_sums();
+                softmax_finish<T, QB, C::KB, C::DB, C::KT, kBS>(sc, oacc, m_run, l_run, c_log2, pc, rs);
+                pv_tile<T, D, QB, C::DB, C::KT>(pc, vbuf(j), oacc, lane, hh);
+                order_pv_block<D, WAVES, QB>();
             }
         } else if (!G || wave_sees(j)) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
                 if (M) apply_mask(sc[qb], j, qb);
-            softmax_pv<T, D, QB, C::KB, C::DB, C::KT, kBS>(sc, vbuf(j), oacc, m_run, l_run, lr_run, c_log2, lane,
-                                                           hh);
-            order_pv_block<D, WAVES, QB, kPvValu>();
-            pin_sums();
+            softmax_pv<T, D, QB, C::KB, C::DB, C::KT, kBS>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
+            order_pv_block<D, WAVES, QB>();
         }
     };
     auto shift_scores = [&]() {
@@ -729,17 +701,16 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
             last_step(masked_t(), j, sa, pa, ra);
     }
 
-    const float (&ln_run)[QB] = SumsRounded<T>::value ? lr_run : l_run;  // normalises O
     if (SPLIT) {
         const int64_t slot = ((int64_t)split * (gridDim.x / ((uint32_t)n_splits * (uint32_t)n_qt)) + bh) * Nq;
-        store_partials<D, QB, C::DB>(oacc, m_run, l_run, ln_run, qrow, Nq, ws_o + slot * D, ws_lse + slot, hh);
+        store_partials<D, QB, C::DB>(oacc, m_run, l_run, qrow, Nq, ws_o + slot * D, ws_lse + slot, hh);
     } else if constexpr (kStaged) {
         __syncthreads();  // every wave is past its last read of K and V
-        store_outputs_staged<T, D, C::DB, MASKS, PADDED>(oacc, m_run, l_run, ln_run, qrow, q0 + wave * 32, Nq,
-                                                         o + q_off, lse + (int64_t)bh * Nq, hh, lane,
-                                                         smem + wave * 32 * (D + 8), dm);
+        store_outputs_staged<T, D, C::DB, MASKS, PADDED>(oacc, m_run, l_run, qrow, q0 + wave * 32, Nq, o + q_off,
+                                                         lse + (int64_t)bh * Nq, hh, lane, smem + wave * 32 * (D + 8),
+                                                         dm);
     } else {
-        store_outputs<T, D, QB, C::DB, MASKS, PADDED>(oacc, m_run, l_run, ln_run, qrow, Nq, o + q_off,
+        store_outputs<T, D, QB, C::DB, MASKS, PADDED>(oacc, m_run, l_run, qrow, Nq, o + q_off,
                                                       lse + (int64_t)bh * Nq, hh, dm);
     }
 }
