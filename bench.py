@@ -19,7 +19,10 @@ with amd-smi while the step loops, times a plain hipBLASLt bf16 GEMM on random o
 context for the roofline, and times the fp64 oracle on the host (cpu_baseline).
 
 Other modes (used to collect counters; each runs a few launches only):
-    --profile-kernels   a few launches of each headline kernel, nothing else
+    --profile-kernels   a few launches of each kernel of --profile-set (d128: the
+                        headline, the default; d64; long: the long-context causal
+                        configuration with and without q x 4), nothing else
+    --profile-timed     the same workloads after a warmup (for kernel traces)
     --copy-calibration  a plain device-to-device copy of a known size
     --profile-decode    the split-key decode path (one query x 16384 keys, B=1 H=32)
     --profile-masked    the padding and sliding-window workloads of the sweep
@@ -513,17 +516,32 @@ def profile_workloads(args, workloads, label):
     print(json.dumps({"profiled": label, "workloads": workloads, "calls": calls}))
 
 
+# Workload sets of --profile-kernels / --profile-set: the headline (d=128), the
+# headline at d=64, and the long-context causal configuration with and without
+# the heavy-tailed q.
+PROFILE_SETS = {
+    "d128": [HEADLINE],
+    "d64": [dict(B=4, H=16, N=4096, d=64, dtype="bf16", seed=6)],
+    "long": [dict(B=1, H=32, N=16384, d=128, dtype="bf16", seed=8, flags=(1,)),
+             dict(B=1, H=32, N=16384, d=128, dtype="bf16", seed=9, q_scale=4.0, flags=(1,))],
+}
+
+
 def profile_kernels(args):
-    """A few launches of each headline kernel (for rocprofv3 counter passes)."""
+    """A few launches of each kernel of a profile set, nothing else (for rocprofv3
+    counter passes): each workload and causal flag in order, `steps` launches."""
     import torch
     import tiled_attention_forward_fwd_amd as fa
     dev = torch.device("cuda:0")
-    _, _, _, qd, kd, vd = make_inputs(HEADLINE, dev)
-    for causal in (False, True):
-        for _ in range(args.steps):
-            fa.fwd(qd, kd, vd, causal=causal)
-    torch.cuda.synchronize()
-    print(json.dumps({"profiled": "fa_fwd bf16 d=128 N=4096 B=4 H=16", "launches_each": args.steps}))
+    for cfg in PROFILE_SETS[args.profile_set]:
+        _, _, _, qd, kd, vd = make_inputs(cfg, dev)
+        for causal in cfg.get("flags", (False, True)):
+            for _ in range(args.steps):
+                fa.fwd(qd, kd, vd, causal=bool(causal))
+        torch.cuda.synchronize()
+        del qd, kd, vd
+    print(json.dumps({"profiled": args.profile_set, "workloads": PROFILE_SETS[args.profile_set],
+                      "launches_each": args.steps}))
 
 
 DECODE = dict(B=1, H=32, Nq=1, N=16384, d=128, dtype="bf16", seed=10)
@@ -596,7 +614,12 @@ def main():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--no-sweep-oracle", dest="sweep_oracle", action="store_false",
                     help="skip the per-configuration oracle timing of --sweep")
-    ap.add_argument("--profile-kernels", action="store_true")
+    ap.add_argument("--profile-kernels", action="store_true",
+                    help="`steps` launches of each kernel of --profile-set, nothing else")
+    ap.add_argument("--profile-set", default="d128", choices=sorted(PROFILE_SETS),
+                    help="workloads of --profile-kernels and --profile-timed")
+    ap.add_argument("--profile-timed", action="store_true",
+                    help="the --profile-set workloads with a warmup before the counted calls (kernel traces)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--profile-decode", action="store_true",
                     help="split-key decode calls only (one query x 16384 keys), for rocprofv3")
@@ -629,6 +652,9 @@ def main():
         return profile_workloads(args, MASKED_WORKLOADS, "masked workloads")
     if args.profile_variants:
         return profile_workloads(args, VARIANT_WORKLOADS, "head-dim and fp32 workloads")
+    if args.profile_timed:
+        return profile_workloads(args, [dict(w, flags=w.get("flags", (0, 1))) for w in PROFILE_SETS[args.profile_set]],
+                                 f"profile set {args.profile_set}")
 
     out, (q, k, v) = headline(args)
     if args.backward:
