@@ -324,8 +324,9 @@ typedef struct {
     int lds_bytes;          /* LDS per workgroup */
     int64_t workgroups;     /* grid size */
     int64_t pairs_visited;  /* visited (query tile, key tile) pairs, all heads */
-    double mfma_flops;      /* FLOPs the matrix cores execute, D the kernel's
-                               head dim (64 or 128): 2*32*64*D for each block of
+    double mfma_flops;      /* FLOPs the matrix cores execute, D the head dim
+                               rounded up to a multiple of 32 (the dims the
+                               forward kernel computes): 2*32*64*D for each block of
                                32 query rows x 64 keys of which a wave computes
                                S = Q K^T, and as much for each it computes P V.
                                Every visited tile pair counts, masked ones too,

@@ -469,13 +469,15 @@ def test_split_count_suggestion(lib):
 @pytest.mark.parametrize("d", [8, 16, 32, 40, 48, 56, 72, 80, 96, 112, 120])
 def test_plan_other_head_dims(lib, d):
     D = 64 if d <= 64 else 128
+    DC = -(-d // 32) * 32  # the dims the kernel's MFMAs cover
     for causal in (0, 1):
         p = fa.fa_plan_qk(2, 8, 1000, 1500, d, causal, fa.FA_DTYPE_BF16)
         ref = fa.fa_plan_qk(2, 8, 1000, 1500, D, causal, fa.FA_DTYPE_BF16)
         # same grid and tiles as the kernel head dim; algorithmic work at d,
-        # executed MFMA work at the kernel head dim
-        for key in ("block_m", "block_n", "threads", "lds_bytes", "workgroups", "pairs_visited", "mfma_flops"):
+        # executed MFMA work at d rounded up to 32
+        for key in ("block_m", "block_n", "threads", "lds_bytes", "workgroups", "pairs_visited"):
             assert p[key] == ref[key], key
+        assert p["mfma_flops"] == ref["mfma_flops"] * DC / D
         assert p["algo_flops"] == ref["algo_flops"] * d / D
         assert p["algo_bytes"] == 4 * 2 * 8 * (1000 + 1500) * d + 4 * 2 * 8 * 1000
     assert fa.fa_split_workspace_bytes(1, 4, 3, d, 5) == 5 * 4 * 3 * (D + 1) * 4

@@ -178,16 +178,18 @@ def test_backward_head_dims_match_oracle(case, causal):
 @pytest.mark.parametrize("d,D", [(96, 128), (40, 64), (120, 128), (8, 64)])
 def test_backward_head_dim_equals_the_native_kernel_on_zero_padded_inputs(d, D):
     # same tiles, same LDS contents and the same MFMA sums: bit for bit, and
-    # the native kernel's gradients past d are zero
+    # the native kernel's gradients past d are zero. Both backward calls take
+    # the same O and lse (the native forward's), so only the backward is
+    # compared (the forward at 96 computed dims adds its row sums in another
+    # order than the d = 128 kernel)
     B, H, N = 2, 3, 333
     q, k, v = (t.cuda() for t in make_qkv(B, H, N, d, "bf16", 600 + d))
     dout = make_qkv(B, H, N, d, "bf16", 607 + d)[0].cuda()
     pad = lambda t: torch.nn.functional.pad(t, (0, D - d)).contiguous()
     sc = fa.default_scale(d)  # the padded calls take d's scale, not D's
     for causal in (False, True):
-        o, lse = fa.fwd(q, k, v, causal=causal, scale=sc, splits=1)
-        g = fa.bwd(q, k, v, o, lse, dout, causal=causal, scale=sc)
         o_n, lse_n = fa.fwd(pad(q), pad(k), pad(v), causal=causal, scale=sc, splits=1)
+        g = fa.bwd(q, k, v, o_n[..., :d].contiguous(), lse_n, dout, causal=causal, scale=sc)
         g_n = fa.bwd(pad(q), pad(k), pad(v), o_n, lse_n, pad(dout), causal=causal, scale=sc)
         torch.cuda.synchronize()
         for name, a, b in zip(("dq", "dk", "dv"), g, g_n):

@@ -1,9 +1,11 @@
 """GPU parity at head dims other than 64 and 128 (a multiple of 8 up to 128),
-which libfa runs with the d = 64 or d = 128 kernel and the missing dims held
-at zero. Checked against the fp64 oracle at the same tolerances as the other
-forward tests (4e-3 fp16 / 3.2e-2 bf16 on O, 1e-3 relative on lse), and bit
-for bit against the d = 64 / 128 kernel on the same inputs zero-padded, which
-must be identical arithmetic.
+which libfa runs with the d = 64 or d = 128 kernel's tiles and the missing
+dims held at zero, computing only d rounded up to 32. Checked against the
+fp64 oracle at the same tolerances as the other forward tests (4e-3 fp16 /
+3.2e-2 bf16 on O, 1e-3 relative on lse), and against the d = 64 / 128 kernel
+on the same inputs zero-padded: bit for bit where the arithmetic is the same
+(the skipped dims only add zeros), within one output ulp where the row sums
+are added in another order (96 computed dims).
 """
 
 import numpy as np
@@ -77,8 +79,12 @@ def test_head_dim_parity(d):
         check(q, k, v, causal, label=f"d={d} N=333 {dtype}")
 
 
-@pytest.mark.parametrize("d,D", [(96, 128), (40, 64), (120, 128), (8, 64)])
+@pytest.mark.parametrize("d,D", [(96, 128), (72, 128), (40, 64), (120, 128), (8, 64), (32, 64)])
 def test_equals_the_native_kernel_on_zero_padded_inputs(d, D):
+    # 96 computed dims sum each row per 32-key block (the d = 64 order), the
+    # d = 128 kernel over all 64 keys of a tile: the fp32 row sums then differ
+    # in their last bits, which moves an output by at most one bf16 ulp
+    same_order = -(-d // 32) * 32 != 96
     # large enough for the 256-row non-causal shape, ragged in N
     for B, H, N in ((8, 16, 1000), (1, 2, 257)):
         q, k, v = make_qkv(B, H, N, d, "bf16", 310 + d)
@@ -88,7 +94,13 @@ def test_equals_the_native_kernel_on_zero_padded_inputs(d, D):
             o, lse = fa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
             o_n, lse_n = fa.fwd(pad(q), pad(k), pad(v), causal=causal, scale=scale)
             torch.cuda.synchronize()
-            assert torch.equal(o, o_n[..., :d]) and torch.equal(lse, lse_n), (d, B, H, N, causal)
+            o_n = o_n[..., :d]
+            if same_order:
+                assert torch.equal(o, o_n) and torch.equal(lse, lse_n), (d, B, H, N, causal)
+            else:
+                a, b = o.float(), o_n.float()
+                assert bool(((a - b).abs() <= 2.0 ** -7 * b.abs()).all()), (d, B, H, N, causal)
+                assert float((lse - lse_n).abs().max()) <= 1e-5, (d, B, H, N, causal)
 
 
 @pytest.mark.parametrize("d,dtype", [(96, "bf16"), (48, "fp16")])

@@ -222,7 +222,7 @@ struct PlanMasks {
 //  * a wave that fuses the exp work with the next scores computes the scores
 //    of j+1 only in a step in which it computes tile j.
 int64_t wave_blocks(int64_t q0, int waves, int64_t Nq, int64_t Nk, bool causal, const PlanMasks* m, int D,
-                    bool padded)
+                    int DC, bool padded)
 {
     const int64_t BM = 32 * waves, BN = fa::block_n(D);
     int64_t jb, je, u_lo, u_hi;
@@ -241,7 +241,7 @@ int64_t wave_blocks(int64_t q0, int waves, int64_t Nq, int64_t Nk, bool causal, 
         u_lo = 0;
         u_hi = sp.unmasked;
     }
-    const bool fused = fa::fuses_exp(D, waves, false, m != nullptr, padded);
+    const bool fused = fa::fuses_exp(DC, waves, false, m != nullptr, padded);
     int64_t blocks = 0;
     for (int w = 0; w < waves; ++w) {
         int64_t n_wave = causal ? std::min(je, (q0 + (w + 1) * 32 - 1) / BN + 1) : je;
@@ -266,8 +266,9 @@ int64_t wave_blocks(int64_t q0, int waves, int64_t Nq, int64_t Nk, bool causal, 
     return blocks;
 }
 
-// FLOPs of one 32 x 64 block of S = Q K^T or of P V at the kernel's head dim.
-double block_flops(int d) { return 2.0 * 32 * 64 * fa::kernel_dim(d); }
+// FLOPs of one 32 x 64 block of S = Q K^T or of P V over the dims the
+// forward kernel computes (d rounded up to 32).
+double block_flops(int d) { return 2.0 * 32 * 64 * fa::compute_dim(d); }
 
 int bwd_checked(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                 void* dq, void* dk, void* dv, float* delta, int B, int H, int Nq, int Nk, int d, int causal,
@@ -379,7 +380,8 @@ int fa_plan_qk(int B, int H, int Nq, int Nk, int d, int causal, int dtype, fa_pl
     const bool padded = d != fa::kernel_dim(d);
     int64_t blocks = 0;
     for (int64_t q0 = 0; q0 < Nq; q0 += bm)
-        blocks += wave_blocks(q0, sh.waves, Nq, Nk, causal != 0, nullptr, fa::kernel_dim(d), padded);
+        blocks += wave_blocks(q0, sh.waves, Nq, Nk, causal != 0, nullptr, fa::kernel_dim(d), fa::compute_dim(d),
+                              padded);
     plan->mfma_flops = block_flops(d) * (double)blocks * (double)bh;
     const double pairs = causal ? causal_area(Nq, Nk) : (double)Nq * (double)Nk;
     plan->algo_flops = 4.0 * (double)bh * pairs * d;
@@ -438,7 +440,7 @@ int fa_plan_masked(int B, int H, int Nq, int Nk, int d, int causal, int window_l
         const PlanMasks pm{window_left, window_right, kl};
         for (int64_t q0 = 0; q0 < Nq; q0 += bm)
             blocks += (double)wave_blocks(q0, sh.waves, Nq, Nk, causal != 0, off ? nullptr : &pm,
-                                          fa::kernel_dim(d), padded);
+                                          fa::kernel_dim(d), fa::compute_dim(d), padded);
         // visible (query, key) pairs, and the keys some row sees (the union
         // of the rows' ranges; lo and hi never decrease with the row)
         int64_t reach = 0;

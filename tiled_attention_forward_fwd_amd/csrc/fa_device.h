@@ -45,10 +45,14 @@ struct Mma<_Float16> {
 constexpr int kXcds = 8;  // XCDs of an MI355X
 
 // Tile shape: head dim D, WAVES waves per workgroup, QB 32-row query blocks
-// per wave, BN = 64 keys per K/V tile.
-template <int D, int WAVES, int QB>
+// per wave, BN = 64 keys per K/V tile. DC: the dims the MFMAs cover, a
+// multiple of 32 up to D; a head dim below D is padded with zeros to D in LDS
+// (the layout and swizzle of D) but computed only up to DC, so the score
+// k-steps and O^T blocks past it are never issued.
+template <int D, int WAVES, int QB, int DC = D>
 struct Cfg {
     static_assert(D == 64 || D == 128, "head dim");
+    static_assert(DC % 32 == 0 && DC >= 32 && DC <= D, "compute dims");
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int BM = 32 * QB * WAVES;    // query rows per workgroup
     static constexpr int BN = 64;                 // keys per tile
@@ -56,8 +60,8 @@ struct Cfg {
     static constexpr int TILE = BN * D;           // elements of one K or V tile (dense)
     static constexpr int LDS_BYTES = 4 * TILE * 2;  // two K and two V tile buffers
     static constexpr int KB = BN / 32;            // 32-key blocks per tile
-    static constexpr int DS = D / 16;             // MFMA k-steps of S^T = K Q^T
-    static constexpr int DB = D / 32;             // 32-row blocks of O^T
+    static constexpr int DS = DC / 16;            // MFMA k-steps of S^T = K Q^T
+    static constexpr int DB = DC / 32;            // 32-row blocks of O^T
     static constexpr int KT = BN / 16;            // MFMA k-steps of O^T += V^T P^T
     static constexpr int LOADS = BN * CPR / THREADS;  // 16-byte copies per thread, each of K and V
     static_assert(LOADS * THREADS == BN * CPR, "tile split");
@@ -510,10 +514,10 @@ __device__ __forceinline__ void softmax_pv(const f32x16 (&s)[QB][KB], const uint
 // a few MFMAs ahead; then the P.V MFMAs follow with their transposed V reads
 // issued ahead. Vector instructions keep their program order between the
 // MFMAs (scores_with_exp places them).
-template <int D, int WAVES, int QB>
+template <int D, int WAVES, int QB, int DC = D>
 __device__ __forceinline__ void order_scores_block()
 {
-    typedef Cfg<D, WAVES, QB> C;
+    typedef Cfg<D, WAVES, QB, DC> C;
     constexpr int n_reads = C::KB * C::DS;  // one K read per QB MFMAs
     constexpr int lead = 4;
     __builtin_amdgcn_sched_group_barrier(0x100, lead, 0);
@@ -526,10 +530,10 @@ __device__ __forceinline__ void order_scores_block()
     for (int i = 0; i < lead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
 }
 
-template <int D, int WAVES, int QB>
+template <int D, int WAVES, int QB, int DC = D>
 __device__ __forceinline__ void order_pv_block()
 {
-    typedef Cfg<D, WAVES, QB> C;
+    typedef Cfg<D, WAVES, QB, DC> C;
     constexpr int n_ops = C::DB * C::KT;  // two V reads per QB MFMAs
     constexpr int lead = 4;
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * lead, 0);

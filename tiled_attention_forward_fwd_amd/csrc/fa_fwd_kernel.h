@@ -267,15 +267,16 @@ __device__ __forceinline__ void store_partials(const f32x16 (&oacc)[QB][DB], con
 // in groups of 16 whose loads are all issued before any is used, so a call
 // with up to 16 chunks makes two rounds of memory reads (the logsumexps, then
 // the partial outputs) instead of one per chunk.
-// The partial rows hold D floats (a PADDED launch's extra dims are zero);
-// O rows are dm elements apart and only dims below dm are written.
-template <typename T, int D>
+// The partial rows are D floats apart and hold the DC computed dims (a PADDED
+// launch's dims past dm are zero there); O rows are dm elements apart and
+// only dims below dm are written.
+template <typename T, int D, int DC>
 __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__ ws_o,
                                                        const float* __restrict__ ws_lse, T* __restrict__ o,
                                                        float* __restrict__ lse, int64_t n_rows, int n_splits, int dm)
 {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
-    constexpr int TPR = D / 8, G = 16;  // threads per row, chunks per group
+    constexpr int TPR = DC / 8, G = 16;  // threads per row, chunks per group
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t row = t / TPR;
     const int c0 = (int)(t % TPR) * 8;
@@ -334,14 +335,14 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
 // PADDED: the head dim dm (a multiple of 8 below D) is run with D; K/V
 // lanes of the missing dims copy nothing and their LDS chunks stay zero, Q
 // loads zeros there, and only dm dims of O are written.
-template <typename T, int D, bool CAUSAL, int WAVES, int QB, bool SPLIT, bool MASKS, bool PADDED>
+template <typename T, int D, bool CAUSAL, int WAVES, int QB, bool SPLIT, bool MASKS, bool PADDED, int DC = D>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
                           amdgpu_waves_per_eu(2 / QB, 2 / QB)))
 void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                    T* __restrict__ o, float* __restrict__ lse, int Nq, int Nk, int n_qt, float c_log2,
                    int n_splits, float* __restrict__ ws_o, float* __restrict__ ws_lse, MaskArgs mask, int dm)
 {
-    typedef Cfg<D, WAVES, QB> C;
+    typedef Cfg<D, WAVES, QB, DC> C;
     typedef typename Mma<T>::vec8 vec8;
     // kStaged: the epilogue goes through LDS (store_outputs_staged); padded head
     // dims below 64 measured 1% slower with it and keep the direct stores.
@@ -377,19 +378,22 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     const T* kh = k + kv_off;
     const T* vh = v + kv_off;
     // The exp2 work of tile j is interleaved with the score MFMAs of tile j+1
-    // (scores_with_exp). The 4-wave d=128 shape keeps them apart in its split,
-    // masked and padded variants, which run out of registers fused.
-    constexpr bool kFuseExp = QB == 1 && fuses_exp(D, WAVES, SPLIT, MASKS, PADDED);
+    // (scores_with_exp). The 4-wave shape computing 128 dims keeps them apart
+    // in its split, masked and padded variants, which run out of registers
+    // fused.
+    constexpr bool kFuseExp = QB == 1 && fuses_exp(DC, WAVES, SPLIT, MASKS, PADDED);
     // d=64 without masks splits the exp work of a tile in two halves by its
     // 32-key blocks: the second block's goes between the next tile's score
     // MFMAs as above, the first block's between the MFMAs of the previous
     // tile's P.V, so both MFMA blocks carry vector work. The lazy-max test
     // still sees the whole tile before any of its P enters P.V. Measured +3%
     // at B4 H16 N4096 d=64 non-causal, causal unchanged; at d=128 the same
-    // split ran 5% slower in every instruction order tried. (With masks a
-    // wave can start at a tile whose scores it never computed, which this
-    // order would leave unmasked.)
-    constexpr bool kSplitExp = kFuseExp && !MASKS && D == 64;
+    // split ran 5% slower in every instruction order tried. Computing 96
+    // dims, the direct non-causal kernels take it too (+1-1.7% at d = 80 and
+    // 96; the causal and split ones spill with it). (With masks a wave can
+    // start at a tile whose scores it never computed, which this order would
+    // leave unmasked.)
+    constexpr bool kSplitExp = kFuseExp && !MASKS && (D == 64 || (DC == 96 && !CAUSAL && !SPLIT));
     // While a wave runs a mixed score/exp block it gets issue priority over the
     // other wave of its SIMD, whose next instructions are then mostly P.V
     // MFMAs: the matrix core keeps taking the mixed block's MFMAs as they come
@@ -397,12 +401,13 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     // the 8-wave shapes, +3% for 4-wave d=128 and +1.5% for 4-wave d=64 with
     // the split above; 4-wave d=64 without the split ran 1-2% slower with it.
     constexpr bool kPrioMixed = WAVES == 8 || D == 128 || kSplitExp;
-    // Row sums of a tile: d=64 adds one partial sum per 32-key block, in
-    // element order, and then the blocks (the split above produces them
-    // apart); d=128 adds all 64 scores in element order. Every path of a
-    // kernel (fused or not, first tile, rescaled tile) uses the same order, so
-    // the masked and unmasked kernels of one head dim agree bit for bit.
-    constexpr bool kBS = D == 64;
+    // Row sums of a tile: d=64 and the kernels computing 96 dims add one
+    // partial sum per 32-key block, in element order, and then the blocks (the
+    // split above produces them apart); d=128 adds all 64 scores in element
+    // order. Every path of a kernel (fused or not, first tile, rescaled tile)
+    // uses the same order, so the masked and unmasked kernels of one head dim
+    // agree bit for bit.
+    constexpr bool kBS = D == 64 || DC == 96;
 
     int qrow[QB];
     vec8 qf[QB][C::DS];
@@ -572,7 +577,7 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
                     if constexpr (kPrioMixed) __builtin_amdgcn_s_setprio(1);
                     scores_with_exp<T, D, C::KB, C::DS, C::KT, 16, 32, kBS>(sn, kbuf(j + 1), qf, l32, hh, sc,
                                                                             m_run[0], c_log2, pc, rs);
-                    order_scores_block<D, WAVES, QB>();
+                    order_scores_block<D, WAVES, QB, DC>();
                     pin_regs(pc[0][2]);
                     pin_regs(pc[0][3]);
                     pin_reg(rs[0]);
@@ -586,13 +591,13 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
                     if (M || j + 1 >= u_hi) apply_mask(sn[0], j + 1, 0);
                     pv_with_exp<T, D, C::DB, C::KT, C::KB, 0, 16>(pc, vbuf(j), oacc, lane, hh, sn, m_run[0], c_log2,
                                                                   pn, rn);
-                    order_pv_block<D, WAVES, QB>();
+                    order_pv_block<D, WAVES, QB, DC>();
                     pin_regs(pn[0][0]);
                     pin_regs(pn[0][1]);
                     pin_reg(rn);
                 } else {
                     pv_tile<T, D, QB, C::DB, C::KT>(pc, vbuf(j), oacc, lane, hh);
-                    order_pv_block<D, WAVES, QB>();
+                    order_pv_block<D, WAVES, QB, DC>();
                 }
             }
         } else if constexpr (kFuseExp) {
@@ -604,26 +609,26 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
                     if constexpr (kPrioMixed) __builtin_amdgcn_s_setprio(1);
                     scores_with_exp<T, D, C::KB, C::DS, C::KT, 0, C::KB * 16, kBS>(sn, kbuf(j + 1), qf, l32, hh,
                                                                                    sc, m_run[0], c_log2, p, rs);
-                    order_scores_block<D, WAVES, QB>();
+                    order_scores_block<D, WAVES, QB, DC>();
                     if constexpr (kPrioMixed) __builtin_amdgcn_s_setprio(0);
                 } else {
                     exp_tile<T, QB, C::KB, C::KT, kBS>(sc, m_run, c_log2, p, rs);
                 }
                 softmax_finish<T, QB, C::KB, C::DB, C::KT, kBS>(sc, oacc, m_run, l_run, c_log2, p, rs);
                 pv_tile<T, D, QB, C::DB, C::KT>(p, vbuf(j), oacc, lane, hh);
-                order_pv_block<D, WAVES, QB>();
+                order_pv_block<D, WAVES, QB, DC>();
             }
         } else {
             if (!G || wave_sees(j + 1)) {
                 scores<T, D, QB, C::KB, C::DS>(sn, kbuf(j + 1), qf, l32, hh);
-                order_scores_block<D, WAVES, QB>();
+                order_scores_block<D, WAVES, QB, DC>();
             }
             if (!G || wave_sees(j)) {
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
                     if (M) apply_mask(sc[qb], j, qb);
                 softmax_pv<T, D, QB, C::KB, C::DB, C::KT, kBS>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
-                order_pv_block<D, WAVES, QB>();
+                order_pv_block<D, WAVES, QB, DC>();
             }
         }
         stage_barrier();
@@ -644,14 +649,14 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
                 rs[0] = rc + exp_range<T, C::KB, C::KT, 16, 32>(sc[0], m_run[0], c_log2, pc[0]);
                 softmax_finish<T, QB, C::KB, C::DB, C::KT, kBS>(sc, oacc, m_run, l_run, c_log2, pc, rs);
                 pv_tile<T, D, QB, C::DB, C::KT>(pc, vbuf(j), oacc, lane, hh);
-                order_pv_block<D, WAVES, QB>();
+                order_pv_block<D, WAVES, QB, DC>();
             }
         } else if (!G || wave_sees(j)) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
                 if (M) apply_mask(sc[qb], j, qb);
             softmax_pv<T, D, QB, C::KB, C::DB, C::KT, kBS>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
-            order_pv_block<D, WAVES, QB>();
+            order_pv_block<D, WAVES, QB, DC>();
         }
     };
     auto shift_scores = [&]() {
@@ -715,7 +720,7 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     }
 }
 
-template <typename T, int D, bool CAUSAL, int WAVES, int QB, bool MASKS, bool PADDED>
+template <typename T, int D, bool CAUSAL, int WAVES, int QB, bool MASKS, bool PADDED, int DC>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                       int Nq, int Nk, float scale, const MaskArgs& mask, int dm, hipStream_t stream)
 {
@@ -723,7 +728,7 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o, floa
     const int n_qt = (Nq + C::BM - 1) / C::BM;
     const float c_log2 = scale * 1.4426950408889634f;
     dim3 grid((unsigned)((int64_t)n_qt * BH)), block(C::THREADS);
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, WAVES, QB, false, MASKS, PADDED>), grid, block, 0, stream,
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, WAVES, QB, false, MASKS, PADDED, DC>), grid, block, 0, stream,
                        (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, Nq, Nk, n_qt, c_log2, 1,
                        (float*)nullptr, (float*)nullptr, mask, dm);
     return hipGetLastError();
@@ -732,7 +737,7 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o, floa
 // Split launch (4-wave, 128-row workgroups) followed by the merge; the
 // workspace holds n_splits * B*H*Nq partial rows of D floats and then as many
 // logsumexps.
-template <typename T, int D, bool CAUSAL, bool MASKS, bool PADDED>
+template <typename T, int D, bool CAUSAL, bool MASKS, bool PADDED, int DC>
 hipError_t launch_split(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                         int Nq, int Nk, float scale, int n_splits, float* ws, const MaskArgs& mask,
                         int dm, hipStream_t stream)
@@ -744,19 +749,19 @@ hipError_t launch_split(const void* q, const void* k, const void* v, void* o, fl
     float* ws_o = ws;
     float* ws_lse = ws + (int64_t)n_splits * n_rows * D;
     dim3 grid((unsigned)((int64_t)n_qt * BH * n_splits)), block(C::THREADS);
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, 4, 1, true, MASKS, PADDED>), grid, block, 0, stream,
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, 4, 1, true, MASKS, PADDED, DC>), grid, block, 0, stream,
                        (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, Nq, Nk, n_qt, c_log2, n_splits,
                        ws_o, ws_lse, mask, dm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t threads = n_rows * (D / 8);
+    const int64_t threads = n_rows * (DC / 8);
     dim3 mgrid((unsigned)((threads + 255) / 256)), mblock(256);
-    hipLaunchKernelGGL((fa_merge_kernel<T, D>), mgrid, mblock, 0, stream, (const float*)ws_o,
+    hipLaunchKernelGGL((fa_merge_kernel<T, D, DC>), mgrid, mblock, 0, stream, (const float*)ws_o,
                        (const float*)ws_lse, (T*)o, lse, n_rows, n_splits, PADDED ? dm : D);
     return hipGetLastError();
 }
 
-template <typename T, int D, bool CAUSAL, bool MASKS, bool PADDED>
+template <typename T, int D, bool CAUSAL, bool MASKS, bool PADDED, int DC>
 hipError_t launch_shape(const Shape& sh, const void* q, const void* k, const void* v, void* o,
                         float* lse, int BH, int Nq, int Nk, float scale, const MaskArgs& mask, int dm,
                         hipStream_t stream)
@@ -765,10 +770,10 @@ hipError_t launch_shape(const Shape& sh, const void* q, const void* k, const voi
     // d=128: that kernel has no registers left for the per-row key ranges
     if constexpr (!CAUSAL && !(MASKS && D == 128)) {
         if (sh.waves == 8)
-            return launch_one<T, D, CAUSAL, 8, 1, MASKS, PADDED>(q, k, v, o, lse, BH, Nq, Nk, scale, mask, dm,
+            return launch_one<T, D, CAUSAL, 8, 1, MASKS, PADDED, DC>(q, k, v, o, lse, BH, Nq, Nk, scale, mask, dm,
                                                                  stream);
     }
-    return launch_one<T, D, CAUSAL, 4, 1, MASKS, PADDED>(q, k, v, o, lse, BH, Nq, Nk, scale, mask, dm, stream);
+    return launch_one<T, D, CAUSAL, 4, 1, MASKS, PADDED, DC>(q, k, v, o, lse, BH, Nq, Nk, scale, mask, dm, stream);
 }
 
 template <typename T>
@@ -777,25 +782,36 @@ struct TypeTag {
 };
 
 // One forward launch of the MASKS / PADDED variant: dispatch on dtype, the
-// kernel head dim and causality, then the direct or the split launch.
+// kernel head dim, the computed dims and causality, then the direct or the
+// split launch. A PADDED launch computes compute_dim(d) dims (d rounded up to
+// 32): at d = 96 three quarters of the d = 128 kernel's MFMAs, at d <= 32
+// half of the d = 64 kernel's.
 template <bool MASKS, bool PADDED>
 hipError_t launch_variant(const FwdArgs& a)
 {
     const int BH = a.B * a.H;
-    auto go = [&](auto t, auto dd, auto cc) -> hipError_t {
+    auto go = [&](auto t, auto dd, auto dc, auto cc) -> hipError_t {
         typedef typename decltype(t)::type T;
-        constexpr int D = decltype(dd)::value;
+        constexpr int D = decltype(dd)::value, DC = decltype(dc)::value;
         constexpr bool CAUSAL = decltype(cc)::value;
         if (a.split)
-            return launch_split<T, D, CAUSAL, MASKS, PADDED>(a.q, a.k, a.v, a.o, a.lse, BH, a.Nq, a.Nk, a.scale,
-                                                             a.n_splits, a.workspace, a.mask, a.d, a.stream);
+            return launch_split<T, D, CAUSAL, MASKS, PADDED, DC>(a.q, a.k, a.v, a.o, a.lse, BH, a.Nq, a.Nk,
+                                                                 a.scale, a.n_splits, a.workspace, a.mask, a.d,
+                                                                 a.stream);
         const Shape sh = MASKS ? pick_shape_masked(a.B, a.H, a.Nq, a.d, a.causal)
                                : pick_shape(a.B, a.H, a.Nq, a.d, a.causal);
-        return launch_shape<T, D, CAUSAL, MASKS, PADDED>(sh, a.q, a.k, a.v, a.o, a.lse, BH, a.Nq, a.Nk, a.scale,
-                                                         a.mask, a.d, a.stream);
+        return launch_shape<T, D, CAUSAL, MASKS, PADDED, DC>(sh, a.q, a.k, a.v, a.o, a.lse, BH, a.Nq, a.Nk,
+                                                             a.scale, a.mask, a.d, a.stream);
+    };
+    auto by_compute = [&](auto t, auto dd, auto cc) -> hipError_t {
+        constexpr int D = decltype(dd)::value;
+        if constexpr (PADDED) {
+            if (compute_dim(a.d) < D) return go(t, dd, std::integral_constant<int, D - 32>(), cc);
+        }
+        return go(t, dd, dd, cc);
     };
     auto by_causal = [&](auto t, auto dd) -> hipError_t {
-        return a.causal ? go(t, dd, std::true_type()) : go(t, dd, std::false_type());
+        return a.causal ? by_compute(t, dd, std::true_type()) : by_compute(t, dd, std::false_type());
     };
     auto by_dim = [&](auto t) -> hipError_t {
         return kernel_dim(a.d) == 64 ? by_causal(t, std::integral_constant<int, 64>())

@@ -48,6 +48,9 @@ struct FwdArgs {
 
 // The head dim the kernel runs with: 64 or 128.
 inline int kernel_dim(int d) { return d <= 64 ? 64 : 128; }
+// The dims the forward kernel's MFMAs cover: d rounded up to a multiple of 32
+// (32, 64, 96 or 128), at most kernel_dim(d).
+inline int compute_dim(int d) { return (d + 31) / 32 * 32; }
 
 Shape pick_shape(int B, int H, int n_queries, int d, bool causal);
 // The shape of a masked launch: pick_shape's, except that a kernel head dim

@@ -22,13 +22,14 @@
 namespace fa {
 
 // Whether a forward kernel variant interleaves the exp2 work of tile j with
-// the score MFMAs of tile j+1. Every 32-row variant does, except the 4-wave
-// head-dim-128 kernels with a split, masks or padding, which run out of
+// the score MFMAs of tile j+1. DC: the head dims the kernel computes (the
+// head dim rounded up to 32). Every 32-row variant does, except the 4-wave
+// kernels computing 128 dims with a split, masks or padding, which run out of
 // registers fused. The kernel and the host's count of executed MFMA work
 // (fa_plan) both take it from here.
-FA_HD constexpr bool fuses_exp(int D, int waves, bool split, bool masks, bool padded)
+FA_HD constexpr bool fuses_exp(int DC, int waves, bool split, bool masks, bool padded)
 {
-    return !(D == 128 && waves == 4 && (split || masks || padded));
+    return !(DC == 128 && waves == 4 && (split || masks || padded));
 }
 
 struct KeyRange {
