@@ -113,9 +113,13 @@ int fa_fwd_qk(const void *q, const void *k, const void *v, void *o, float *lse, 
  * The profiler page names KV-cache decode as the next step ("Getting the
  * kernel correct, then benchmarking it honestly", closing paragraph).
  *
- * fa_split_count -- a suggested n_splits (>= 1): about 256 to 1024
- *   workgroups in all and at least 16 key tiles of 64 per chunk (1, the
- *   direct path, for short key sequences). Returns 0 on invalid arguments.
+ * fa_split_count -- a suggested n_splits (>= 1), from timings on MI355X:
+ *   for up to 32 query rows about 512 workgroups in all and chunks of at
+ *   least two key tiles of 64; with more query rows at most 256 workgroups
+ *   and chunks of at least 16 key tiles (8 for grids of at most 16
+ *   workgroups); 1, the direct path, under 16 key tiles. A causal problem
+ *   counts the min(Nq, Nk) keys its longest query tile sees. Returns 0 on
+ *   invalid arguments.
  * fa_split_workspace_bytes -- bytes of workspace fa_fwd_split_qk needs:
  *   n_splits * B*H*Nq * (D + 1) * 4, with D = 64 for d <= 64 and 128
  *   otherwise (the kernel's head dim). Returns 0 on invalid arguments.

@@ -448,8 +448,14 @@ def test_split_count_suggestion(lib):
     assert fa.fa_split_count(4, 32, 1, 16384, 128, 0) == 8    # long caches: 8 chunks
     assert fa.fa_split_count(16, 32, 1, 2048, 128, 0) == 1    # a large grid of short caches
     assert fa.fa_split_count(16, 32, 1, 8192, 128, 0) == 2
-    assert fa.fa_split_count(2, 32, 128, 8192, 128, 0) == 4   # full query tiles: about 256 workgroups
-    assert fa.fa_split_count(2, 32, 128, 1024, 128, 0) == 2   # ... with chunks of 8 key tiles
+    assert fa.fa_split_count(2, 32, 128, 8192, 128, 0) == 4   # full query tiles: at most 256 workgroups
+    assert fa.fa_split_count(2, 32, 128, 2048, 128, 0) == 2   # ... with chunks of 16 key tiles
+    assert fa.fa_split_count(2, 32, 128, 1024, 128, 0) == 1
+    assert fa.fa_split_count(1, 16, 128, 1536, 128, 0) == 3   # 16 workgroups: chunks of 8 key tiles
+    assert fa.fa_split_count(2, 4, 1000, 1000, 64, 0) == 1    # 64 workgroups, 16 key tiles
+    assert fa.fa_split_count(2, 4, 3000, 3000, 64, 0) == 1    # 192 workgroups
+    assert fa.fa_split_count(1, 1, 8192, 8192, 64, 1) == 4
+    assert fa.fa_split_count(2, 32, 128, 8192, 128, 1) == 1   # causal: the queries see 128 keys
     assert fa.fa_split_count(8, 32, 128, 8192, 128, 0) == 1
     assert fa.fa_split_count(4, 16, 4096, 4096, 128, 0) == 1
     assert fa.fa_split_count(1, 1, 1, 512, 64, 0) == 1

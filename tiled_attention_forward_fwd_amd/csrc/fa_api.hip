@@ -498,21 +498,32 @@ int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* l
 int fa_split_count(int B, int H, int Nq, int Nk, int d, int causal)
 {
     if (check_problem(B, H, Nq, Nk, d, causal, FA_DTYPE_BF16) != FA_OK) return 0;
-    // Measured on MI355X (bf16, d = 64 and 128, B*H from 32 to 2048, 1 to
-    // 128 query rows, 512 to 16384 keys; every split count timed).
+    // Measured on MI355X (bf16, d = 64 and 128, B*H from 8 to 2048, 1 to
+    // 4000 query rows, 512 to 16384 keys; every split count timed).
     //  * Under 16 key tiles the merge costs more than the split gains.
+    //  * Causal: query row i sees keys [0, i], so the longest query tile sees
+    //    min(Nq, Nk) keys; that is what a split could shorten.
     //  * Up to 32 query rows a workgroup has one computing wave and streams
     //    K/V: about 512 workgroups keep HBM busy, and chunks as short as two
     //    key tiles still pay. Small grids with long caches take 8 chunks,
     //    which also balances caches of different lengths (padding); grids
     //    past 128 tiles take 2 chunks from 64 key tiles on.
-    //  * With more query rows every chunk writes a partial of that many rows
-    //    and the workgroups compute more: about 256 workgroups, chunks of at
-    //    least 8 key tiles.
+    //  * With more query rows every chunk writes fp32 partials of all its rows
+    //    and the merge reads them back: the split and merge cost 5-12 us more
+    //    than the direct launch, against 0.6 (d = 64) to 0.85 us (d = 128) per
+    //    key tile taken off the longest workgroup. So at most 256 workgroups
+    //    (one per CU; a second one on a CU shares its SIMDs and shortens
+    //    nothing) and chunks of at least 16 key tiles, or 8 when the grid
+    //    has at most 16 workgroups. At B2 H4 (8 heads, 8 to 63 query tiles
+    //    each), N = 1000 to 4000, the direct launch is as fast or faster at
+    //    every N; at B1 H2 N4096 d128 and B1 H1 N8192 d64 (64 workgroups) 4
+    //    chunks take 0.5-0.6x its time, at B1 H16 Nq128 Nk1536 d128 (16
+    //    workgroups) 8 chunks take 0.7x.
     const int64_t rows = fa::split_rows_per_tile();
     const int64_t rq = Nq < rows ? Nq : rows;
     const int64_t wgs = (int64_t)B * H * (((int64_t)Nq + rows - 1) / rows);
-    const int64_t n_kt = ((int64_t)Nk + 63) / 64;
+    const int64_t keys = causal && Nq < Nk ? Nq : Nk;
+    const int64_t n_kt = (keys + 63) / 64;
     if (n_kt < 16) return 1;
     int64_t s;
     if (rq <= 32) {
@@ -525,8 +536,9 @@ int fa_split_count(int B, int H, int Nq, int Nk, int d, int causal)
         }
         if (s > n_kt / 2) s = n_kt / 2;
     } else {
-        s = (256 + wgs - 1) / wgs;
-        if (s > n_kt / 8) s = n_kt / 8;
+        s = 256 / wgs;
+        const int64_t min_chunk = wgs <= 16 ? 8 : 16;
+        if (s > n_kt / min_chunk) s = n_kt / min_chunk;
     }
     return (int)(s < 1 ? 1 : s);
 }
