@@ -66,9 +66,10 @@ typedef enum {
  *   B, H, N : >= 1, with N*d*2 < 2^32 (one head below 4 GiB).
  *   d       : a multiple of 8 from 8 to 128 (other values: FA_ERR_UNSUPPORTED).
  *             64 and 128 have kernels of their own; any other d runs with
- *             the d = 64 kernel (d < 64) or the d = 128 kernel, the missing
- *             dims held at zero on chip, so the result is that of head dim d
- *             at the MFMA cost of the larger one. ("How to optimise a Triton
+ *             the tiles of the d = 64 kernel (d < 64) or the d = 128 kernel,
+ *             the missing dims held at zero on chip, so the result is that of
+ *             head dim d; the matrix cores compute d rounded up to 32 dims
+ *             (32, 64, 96 or 128). ("How to optimise a Triton
  *             FlashAttention-2 kernel step by step with a profiler" runs its
  *             tests over several shapes, input types and head dims, Round 3.)
  *   causal  : 0 or 1.
@@ -246,7 +247,8 @@ int fa_fwd_f32(const float *q, const float *k, const float *v, float *o, float *
  *                      nothing).
  * Other arguments as fa_fwd, d included (a multiple of 8 from 8 to 128;
  * below 128 other than 64 the d = 64 or 128 kernels run with the missing
- * dims held at zero). Three kernels are enqueued on `stream`; nothing uses
+ * dims held at zero, computing d rounded up to 32 dims). Three kernels are
+ * enqueued on `stream`; nothing uses
  * atomics, so results are deterministic.
  */
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,

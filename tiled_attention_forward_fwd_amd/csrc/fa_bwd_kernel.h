@@ -150,7 +150,7 @@ __device__ __forceinline__ KeyRows key_rows(int64_t j, bool causal, const MaskAr
     return r;
 }
 
-template <typename T, int D, bool CAUSAL, bool MASKS, bool PADDED>
+template <typename T, int D, bool CAUSAL, bool MASKS, bool PADDED, int DC = D>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kBwdWaves, 64 * kBwdWaves),
                           amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -158,7 +158,7 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
                         const float* __restrict__ delta, T* __restrict__ dk, T* __restrict__ dv, int Nq,
                         int Nk, int n_kt, float scale, float c_log2, MaskArgs mask, int dm)
 {
-    typedef Cfg<D, kBwdWaves, 1> C;  // 64-row copies by the whole workgroup, as the forward's tiles
+    typedef Cfg<D, kBwdWaves, 1, DC> C;  // 64-row copies by the whole workgroup, as the forward's tiles
     typedef typename Mma<T>::vec8 vec8;
     static_assert(C::BN == kBwdRows, "tile rows");
     constexpr int TILE = C::TILE;
@@ -322,14 +322,14 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
 }
 
 // ---------------------------------------------------------------- dQ
-template <typename T, int D, bool CAUSAL, bool MASKS, bool PADDED>
+template <typename T, int D, bool CAUSAL, bool MASKS, bool PADDED, int DC = D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                       const T* __restrict__ dout, const float* __restrict__ lse,
                       const float* __restrict__ delta, T* __restrict__ dq, int Nq, int Nk, int n_qt,
                       float scale, float c_log2, MaskArgs mask, int dm)
 {
-    typedef Cfg<D, 4, 1> C;  // 128 query rows, 64-key tiles
+    typedef Cfg<D, 4, 1, DC> C;  // 128 query rows, 64-key tiles
     typedef typename Mma<T>::vec8 vec8;
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * C::TILE];
 
@@ -443,8 +443,8 @@ void fa_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
 }
 
 // The three kernels for head dim dm (dm == D, or a multiple of 8 below D when
-// PADDED).
-template <typename T, int D, bool CAUSAL, bool MASKS, bool PADDED>
+// PADDED), computing DC dims.
+template <typename T, int D, bool CAUSAL, bool MASKS, bool PADDED, int DC>
 hipError_t launch_bwd_typed(const void* q, const void* k, const void* v, const void* o, const void* dout,
                             const float* lse, void* dq, void* dk, void* dv, float* delta, int BH, int Nq,
                             int Nk, int dm, float scale, const MaskArgs& mask, hipStream_t stream)
@@ -458,21 +458,27 @@ hipError_t launch_bwd_typed(const void* q, const void* k, const void* v, const v
     if (e != hipSuccess) return e;
     const int n_kt = (Nk + kBwdKeys - 1) / kBwdKeys;
     dim3 g1((unsigned)((int64_t)n_kt * BH)), b1(64 * kBwdWaves);
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, CAUSAL, MASKS, PADDED>), g1, b1, 0, stream, (const T*)q,
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, CAUSAL, MASKS, PADDED, DC>), g1, b1, 0, stream, (const T*)q,
                        (const T*)k, (const T*)v, (const T*)dout, lse, (const float*)delta, (T*)dk, (T*)dv, Nq,
                        Nk, n_kt, scale, c_log2, mask, dm);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_qt = (Nq + 127) / 128;
     dim3 g2((unsigned)((int64_t)n_qt * BH)), b2(256);
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, CAUSAL, MASKS, PADDED>), g2, b2, 0, stream, (const T*)q,
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, CAUSAL, MASKS, PADDED, DC>), g2, b2, 0, stream, (const T*)q,
                        (const T*)k, (const T*)v, (const T*)dout, lse, (const float*)delta, (T*)dq, Nq, Nk, n_qt,
                        scale, c_log2, mask, dm);
     return hipGetLastError();
 }
 
-// Every (element type, kernel head dim, causal, masks) instance for one
-// PADDED value; d picks the kernel head dim (kernel_dim).
+template <typename T>
+struct BwdType {
+    typedef T type;
+};
+
+// Every (element type, kernel head dim, computed dims, causal, masks) instance
+// for one PADDED value; d picks the kernel head dim (kernel_dim) and, PADDED,
+// the computed dims (compute_dim: d rounded up to 32).
 template <bool PADDED>
 hipError_t launch_bwd_variant(const void* q, const void* k, const void* v, const void* o, const void* dout,
                               const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H,
@@ -481,24 +487,31 @@ hipError_t launch_bwd_variant(const void* q, const void* k, const void* v, const
 {
     const int BH = B * H;
     const MaskArgs none{-1, -1, nullptr, H};
-#define FA_BWD_M(T, D, C)                                                                                  \
-    return mask ? launch_bwd_typed<T, D, C, true, PADDED>(q, k, v, o, dout, lse, dq, dk, dv, delta, BH, Nq, \
-                                                          Nk, d, scale, *mask, stream)                     \
-                : launch_bwd_typed<T, D, C, false, PADDED>(q, k, v, o, dout, lse, dq, dk, dv, delta, BH, Nq,\
-                                                           Nk, d, scale, none, stream)
-#define FA_BWD(T, D)                      \
-    do {                                  \
-        if (causal) FA_BWD_M(T, D, true); \
-        FA_BWD_M(T, D, false);            \
-    } while (0)
-    if (bf16) {
-        if (kernel_dim(d) == 64) FA_BWD(__bf16, 64);
-        FA_BWD(__bf16, 128);
-    }
-    if (kernel_dim(d) == 64) FA_BWD(_Float16, 64);
-    FA_BWD(_Float16, 128);
-#undef FA_BWD
-#undef FA_BWD_M
+    auto go = [&](auto t, auto dd, auto dc, auto cc, auto mm) -> hipError_t {
+        typedef typename decltype(t)::type T;
+        constexpr int D = decltype(dd)::value, DC = decltype(dc)::value;
+        constexpr bool CAUSAL = decltype(cc)::value, MASKS = decltype(mm)::value;
+        return launch_bwd_typed<T, D, CAUSAL, MASKS, PADDED, DC>(q, k, v, o, dout, lse, dq, dk, dv, delta, BH,
+                                                                 Nq, Nk, d, scale, MASKS ? *mask : none, stream);
+    };
+    auto by_masks = [&](auto t, auto dd, auto dc, auto cc) -> hipError_t {
+        return mask ? go(t, dd, dc, cc, std::true_type()) : go(t, dd, dc, cc, std::false_type());
+    };
+    auto by_causal = [&](auto t, auto dd, auto dc) -> hipError_t {
+        return causal ? by_masks(t, dd, dc, std::true_type()) : by_masks(t, dd, dc, std::false_type());
+    };
+    auto by_compute = [&](auto t, auto dd) -> hipError_t {
+        constexpr int D = decltype(dd)::value;
+        if constexpr (PADDED) {
+            if (compute_dim(d) < D) return by_causal(t, dd, std::integral_constant<int, D - 32>());
+        }
+        return by_causal(t, dd, dd);
+    };
+    auto by_dim = [&](auto t) -> hipError_t {
+        return kernel_dim(d) == 64 ? by_compute(t, std::integral_constant<int, 64>())
+                                   : by_compute(t, std::integral_constant<int, 128>());
+    };
+    return bf16 ? by_dim(BwdType<__bf16>()) : by_dim(BwdType<_Float16>());
 }
 
 }  // namespace
