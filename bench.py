@@ -27,6 +27,7 @@ Other modes (used to collect counters; each runs a few launches only):
     --profile-decode    the split-key decode path (one query x 16384 keys, B=1 H=32)
     --profile-masked    the padding and sliding-window workloads of the sweep
     --profile-variants  head dims 96 and 32 and fp32 inputs at the headline shape
+    --profile-bwd       backward calls at the headline shape (both causal flags)
     --sweep             medians of 50 for every configuration of the workload
                         list, with each configuration's own peak memory and
                         the fp64 oracle's rate on a row sample of it (one
@@ -178,7 +179,7 @@ def time_backward(cfg, reps=10):
 
 def backward_leg(reps=10):
     """The backward pass after the timed region: the headline shape, and the same shape at head
-    dim 96 (the d = 128 kernels run padded; FLOPs counted at d = 96)."""
+    dim 96 (the d = 128 tiles computing 96 dims; FLOPs counted at d = 96)."""
     res = time_backward(HEADLINE, reps)
     res["what"] = ("fa.bwd (delta, dK/dV, dQ kernels) at B=4 H=16 N=4096 d=128 bf16, FLOPs = 2.5x "
                    "the forward's; the kernels execute 1.4x that (S and dP are recomputed for dQ)")
@@ -544,6 +545,24 @@ def profile_kernels(args):
                       "launches_each": args.steps}))
 
 
+def profile_bwd(args):
+    """The backward pass at the headline shape, for rocprofv3: per causal flag one forward for O
+    and lse, then `steps` fa.bwd calls (delta, dK/dV and dQ kernels each)."""
+    import torch
+    import tiled_attention_forward_fwd_amd as fa
+    from fa_inputs import make_qkv
+    dev = torch.device("cuda:0")
+    cfg = HEADLINE
+    _, _, _, qd, kd, vd = make_inputs(cfg, dev)
+    dout = make_qkv(cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["dtype"], cfg["seed"] + 100)[0].to(dev)
+    for causal in (False, True):
+        o, lse = fa.fwd(qd, kd, vd, causal=causal)
+        for _ in range(args.steps):
+            fa.bwd(qd, kd, vd, o, lse, dout, causal=causal)
+        torch.cuda.synchronize()
+    print(json.dumps({"profiled": "backward", "workload": cfg, "calls_each": args.steps}))
+
+
 DECODE = dict(B=1, H=32, Nq=1, N=16384, d=128, dtype="bf16", seed=10)
 
 
@@ -627,6 +646,8 @@ def main():
                     help="padding and sliding-window workloads only, for rocprofv3")
     ap.add_argument("--profile-variants", action="store_true",
                     help="head dims 96 / 32 and fp32 inputs at B4 H16 N4096, for rocprofv3")
+    ap.add_argument("--profile-bwd", action="store_true",
+                    help="`steps` backward calls at the headline shape per causal flag, for rocprofv3")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -652,6 +673,8 @@ def main():
         return profile_workloads(args, MASKED_WORKLOADS, "masked workloads")
     if args.profile_variants:
         return profile_workloads(args, VARIANT_WORKLOADS, "head-dim and fp32 workloads")
+    if args.profile_bwd:
+        return profile_bwd(args)
     if args.profile_timed:
         return profile_workloads(args, [dict(w, flags=w.get("flags", (0, 1))) for w in PROFILE_SETS[args.profile_set]],
                                  f"profile set {args.profile_set}")
