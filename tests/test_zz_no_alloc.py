@@ -32,16 +32,19 @@ def test_noalloc_split_matches_the_workspace_launch():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     fa.load_library()
     stream = torch.cuda.current_stream().cuda_stream
-    # (B, H, Nq, Nk, d, dtype, causal): a decode batch, then a smaller problem
-    # of another head dim whose scratch use is a prefix of the first one's
-    cases = [(4, 16, 3, 8192, 128, "bf16", 0), (1, 4, 100, 2500, 64, "fp16", 1)]
-    for B, H, Nq, Nk, d, dtype, causal in cases:
+    # (B, H, Nq, Nk, d, dtype, causal, splits): a decode batch at the suggested
+    # split count, then a smaller causal problem of another head dim whose
+    # scratch use is a prefix of the first one's, at 4 chunks (its 100 queries
+    # see 100 keys, so the suggestion is the direct launch; the chunks past
+    # them are empty and get weight zero in the merge)
+    cases = [(4, 16, 3, 8192, 128, "bf16", 0, None), (1, 4, 100, 2500, 64, "fp16", 1, 4)]
+    for B, H, Nq, Nk, d, dtype, causal, n_splits in cases:
         print(f"[case] noalloc B={B} H={H} Nq={Nq} Nk={Nk} d={d} {dtype} causal={causal}", flush=True)
         q, k, v = _inputs(B, H, Nq, Nk, d, dtype, 95 + d)
         qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
         code = fa.dtype_code(q.dtype)
         scale = fa.default_scale(d)
-        splits = fa.fa_split_count(B, H, Nq, Nk, d, causal)
+        splits = n_splits or fa.fa_split_count(B, H, Nq, Nk, d, causal)
         assert splits > 1
         need = fa.fa_split_workspace_bytes(B, H, Nq, d, splits)
         assert need <= fa.NOALLOC_SCRATCH_BYTES
