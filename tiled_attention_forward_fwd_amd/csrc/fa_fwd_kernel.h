@@ -264,9 +264,10 @@ __device__ __forceinline__ void store_partials(const f32x16 (&oacc)[QB][DB], con
 // Merge of the key chunks of a split launch, per query row:
 // lse = ln sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s. Each thread
 // owns 8 consecutive dims of one row; rows are [B*H*Nq] in order. Chunks go
-// in groups of 16 whose loads are all issued before any is used, so a call
-// with up to 16 chunks makes two rounds of memory reads (the logsumexps, then
-// the partial outputs) instead of one per chunk.
+// in groups of 16 whose loads (logsumexps and partial outputs together) are
+// all issued before any is used, so a call with up to 16 chunks makes one
+// round of memory reads; later groups rescale the running sums to their
+// larger maximum (the online-softmax update, once per group).
 // The partial rows are D floats apart and hold the DC computed dims (a PADDED
 // launch's dims past dm are zero there); O rows are dm elements apart and
 // only dims below dm are written.
@@ -281,39 +282,39 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
     const int64_t row = t / TPR;
     const int c0 = (int)(t % TPR) * 8;
     if (row >= n_rows) return;
-    float mx = -INFINITY;
+    float mx = -INFINITY, wsum = 0.f;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < n_splits; s0 += G) {
         float l[G];
+        f32x4 a[G], b[G];
 #pragma unroll
-        for (int i = 0; i < G; ++i) l[i] = s0 + i < n_splits ? ws_lse[(int64_t)(s0 + i) * n_rows + row] : -INFINITY;
-#pragma unroll
-        for (int i = 0; i < G; ++i) mx = fmaxf(mx, l[i]);
-    }
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
-    if (mx > -INFINITY) {
-        for (int s0 = 0; s0 < n_splits; s0 += G) {
-            float l[G];
-            f32x4 a[G], b[G];
-#pragma unroll
-            for (int i = 0; i < G; ++i) {
-                if (s0 + i < n_splits) {
-                    const float* src = ws_o + ((int64_t)(s0 + i) * n_rows + row) * D + c0;
-                    l[i] = ws_lse[(int64_t)(s0 + i) * n_rows + row];
-                    a[i] = *(const f32x4*)src;
-                    b[i] = *(const f32x4*)(src + 4);
-                } else {
-                    l[i] = -INFINITY;
-                    a[i] = b[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-                }
+        for (int i = 0; i < G; ++i) {
+            if (s0 + i < n_splits) {
+                const float* src = ws_o + ((int64_t)(s0 + i) * n_rows + row) * D + c0;
+                l[i] = ws_lse[(int64_t)(s0 + i) * n_rows + row];
+                a[i] = *(const f32x4*)src;
+                b[i] = *(const f32x4*)(src + 4);
+            } else {
+                l[i] = -INFINITY;
+                a[i] = b[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
             }
+        }
+        float gm = mx;
 #pragma unroll
-            for (int i = 0; i < G; ++i) {
-                const float w = expf(l[i] - mx);  // exp(-inf) = 0 for absent or empty chunks
-                wsum += w;
-                acc0 += w * a[i];
-                acc1 += w * b[i];
-            }
+        for (int i = 0; i < G; ++i) gm = fmaxf(gm, l[i]);
+        if (gm == -INFINITY) continue;  // no chunk so far saw a key of this row
+        // rescale what the earlier groups added (weight 0 when there were none)
+        const float r = mx == -INFINITY ? 0.f : expf(mx - gm);
+        wsum *= r;
+        acc0 *= r;
+        acc1 *= r;
+        mx = gm;
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const float w = expf(l[i] - mx);  // exp(-inf) = 0 for absent or empty chunks
+            wsum += w;
+            acc0 += w * a[i];
+            acc1 += w * b[i];
         }
     }
     const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
