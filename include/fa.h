@@ -118,9 +118,12 @@ int fa_fwd_qk(const void *q, const void *k, const void *v, void *o, float *lse, 
  *   for up to 32 query rows about 512 workgroups in all and chunks of at
  *   least two key tiles of 64; with more query rows at most 256 workgroups
  *   and chunks of at least 16 key tiles (8 for grids of at most 16
- *   workgroups); 1, the direct path, under 16 key tiles. A causal problem
- *   counts the min(Nq, Nk) keys its longest query tile sees. Returns 0 on
- *   invalid arguments.
+ *   workgroups); 1, the direct path, under 16 key tiles and wherever the
+ *   direct entry points run their key-split kernel (more than 32 query rows,
+ *   at most 2048 keys, every 32-row workgroup resident: at most 512 of them
+ *   for d <= 64, 256 above; its four waves split each 32-row block's keys
+ *   and merge on chip). A causal problem counts the min(Nq, Nk) keys its
+ *   longest query tile sees. Returns 0 on invalid arguments.
  * fa_split_workspace_bytes -- bytes of workspace fa_fwd_split_qk needs:
  *   n_splits * B*H*Nq * (D + 1) * 4, with D = 64 for d <= 64 and 128
  *   otherwise (the kernel's head dim). Returns 0 on invalid arguments.

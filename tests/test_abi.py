@@ -140,11 +140,26 @@ def test_plan_flops_match_printed_counts(lib):
     assert c["mfma_flops"] == _walked_mfma_flops(4, 8, 4096, 4096, 64, 1, c["threads"] // 64)
 
 
+def _key_split_launch(B, H, Nq, Nk, D, causal):
+    """The rule that sends a direct launch to the key-split kernel, restated:
+    more than 32 query rows, at most 256 (D = 128) or 512 (D = 64) workgroups
+    of 32 rows, and at most 2048 keys seen by the longest query block."""
+    keys = min(Nq, Nk) if causal else Nk
+    return Nq > 32 and B * H * -(-Nq // 32) <= (512 if D <= 64 else 256) and keys <= 2048
+
+
 def _walked_mfma_flops(B, H, Nq, Nk, D, causal, waves):
     """The forward kernel's step loop walked one step at a time (no masks, no
     split): each wave counts the 32 x 64 blocks whose S = Q K^T and whose P V
     it computes. Restates the kernel's control flow, not the plan's interval
-    arithmetic."""
+    arithmetic. A key-split launch computes every 32-key tile of each 32-row
+    block once (one wave each), S and P V of 32 x 32."""
+    if _key_split_launch(B, H, Nq, Nk, D, causal):
+        tiles = 0
+        for q0 in range(0, Nq, 32):
+            last = min(q0 + 32, Nq, Nk) if causal else Nk  # keys the block's rows see
+            tiles += -(-last // 32)
+        return tiles * 2 * 2 * 32 * 32 * D * B * H
     BM, BN = 32 * waves, 64  # every unmasked, unpadded direct launch fuses the exp work
     blocks = 0
     for q0 in range(0, Nq, BM):
@@ -214,8 +229,23 @@ def test_plan_picks_workgroup_shape(lib):
     # causal problems and small grids keep 128-row, 4-wave workgroups
     causal = fa.fa_plan(4, 16, 4096, 128, 1, fa.FA_DTYPE_BF16)
     assert (causal["block_m"], causal["threads"], causal["workgroups"]) == (128, 256, 2048)
+    short = fa.fa_plan(4, 16, 512, 64, 0, fa.FA_DTYPE_F16)
+    assert (short["block_m"], short["threads"], short["workgroups"]) == (128, 256, 4 * 16 * 4)
+    # when every 32-row workgroup fits on the chip at once (512 at d <= 64, 256
+    # above) and the rows see at most 2048 keys, the key-split kernel runs:
+    # 32-row workgroups of 4 waves over 32-key tiles
     small = fa.fa_plan(2, 4, 1000, 64, 0, fa.FA_DTYPE_F16)
-    assert (small["block_m"], small["threads"], small["workgroups"]) == (128, 256, 64)
+    assert (small["block_m"], small["block_n"], small["threads"], small["workgroups"]) == (32, 32, 256, 2 * 4 * 32)
+    assert small["lds_bytes"] == 4 * 4 * 32 * 64 * 2
+    assert fa.fa_plan(1, 1, 128, 64, 1, fa.FA_DTYPE_F16)["block_m"] == 32
+    assert fa.fa_plan(2, 8, 1000, 64, 0, fa.FA_DTYPE_F16)["block_m"] == 32      # 512 workgroups
+    assert fa.fa_plan(4, 8, 1000, 64, 0, fa.FA_DTYPE_F16)["block_m"] == 128     # 1024
+    assert fa.fa_plan(1, 8, 1500, 128, 0, fa.FA_DTYPE_BF16)["block_m"] == 128   # 376 at d = 128
+    assert fa.fa_plan(1, 2, 2048, 96, 1, fa.FA_DTYPE_BF16)["lds_bytes"] == 4 * 4 * 32 * 128 * 2
+    assert fa.fa_plan(1, 2, 2048, 128, 1, fa.FA_DTYPE_BF16)["block_m"] == 32
+    assert fa.fa_plan(1, 2, 4096, 128, 0, fa.FA_DTYPE_BF16)["block_m"] == 128   # 4096 keys
+    assert fa.fa_plan_qk(1, 2, 32, 2048, 128, 0, fa.FA_DTYPE_BF16)["block_m"] == 128  # decode-like: split path
+    assert fa.fa_plan_qk(1, 2, 600, 4096, 128, 1, fa.FA_DTYPE_BF16)["block_m"] == 32  # sees 600 keys
     # at most 128 query rows: 128-row workgroups whatever the grid, so that
     # no workgroup holds a CU's waves for one block of rows
     for nq in (1, 16, 128):
@@ -449,11 +479,15 @@ def test_split_count_suggestion(lib):
     assert fa.fa_split_count(16, 32, 1, 2048, 128, 0) == 1    # a large grid of short caches
     assert fa.fa_split_count(16, 32, 1, 8192, 128, 0) == 2
     assert fa.fa_split_count(2, 32, 128, 8192, 128, 0) == 4   # full query tiles: at most 256 workgroups
-    assert fa.fa_split_count(2, 32, 128, 2048, 128, 0) == 2   # ... with chunks of 16 key tiles
-    assert fa.fa_split_count(2, 32, 128, 1024, 128, 0) == 1
-    assert fa.fa_split_count(1, 16, 128, 1536, 128, 0) == 3   # 16 workgroups: chunks of 8 key tiles
-    assert fa.fa_split_count(2, 4, 1000, 1000, 64, 0) == 1    # 64 workgroups, 16 key tiles
-    assert fa.fa_split_count(2, 4, 3000, 3000, 64, 0) == 1    # 192 workgroups
+    assert fa.fa_split_count(2, 32, 128, 4096, 128, 0) == 4   # ... with chunks of 16 key tiles
+    assert fa.fa_split_count(1, 32, 128, 3072, 128, 0) == 3
+    assert fa.fa_split_count(1, 16, 128, 4096, 128, 0) == 8   # 16 workgroups: chunks of 8 key tiles
+    # the key-split kernel (up to 2048 keys, its workgroups all resident)
+    # shortens these in one launch
+    assert fa.fa_split_count(2, 32, 128, 2048, 128, 0) == 1
+    assert fa.fa_split_count(1, 16, 128, 1536, 128, 0) == 1
+    assert fa.fa_split_count(2, 4, 1000, 1000, 64, 0) == 1
+    assert fa.fa_split_count(2, 4, 3000, 3000, 64, 0) == 1    # 192 workgroups of 128 rows
     assert fa.fa_split_count(1, 1, 8192, 8192, 64, 1) == 4
     assert fa.fa_split_count(2, 32, 128, 8192, 128, 1) == 1   # causal: the queries see 128 keys
     assert fa.fa_split_count(8, 32, 128, 8192, 128, 0) == 1

@@ -103,8 +103,9 @@ def test_window_zero_returns_values_bitwise(d, dtype):
 
 def test_padding_equals_truncated_keys_bitwise():
     # a padding length L gives what the unmasked kernel gives on the first L
-    # keys (same workgroup shape and exp path at d = 64)
-    B, H, N, d = 3, 4, 900, 64
+    # keys (same workgroup shape and exp path at d = 64; 20 heads keep both
+    # grids 4-wave and the unmasked one off the key-split kernel)
+    B, H, N, d = 3, 20, 900, 64
     q, k, v = make_qkv(B, H, N, d, "fp16", 220)
     lens = [900, 450, 63]
     for causal in (False, True):
@@ -116,8 +117,9 @@ def test_padding_equals_truncated_keys_bitwise():
 
 
 def test_wide_window_equals_no_window():
+    # 10 heads: the unmasked launch takes the direct kernel, not the key split
     for d, dtype in ((64, "fp16"), (128, "bf16")):
-        q, k, v = make_qkv(2, 2, 1000, d, dtype, 230 + d)
+        q, k, v = make_qkv(2, 10, 1000, d, dtype, 230 + d)
         for causal in (False, True):
             o_n, l_n = run_masked(q, k, v, causal)
             o_w, l_w = run_masked(q, k, v, causal, wl=5000, wr=5000)

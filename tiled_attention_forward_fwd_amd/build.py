@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = ["fa_api.hip", "fa_fwd_kernel.hip", "fa_fwd_masked.hip", "fa_fwd_hdim.hip",
-           "fa_fwd_hdim_masked.hip", "fa_fwd_f32.hip", "fa_bwd_kernel.hip",
+           "fa_fwd_hdim_masked.hip", "fa_fwd_ks.hip", "fa_fwd_f32.hip", "fa_bwd_kernel.hip",
            "fa_bwd_hdim.hip"]
 ARCH = "gfx950"
 

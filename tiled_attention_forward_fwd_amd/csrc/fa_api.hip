@@ -316,6 +316,23 @@ int bwd_checked(const void* q, const void* k, const void* v, const void* o, cons
 }
 
 
+// Plan of a key-split launch (fa::uses_key_split): workgroups of 32 query
+// rows and four waves, 32-key tiles each computed by one wave, so the MFMA
+// work is S = Q K^T and P V of every visited 32 x 32 tile pair.
+void key_split_plan(int B, int H, int Nq, int Nk, int d, int causal, fa_plan_t* plan)
+{
+    int64_t counts[4];
+    fa_tile_counts_qk(Nq, Nk, 32, 32, causal, counts);
+    const int64_t bh = (int64_t)B * H;
+    plan->block_m = 32;
+    plan->block_n = 32;
+    plan->threads = 256;
+    plan->lds_bytes = fa::ks_lds_bytes(d);
+    plan->workgroups = bh * ((Nq + 31) / 32);
+    plan->pairs_visited = bh * counts[1];
+    plan->mfma_flops = 2.0 * (2.0 * 32 * 32 * fa::compute_dim(d)) * (double)counts[1] * (double)bh;
+}
+
 }  // namespace
 
 extern "C" {
@@ -364,6 +381,14 @@ int fa_plan_qk(int B, int H, int Nq, int Nk, int d, int causal, int dtype, fa_pl
     if (!plan) return fail(FA_ERR_INVALID_ARG, "plan is NULL");
     const int rc = check_problem(B, H, Nq, Nk, d, causal, dtype);
     if (rc != FA_OK) return rc;
+    const double bh_all = (double)B * H;
+    const double pairs_all = causal ? causal_area(Nq, Nk) : (double)Nq * (double)Nk;
+    if (fa::uses_key_split(B, H, Nq, Nk, d, causal != 0)) {
+        key_split_plan(B, H, Nq, Nk, d, causal, plan);
+        plan->algo_flops = 4.0 * bh_all * pairs_all * d;
+        plan->algo_bytes = 4.0 * bh_all * ((double)Nq + Nk) * d + 4.0 * bh_all * Nq;
+        return FA_OK;
+    }
     const fa::Shape sh = fa::pick_shape(B, H, Nq, d, causal != 0);
     const int bm = sh.block_m, bn = fa::block_n(d);
     int64_t counts[4];
@@ -460,6 +485,8 @@ int fa_plan_masked(int B, int H, int Nq, int Nk, int d, int causal, int window_l
     plan->workgroups = (int64_t)B * H * ((Nq + bm - 1) / bm);
     plan->pairs_visited = (int64_t)(tiles * H);
     plan->mfma_flops = block_flops(d) * blocks * H;
+    if (off && fa::uses_key_split(B, H, Nq, Nk, d, causal != 0))  // the launch the plain entry points take
+        key_split_plan(B, H, Nq, Nk, d, causal, plan);
     plan->algo_flops = 4.0 * H * pairs * d;
     plan->algo_bytes = 4.0 * H * ((double)B * Nq + keys_read) * d + 4.0 * (double)B * H * Nq;
     return FA_OK;
@@ -536,6 +563,8 @@ int fa_split_count(int B, int H, int Nq, int Nk, int d, int causal)
         }
         if (s > n_kt / 2) s = n_kt / 2;
     } else {
+        // the key-split kernel shortens the walk of small grids in one launch
+        if (fa::uses_key_split(B, H, Nq, Nk, d, causal != 0)) return 1;
         s = 256 / wgs;
         const int64_t min_chunk = wgs <= 16 ? 8 : 16;
         if (s > n_kt / min_chunk) s = n_kt / min_chunk;

@@ -48,6 +48,7 @@ hipError_t launch_forward(const FwdArgs& a)
 {
     const bool padded = a.d != 64 && a.d != 128;
     if (a.masked) return padded ? launch_forward_hdim_masked(a) : launch_forward_masked(a);
+    if (!a.split && uses_key_split(a.B, a.H, a.Nq, a.Nk, a.d, a.causal)) return launch_forward_ks(a);
     if (padded) return launch_forward_hdim(a);
     return launch_variant<false, false>(a);
 }

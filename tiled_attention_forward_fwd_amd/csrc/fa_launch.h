@@ -52,6 +52,28 @@ inline int kernel_dim(int d) { return d <= 64 ? 64 : 128; }
 // (32, 64, 96 or 128), at most kernel_dim(d).
 inline int compute_dim(int d) { return (d + 31) / 32 * 32; }
 
+// Whether an unmasked direct launch runs the key-split kernel (fa_fwd_ks.h):
+// more than 32 query rows (fewer go to the split-key path), every 32-row
+// workgroup resident at once (256 at head dims above 64, where one workgroup's
+// 128 KB of LDS fills a CU, 512 below), and at most 2048 keys seen by the
+// longest query block (causal: min(Nq, Nk)). Measured on MI355X against the
+// direct and split launches (bf16, B*H from 1 to 64, 128 to 4096 query rows,
+// 128 to 16384 keys): it is the fastest inside these bounds (B2 H4 N1000
+// d64: 8.5 us against 13.7 direct and 15.9 split; N128: 4.1 against 4.8),
+// while more workgroups or longer key ranges favour the direct launch or the
+// split (more waves per key range).
+inline bool uses_key_split(int B, int H, int Nq, int Nk, int d, bool causal)
+{
+    const int64_t blocks = (int64_t)B * H * ((Nq + 31) / 32);
+    const int64_t keys = causal && Nq < Nk ? Nq : Nk;
+    const int64_t resident = kernel_dim(d) == 64 ? 512 : 256;
+    return Nq > 32 && blocks <= resident && keys <= 2048;
+}
+
+// LDS per key-split workgroup: two K and two V tiles of 32 keys for each of
+// its four waves (the merge reuses less than that).
+inline int ks_lds_bytes(int d) { return 4 * 4 * 32 * kernel_dim(d) * 2; }
+
 Shape pick_shape(int B, int H, int n_queries, int d, bool causal);
 // The shape of a masked launch: pick_shape's, except that a kernel head dim
 // of 128 keeps 4 waves.
@@ -69,6 +91,8 @@ hipError_t launch_forward(const FwdArgs& a);
 hipError_t launch_forward_masked(const FwdArgs& a);
 hipError_t launch_forward_hdim(const FwdArgs& a);
 hipError_t launch_forward_hdim_masked(const FwdArgs& a);
+// The key-split kernel for small grids (uses_key_split), any head dim.
+hipError_t launch_forward_ks(const FwdArgs& a);
 
 // fp32 inputs and outputs (d = 64 or 128): splits K and V into bf16 hi/lo
 // parts in `workspace` (4 * B*H*Nk*d bf16 values), then one kernel.
