@@ -445,7 +445,10 @@ def sweep(args):
             rows.append({"B": B, "H": H, "Nq": Nq, "N": Nk, "d": d,
                          "dtype": cfg["dtype"], "q_scale": cfg.get("q_scale", 1.0),
                          **({"window_left": wl, "window_right": wr, "key_lens": kls} if masked else {}),
-                         "causal": bool(causal), "splits": splits, "median_ms": med,
+                         "causal": bool(causal), "splits": splits,
+                         "launch": ("split" if splits > 1 else
+                                    "key-split" if (plan["block_m"], plan["block_n"]) == (32, 32) else "direct"),
+                         "workgroups": plan["workgroups"], "median_ms": med,
                          "min_ms": min(ts), "max_ms": max(ts),
                          "tflops": plan["algo_flops"] / (med * 1e-3) / 1e12,
                          "frac_peak": plan["algo_flops"] / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
