@@ -377,9 +377,50 @@ def headline(args):
     return out, (q, k, v)
 
 
+def c_call(fa, qd, kd, vd, out, lse, causal, splits, ws, ws_bytes, kl_ptr, wl, wr, code, stream):
+    """One forward call bound straight to its C entry point (pointers, sizes and stream fixed
+    beforehand), so that timing it measures the launch and the kernels rather than the Python
+    binding's argument checks: the call fa.fwd would make for the same arguments."""
+    lib = fa.load_library()
+    B, H, Nq, d = qd.shape
+    Nk = kd.shape[2]
+    scale = fa.default_scale(d)
+    p = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out.data_ptr(), lse.data_ptr())
+    masked = kl_ptr is not None or wl != -1 or wr != -1
+    if qd.dtype.itemsize == 4:
+        f, a = lib.fa_fwd_f32, p + (B, H, Nq, Nk, d, int(causal), scale, ws, ws_bytes, stream)
+    elif masked and splits == 1:
+        f, a = lib.fa_fwd_masked, p + (B, H, Nq, Nk, d, int(causal), wl, wr, kl_ptr, scale, code, stream)
+    elif masked:
+        f, a = lib.fa_fwd_split_masked, p + (B, H, Nq, Nk, d, int(causal), wl, wr, kl_ptr, scale, code, splits,
+                                             ws, ws_bytes, stream)
+    elif splits == 1:
+        f, a = lib.fa_fwd_qk, p + (B, H, Nq, Nk, d, int(causal), scale, code, stream)
+    else:
+        f, a = lib.fa_fwd_split_qk, p + (B, H, Nq, Nk, d, int(causal), scale, code, splits, ws, ws_bytes, stream)
+    rc = f(*a)
+    if rc != fa.FA_OK:
+        raise RuntimeError(f"forward call failed: {fa.fa_status_string(rc)}")
+    return lambda: f(*a)
+
+
+def back_to_back(fn, n, stream):
+    """Mean ms per call of n calls enqueued back to back between two HIP events on `stream`."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    b.synchronize()
+    return a.elapsed_time(b) / n
+
+
 def sweep(args):
     """Medians of 50 (after a separate warmup) for each configuration, with peak memory and
-    the fp64 oracle's rate on the host for the same configuration.
+    the fp64 oracle's rate on the host for the same configuration. Calls go straight to the C
+    entry points (c_call); median_ms brackets each call with its own events (the launch
+    latency included), b2b_ms is the mean of 50 calls enqueued back to back.
 
     peak_mem_bytes is the peak device allocation during the configuration's timed calls
     (statistics reset after its warmup) minus what was allocated before its inputs were
@@ -423,18 +464,19 @@ def sweep(args):
         masked = wl != -1 or wr != -1 or kls is not None
         kl_dev = None if kls is None else torch.tensor(kls, dtype=torch.int32, device=dev)
         for causal in cfg["flags"]:
-            splits = fa.fa_split_count(B, H, Nq, Nk, d, causal)
+            splits = 1 if cfg["dtype"] == "fp32" else fa.fa_split_count(B, H, Nq, Nk, d, causal)
             out = torch.empty_like(qd)
             lse = torch.empty((B, H, Nq), device=dev, dtype=torch.float32)
-            ws = (torch.empty(fa.fa_split_workspace_bytes(B, H, Nq, d, splits) // 4, device=dev,
-                              dtype=torch.float32) if splits > 1 else None)
-
-            def fn(causal=causal, splits=splits, out=out, lse=lse, ws=ws):
-                fa.fwd(qd, kd, vd, causal=bool(causal), out=out, lse=lse, splits=splits, workspace=ws,
-                       window_left=wl, window_right=wr, key_lens=kl_dev)
+            ws_bytes = (fa.fa_f32_workspace_bytes(B, H, Nk, d) if cfg["dtype"] == "fp32" else
+                        fa.fa_split_workspace_bytes(B, H, Nq, d, splits) if splits > 1 else 0)
+            ws = torch.empty(max(ws_bytes, 16) // 4, device=dev, dtype=torch.float32) if ws_bytes else None
+            stream = torch.cuda.current_stream(dev)
+            fn = c_call(fa, qd, kd, vd, out, lse, causal, splits, None if ws is None else ws.data_ptr(),
+                        ws_bytes, None if kl_dev is None else kl_dev.data_ptr(), wl, wr, code, stream.cuda_stream)
             warm(fn, 20, 0.5)
             torch.cuda.reset_peak_memory_stats(dev)
-            ts = timed_launches(fn, 50, torch.cuda.current_stream(dev))
+            ts = timed_launches(fn, 50, stream)
+            b2b = back_to_back(fn, 50, stream)
             if masked:
                 plan = fa.fa_plan_masked(B, H, Nq, Nk, d, causal, wl, wr, kls, code)
             else:
@@ -449,7 +491,7 @@ def sweep(args):
                          "launch": ("split" if splits > 1 else
                                     "key-split" if (plan["block_m"], plan["block_n"]) == (32, 32) else "direct"),
                          "workgroups": plan["workgroups"], "median_ms": med,
-                         "min_ms": min(ts), "max_ms": max(ts),
+                         "min_ms": min(ts), "max_ms": max(ts), "b2b_ms": b2b,
                          "tflops": plan["algo_flops"] / (med * 1e-3) / 1e12,
                          "frac_peak": plan["algo_flops"] / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                          "hbm_gbs_compulsory": plan["algo_bytes"] / (med * 1e-3) / 1e9,
