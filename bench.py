@@ -21,7 +21,8 @@ context for the roofline, and times the fp64 oracle on the host (cpu_baseline).
 Other modes (used to collect counters; each runs a few launches only):
     --profile-kernels   a few launches of each kernel of --profile-set (d128: the
                         headline, the default; d64; long: the long-context causal
-                        configuration with and without q x 4), nothing else
+                        configuration with and without q x 4; small: the two
+                        smallest configurations), nothing else
     --profile-timed     the same workloads after a warmup (for kernel traces)
     --copy-calibration  a plain device-to-device copy of a known size
     --profile-decode    the split-key decode path (one query x 16384 keys, B=1 H=32)
@@ -563,13 +564,16 @@ def profile_workloads(args, workloads, label):
 
 
 # Workload sets of --profile-kernels / --profile-set: the headline (d=128), the
-# headline at d=64, and the long-context causal configuration with and without
-# the heavy-tailed q.
+# headline at d=64, the long-context causal configuration with and without the
+# heavy-tailed q, and the two smallest configurations.
 PROFILE_SETS = {
     "d128": [HEADLINE],
     "d64": [dict(B=4, H=16, N=4096, d=64, dtype="bf16", seed=6)],
     "long": [dict(B=1, H=32, N=16384, d=128, dtype="bf16", seed=8, flags=(1,)),
              dict(B=1, H=32, N=16384, d=128, dtype="bf16", seed=9, q_scale=4.0, flags=(1,))],
+    # the two smallest configurations (key-split launches)
+    "small": [dict(B=1, H=1, N=128, d=64, dtype="fp16", seed=1),
+              dict(B=2, H=4, N=1000, d=64, dtype="bf16", seed=2)],
 }
 
 

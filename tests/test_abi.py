@@ -424,6 +424,12 @@ def test_plan_masked_shape(lib):
     # no mask in effect: the unmasked launch and its plan
     off = fa.fa_plan_masked(4, 16, 4096, 4096, 128, 1, -1, 7, None, fa.FA_DTYPE_BF16)
     assert off["block_m"] == fa.fa_plan_qk(4, 16, 4096, 4096, 128, 1, 1)["block_m"]
+    small = fa.fa_plan_masked(2, 4, 1000, 1000, 64, 0, -1, -1, None, fa.FA_DTYPE_BF16)
+    ref = fa.fa_plan_qk(2, 4, 1000, 1000, 64, 0, fa.FA_DTYPE_BF16)
+    assert ref["block_m"] == 32  # the key-split launch, also through the masked entry point
+    for key in ("block_m", "block_n", "threads", "lds_bytes", "workgroups", "pairs_visited", "mfma_flops",
+                "algo_flops", "algo_bytes"):
+        assert small[key] == ref[key], key
     with pytest.raises(fa.FaError):
         fa.fa_plan_masked(2, 1, 64, 64, 64, 0, -1, -1, [64, 65], fa.FA_DTYPE_BF16)
     with pytest.raises(fa.FaError):
