@@ -408,26 +408,29 @@ __device__ __forceinline__ void exp_tile(const f32x16 (&s)[QB][KB], const float 
 //     running max, where its P is 1 and rounds to the input type exactly; at
 //     P = 2^k (0 < k <= 12) its rounding (up to 2^-8 of itself for bf16)
 //     would move a row dominated by it by up to one output ulp.
-// Otherwise (always on the first tile, where m is still the initial -1e30,
-// when the scores grew by more than about 2^12 over m, and when a tile's keys
-// outweigh the row so far) the wave takes the true row max, rescales O and l
-// by alpha = 2^(m_old - m_new) and recomputes the tile's P (the update of
+// Otherwise (on the first tile, where m is still the initial -1e30, when the
+// scores grew by more than about 2^12 over m, and when a tile's keys outweigh
+// the row so far) the wave takes the true row max, rescales O and l by
+// alpha = 2^(m_old - m_new) and recomputes the tile's P (the update of
 // "Programming an attention kernel in Triton", online softmax). The branch is
-// wave-uniform. On iid N(0,1) inputs the second rule adds almost no refresh
-// beyond the first tile's.
+// wave-uniform. A caller that set m to the first tile's own row max before
+// its exponentials passes check = false for that tile: every P is then at
+// most 1, the largest exactly 1, and neither rule can ask for a refresh.
+// On iid N(0,1) inputs the second rule adds almost no refresh beyond that.
 constexpr float kLaneSumBound = 4096.0f;
 constexpr float kLaneSumGrowth = 4.0f;
 
 template <typename T, int QB, int KB, int DB, int KT, bool BS>
 __device__ __forceinline__ void softmax_finish(const f32x16 (&s)[QB][KB], f32x16 (&o)[QB][DB],
                                                float (&m_run)[QB], float (&l_run)[QB], float c_log2,
-                                               typename Mma<T>::vec8 (&p)[QB][KT], float (&rs)[QB])
+                                               typename Mma<T>::vec8 (&p)[QB][KT], float (&rs)[QB],
+                                               bool check = true)
 {
     bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
         bad = bad || !(rs[qb] <= kLaneSumBound) || rs[qb] > kLaneSumGrowth * l_run[qb];
-    if (__builtin_amdgcn_ballot_w64(bad)) {
+    if (check && __builtin_amdgcn_ballot_w64(bad)) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const float mx = row_max_log2<KB>(s[qb], c_log2);
@@ -447,11 +450,11 @@ __device__ __forceinline__ void softmax_finish(const f32x16 (&s)[QB][KB], f32x16
 template <typename T, int QB, int KB, int DB, int KT, bool BS>
 __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[QB][KB], f32x16 (&o)[QB][DB],
                                              float (&m_run)[QB], float (&l_run)[QB], float c_log2,
-                                             typename Mma<T>::vec8 (&p)[QB][KT])
+                                             typename Mma<T>::vec8 (&p)[QB][KT], bool check = true)
 {
     float rs[QB];
     exp_tile<T, QB, KB, KT, BS>(s, m_run, c_log2, p, rs);
-    softmax_finish<T, QB, KB, DB, KT, BS>(s, o, m_run, l_run, c_log2, p, rs);
+    softmax_finish<T, QB, KB, DB, KT, BS>(s, o, m_run, l_run, c_log2, p, rs, check);
 }
 
 // O^T += V^T P^T (operand layout at vt_operand). Each V operand feeds QB
@@ -502,10 +505,11 @@ __device__ __forceinline__ void pv_with_exp(const typename Mma<T>::vec8 (&p)[1][
 template <typename T, int D, int QB, int KB, int DB, int KT, bool BS>
 __device__ __forceinline__ void softmax_pv(const f32x16 (&s)[QB][KB], const uint16_t* __restrict__ vts,
                                            f32x16 (&o)[QB][DB], float (&m_run)[QB],
-                                           float (&l_run)[QB], float c_log2, int lane, int hh)
+                                           float (&l_run)[QB], float c_log2, int lane, int hh,
+                                           bool check = true)
 {
     typename Mma<T>::vec8 p[QB][KT];
-    softmax_tile<T, QB, KB, DB, KT, BS>(s, o, m_run, l_run, c_log2, p);
+    softmax_tile<T, QB, KB, DB, KT, BS>(s, o, m_run, l_run, c_log2, p, check);
     pv_tile<T, D, QB, DB, KT>(p, vts, o, lane, hh);
 }
 

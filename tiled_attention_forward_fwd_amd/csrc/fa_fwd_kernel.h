@@ -517,6 +517,7 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     // filled one step ahead) and the first block's partial row sum
     vec8 pa[QB][C::KT], pb[QB][C::KT];
     float ra = 0.f, rb = 0.f;
+    bool premax = false;  // m_run holds tile jb's row max (wave-uniform)
     if (MASKS) {
         // a wave's extra leading tile is masked without its scores having been
         // computed: give the registers a defined value
@@ -549,10 +550,18 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
         // every wave processes an unmasked tile of a direct launch
         if ((!SPLIT && (!MASKS || (jb >= u_lo && jb < u_hi))) || wave_sees(jb)) {
             scores<T, D, QB, C::KB, C::DS>(sa, kbuf(jb), qf, l32, hh);
-            if constexpr (kSplitExp) {
-                if (jb >= u_hi) apply_mask(sa[0], jb, 0);
-                ra = exp_range<T, C::KB, C::KT, 0, 16>(sa[0], m_run[0], c_log2, pa[0]);
+            // The running max starts at the first tile's own row max, so that
+            // tile's exponentials are taken once: against the initial -1e30
+            // they would fail the lazy-max test and be taken again. (A row
+            // that sees none of the tile's keys keeps -1e30.)
+            if (MASKS ? (jb < u_lo || jb >= u_hi) : jb >= u_hi) {
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) apply_mask(sa[qb], jb, qb);
             }
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) m_run[qb] = fmaxf(m_run[qb], row_max_log2<C::KB>(sa[qb], c_log2));
+            premax = true;
+            if constexpr (kSplitExp) ra = exp_range<T, C::KB, C::KT, 0, 16>(sa[0], m_run[0], c_log2, pa[0]);
         }
         stage_barrier();  // K_jb's buffer is refilled in the first iteration
     }
@@ -587,7 +596,8 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
                     rs[0] = exp_range<T, C::KB, C::KT, 16, 32>(sc[0], m_run[0], c_log2, pc[0]);
                 }
                 rs[0] = rc + rs[0];
-                softmax_finish<T, QB, C::KB, C::DB, C::KT, kBS>(sc, oacc, m_run, l_run, c_log2, pc, rs);
+                softmax_finish<T, QB, C::KB, C::DB, C::KT, kBS>(sc, oacc, m_run, l_run, c_log2, pc, rs,
+                                                                !(premax && j == jb));
                 if (!G || wave_sees(j + 1)) {
                     if (M || j + 1 >= u_hi) apply_mask(sn[0], j + 1, 0);
                     pv_with_exp<T, D, C::DB, C::KT, C::KB, 0, 16>(pc, vbuf(j), oacc, lane, hh, sn, m_run[0], c_log2,
@@ -615,7 +625,8 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
                 } else {
                     exp_tile<T, QB, C::KB, C::KT, kBS>(sc, m_run, c_log2, p, rs);
                 }
-                softmax_finish<T, QB, C::KB, C::DB, C::KT, kBS>(sc, oacc, m_run, l_run, c_log2, p, rs);
+                softmax_finish<T, QB, C::KB, C::DB, C::KT, kBS>(sc, oacc, m_run, l_run, c_log2, p, rs,
+                                                                !(premax && j == jb));
                 pv_tile<T, D, QB, C::DB, C::KT>(p, vbuf(j), oacc, lane, hh);
                 order_pv_block<D, WAVES, QB, DC>();
             }
@@ -628,7 +639,8 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
                     if (M) apply_mask(sc[qb], j, qb);
-                softmax_pv<T, D, QB, C::KB, C::DB, C::KT, kBS>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
+                softmax_pv<T, D, QB, C::KB, C::DB, C::KT, kBS>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh,
+                                                            !(premax && j == jb));
                 order_pv_block<D, WAVES, QB, DC>();
             }
         }
@@ -648,7 +660,8 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
             if (!G || wave_sees(j)) {
                 float rs[QB];
                 rs[0] = rc + exp_range<T, C::KB, C::KT, 16, 32>(sc[0], m_run[0], c_log2, pc[0]);
-                softmax_finish<T, QB, C::KB, C::DB, C::KT, kBS>(sc, oacc, m_run, l_run, c_log2, pc, rs);
+                softmax_finish<T, QB, C::KB, C::DB, C::KT, kBS>(sc, oacc, m_run, l_run, c_log2, pc, rs,
+                                                                !(premax && j == jb));
                 pv_tile<T, D, QB, C::DB, C::KT>(pc, vbuf(j), oacc, lane, hh);
                 order_pv_block<D, WAVES, QB, DC>();
             }
@@ -656,7 +669,8 @@ void fa_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
                 if (M) apply_mask(sc[qb], j, qb);
-            softmax_pv<T, D, QB, C::KB, C::DB, C::KT, kBS>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh);
+            softmax_pv<T, D, QB, C::KB, C::DB, C::KT, kBS>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh,
+                                                            !(premax && j == jb));
             order_pv_block<D, WAVES, QB, DC>();
         }
     };

@@ -138,7 +138,11 @@ void fa_fwd_ks_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
         f32x16 s[1][1];
         scores<T, D, 1, 1, C::DS>(s, kb + cur * TILE, qf, l32, hh);
         if (j >= u_hi) mask_scores<1, CAUSAL>(s[0], j * kKsKeys, qrow[0], Nk, hh);
-        softmax_pv<T, D, 1, 1, C::DB, 2, false>(s, vb + cur * TILE, oacc, m_run, l_run, c_log2, lane, hh);
+        // the wave's first tile starts the running max at its own row max,
+        // so its exponentials are taken once (no lazy-max check needed)
+        if (j == jb) m_run[0] = fmaxf(m_run[0], row_max_log2<1>(s[0], c_log2));
+        softmax_pv<T, D, 1, 1, C::DB, 2, false>(s, vb + cur * TILE, oacc, m_run, l_run, c_log2, lane, hh,
+                                                j != jb);
     }
 
     // merge: every wave's partial O (its accumulator layout), row max m (log2
