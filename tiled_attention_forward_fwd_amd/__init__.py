@@ -399,8 +399,10 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None, spli
               ``[B, H, Nq]`` float32).
     splits  : key chunks of the split-key path (``fa_fwd_split_qk``). None
               takes ``fa_split_count``'s suggestion, which is 1 (the direct
-              path) unless the grid is too small to fill the GPU; the
-              workspace is then allocated with torch unless given.
+              entry point, which runs its key-split kernel on small grids of
+              up to 2048 keys) unless the grid is too small to fill the GPU
+              over longer key ranges; the workspace is then allocated with
+              torch unless given.
     window_left, window_right, key_lens : the masks of ``fa_fwd_masked``
               (-1 = unbounded; key_lens a length-B int32 GPU tensor or a
               sequence, copied to the GPU). A row that sees no key gets O = 0

@@ -1,6 +1,7 @@
 // fa_fwd_kernel.hip -- host side of the attention forward: workgroup shape,
-// the choice among the four launch variants, and the variant without masks at
-// head dims 64 and 128 (kernels in fa_fwd_kernel.h).
+// the choice among the launch variants (masks, other head dims, the key-split
+// kernel for small grids), and the variant without masks at head dims 64 and
+// 128 (kernels in fa_fwd_kernel.h).
 
 #include "fa_fwd_kernel.h"
 

@@ -1,8 +1,9 @@
 // fa_launch.h -- internal interface between the C ABI (fa_api.hip) and the
-// kernels. The forward launches are split over four sources by variant
+// kernels. The forward launches are split over five sources by variant
 // (fa_fwd_kernel.hip: no masks, head dim 64 or 128; fa_fwd_masked.hip: masks;
-// fa_fwd_hdim.hip and fa_fwd_hdim_masked.hip: other head dims), all built
-// from the kernel template in fa_fwd_kernel.h. The backward pass is in
+// fa_fwd_hdim.hip and fa_fwd_hdim_masked.hip: other head dims), built from
+// the kernel template in fa_fwd_kernel.h, and fa_fwd_ks.hip, the key-split
+// kernel of fa_fwd_ks.h for small grids (any head dim). The backward pass is in
 // fa_bwd_kernel.h, launched from fa_bwd_kernel.hip (head dim 64 or 128) and
 // fa_bwd_hdim.hip (other head dims). Not installed; the public header is include/fa.h.
 #pragma once
