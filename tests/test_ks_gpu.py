@@ -126,3 +126,13 @@ def test_key_split_query_prefix_bitwise():
     o_pre, l_pre = fa.fwd(q[:, :, :704].contiguous().cuda(), k.cuda(), v.cuda(), causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o_pre, o_sq[:, :, :704]) and torch.equal(l_pre, l_sq[:, :, :704])
+
+
+@pytest.mark.parametrize("Nq,Nk,causal,d", [(100, 1, False, 64), (100, 1, True, 128), (40, 31, False, 64),
+                                            (33, 65, True, 128), (35, 97, False, 40), (1000, 33, True, 64),
+                                            (257, 100, False, 128)])
+def test_key_split_waves_without_keys(Nq, Nk, causal, d):
+    # fewer than four 32-key tiles: the later waves get empty ranges and must
+    # get weight zero in the merge; 33-35 query rows leave a block of 1-3 rows
+    q, k, v = qk_inputs(1, 3, Nq, Nk, d, "fp16", 760 + Nq + Nk)
+    run_and_check(q, k, v, causal, f"Nq{Nq} Nk{Nk} d{d}")
