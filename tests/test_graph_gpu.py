@@ -62,9 +62,12 @@ def replay_and_check(g, outs, inputs, eager, dtype, seed0):
         print(f"[graph] replay {r} equal to eager", flush=True)
 
 
+# (B, H): the key-split launch of a small grid, and the direct kernel
+@pytest.mark.parametrize("B,H,key_split", [(2, 4, True), (4, 16, False)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_forward_in_a_graph(causal):
-    q, k, v = (t.cuda() for t in make_qkv(2, 4, 1000, 128, "bf16", 700))
+def test_forward_in_a_graph(causal, B, H, key_split):
+    assert (fa.fa_plan_qk(B, H, 1000, 1000, 128, int(causal), fa.FA_DTYPE_BF16)["block_m"] == 32) == key_split
+    q, k, v = (t.cuda() for t in make_qkv(B, H, 1000, 128, "bf16", 700))
     f = lambda: fa.fwd(q, k, v, causal=causal, splits=1)  # noqa: E731
     g, outs = capture(f)
     replay_and_check(g, outs, (q, k, v), f, "bf16", 710)
