@@ -73,3 +73,52 @@ def test_random_shape(case):
     assert err_o <= TOL_O[q.dtype] and err_l <= 1e-3
     if causal:
         assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0])
+
+
+def draw_masked_cases(n, seed):
+    rng = random.Random(seed)
+    cases = []
+    while len(cases) < n:
+        B, H = rng.choice([1, 2, 3, 4]), rng.choice([1, 2, 4, 8])
+        Nq = rng.choice([1, 33, 100, 257, 640, 1000])
+        Nk = rng.choice([31, 64, 200, 511, 1000, 2048])
+        d = rng.choice([16, 40, 64, 96, 128])
+        dtype = rng.choice(["bf16", "fp16"])
+        causal = rng.random() < 0.5
+        wl = rng.choice([-1, -1, 0, 17, 128, 1000])
+        wr = -1 if causal else rng.choice([-1, -1, 0, 5, 300])
+        key_lens = [rng.randint(0, Nk) for _ in range(B)] if rng.random() < 0.6 else None
+        if wl == -1 and wr == -1 and key_lens is None:
+            continue  # no mask in effect: covered above
+        if B * H * Nq * Nk > 30_000_000:
+            continue
+        cases.append((B, H, Nq, Nk, d, dtype, causal, wl, wr, key_lens))
+    return cases
+
+
+MASKED_CASES = draw_masked_cases(24, 2025)
+
+
+@pytest.mark.parametrize("case", MASKED_CASES, ids=[f"B{c[0]}H{c[1]}q{c[2]}k{c[3]}d{c[4]}{c[5]}{'c' if c[6] else ''}"
+                                                    f"w{c[7]}_{c[8]}{'p' if c[9] else ''}" for c in MASKED_CASES])
+def test_random_masked_shape(case):
+    B, H, Nq, Nk, d, dtype, causal, wl, wr, key_lens = case
+    q = make_qkv(B, H, Nq, d, dtype, 900 + Nq + d)[0]
+    _, k, v = make_qkv(B, H, Nk, d, dtype, 901 + Nk)
+    splits = fa.fa_split_count(B, H, Nq, Nk, d, int(causal))
+    print(f"[case] masked {case} splits={splits}", flush=True)
+    scale = fa.default_scale(d)
+    o, lse = fa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale, window_left=wl, window_right=wr,
+                    key_lens=key_lens)
+    torch.cuda.synchronize()
+    o64, l64 = oracle.attention_fwd(q, k, v, causal, scale, window_left=wl, window_right=wr, key_lens=key_lens)
+    og = o.cpu().float().numpy().astype(np.float64)
+    lg = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(l64)
+    # rows that see no key: O = 0 and lse = -inf exactly
+    assert np.array_equal(np.isfinite(lg), fin) and np.all(og[~fin] == 0)
+    err_o = float(np.abs(og - o64).max())
+    err_l = float((np.abs(lg[fin] - l64[fin]) / np.maximum(1.0, np.abs(l64[fin]))).max()) if fin.any() else 0.0
+    print(f"[parity] random masked {case} max|dO|={err_o:.3e} ({100 * err_o / TOL_O[q.dtype]:.0f}% of bar) "
+          f"max rel dlse={err_l:.3e}", flush=True)
+    assert err_o <= TOL_O[q.dtype] and err_l <= 1e-3
