@@ -242,6 +242,8 @@ def test_plan_picks_workgroup_shape(lib):
     assert fa.fa_plan(4, 8, 1000, 64, 0, fa.FA_DTYPE_F16)["block_m"] == 128     # 1024
     assert fa.fa_plan(1, 8, 1500, 128, 0, fa.FA_DTYPE_BF16)["block_m"] == 128   # 376 at d = 128
     assert fa.fa_plan(1, 2, 2048, 96, 1, fa.FA_DTYPE_BF16)["lds_bytes"] == 4 * 4 * 32 * 128 * 2
+    # computing 128 dims it keeps a third K tile per wave (the next tile's scores come first)
+    assert fa.fa_plan(1, 2, 2048, 128, 1, fa.FA_DTYPE_BF16)["lds_bytes"] == 4 * 5 * 32 * 128 * 2
     assert fa.fa_plan(1, 2, 2048, 128, 1, fa.FA_DTYPE_BF16)["block_m"] == 32
     assert fa.fa_plan(1, 2, 4096, 128, 0, fa.FA_DTYPE_BF16)["block_m"] == 128   # 4096 keys
     assert fa.fa_plan_qk(1, 2, 32, 2048, 128, 0, fa.FA_DTYPE_BF16)["block_m"] == 128  # decode-like: split path

@@ -12,9 +12,11 @@
 // identity the split launch's merge applies (O = sum_w 2^(m_w - M) O_w /
 // sum_w 2^(m_w - M) l_w, M the largest m_w): one launch, no HBM partials.
 //
-//  * Tiles are 32 keys; each wave streams its own tiles through its own two
-//    K and two V buffers in LDS (the LDS DMA copies and swizzled layout of the
+//  * Tiles are 32 keys; each wave streams its own tiles through its own K
+//    and V buffers in LDS (the LDS DMA copies and swizzled layout of the
 //    direct kernel), so waves never wait for each other before the merge.
+//    Computing 128 dims, a wave issues the next tile's scores before this
+//    tile's softmax (ks_pipelined).
 //  * S^T = K Q^T, the lazy-max online softmax and O^T += V^T P^T are the
 //    direct kernel's device code at one 32-key block per tile.
 //  * Causal (top-left: row i sees keys j <= i) and ragged key counts mask the
@@ -64,13 +66,21 @@ __device__ __forceinline__ void ks_zero_pad(uint16_t* buf0, int n, int lane, int
     }
 }
 
-// LDS of the key-split kernel, in 2-byte units: per wave two K and two V
-// tiles; the merge then reuses the same memory for every wave's fp32 partial
-// O (DB blocks of 16 registers x 64 lanes) and its 32 row maxima and sums.
+// Whether the kernel computing DC dims issues the next tile's scores before
+// this tile's softmax (three K buffers). With 128 dims a workgroup's LDS
+// fills a CU and its waves run one per SIMD, and the overlap within the wave
+// measured 6-12% faster; with two waves per SIMD (64 dims and fewer) it was
+// 2-5% slower, and computing 96 dims 2%.
+constexpr bool ks_pipelined(int DC) { return DC == 128; }
+
+// LDS of the key-split kernel, in 2-byte units: per wave two (three when
+// pipelined) K and two V tiles; the merge then reuses the same memory for
+// every wave's fp32 partial O (DB blocks of 16 registers x 64 lanes) and its
+// 32 row maxima and sums.
 template <int D, int DC>
 constexpr int ks_lds_elems()
 {
-    constexpr int tiles = kKsWaves * 4 * kKsKeys * D;
+    constexpr int tiles = kKsWaves * (ks_pipelined(DC) ? 5 : 4) * kKsKeys * D;
     constexpr int merge = 2 * kKsWaves * ((DC / 32) * 16 * 64 + 2 * kKsRows);
     return tiles > merge ? tiles : merge;
 }
@@ -109,40 +119,79 @@ void fa_fwd_ks_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
     const int per = (n_t + kKsWaves - 1) / kKsWaves;
     const int jb = min(n_t, wave * per), je = min(n_t, jb + per);
 
-    uint16_t* const kb = smem + wave * 4 * TILE;  // K buffers 0, 1
-    uint16_t* const vb = kb + 2 * TILE;           // V buffers 0, 1
+    constexpr bool kPipe = ks_pipelined(DC);
+    constexpr int kKBufs = kPipe ? 3 : 2;
+    uint16_t* const kb = smem + wave * (kKBufs + 2) * TILE;  // K buffers
+    uint16_t* const vb = kb + kKBufs * TILE;                  // V buffers 0, 1
     const uint32_t row_bytes = (uint32_t)dmem * 2;
     const uint32_t head_bytes = (uint32_t)Nk * row_bytes;
     const rsrc_t krs = head_rsrc(k + kv_off, head_bytes), vrs = head_rsrc(v + kv_off, head_bytes);
-    if (PADDED) ks_zero_pad<D>(kb, 4, lane, dm);
+    if (PADDED) ks_zero_pad<D>(kb, kKBufs + 2, lane, dm);
 
     f32x16 oacc[1][C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) oacc[0][db] = (f32x16){};
     float m_run[1] = {-1e30f}, l_run[1] = {0.f};
 
-    if (jb < je) {
-        ks_copy_tile<D, PADDED>(kb, krs, jb * kKsKeys, lane, row_bytes, dm);
-        ks_copy_tile<D, PADDED>(vb, vrs, jb * kKsKeys, lane, row_bytes, dm);
-    }
-    for (int j = jb; j < je; ++j) {
-        // tile j has landed (and the zeroed chunks are written); the other
-        // buffers were last read by tile j - 1, whose reads have completed
-        __builtin_amdgcn_s_waitcnt(0);
-        asm volatile("" ::: "memory");
-        const int cur = (j - jb) & 1;
-        if (j + 1 < je) {
-            ks_copy_tile<D, PADDED>(kb + (cur ^ 1) * TILE, krs, (j + 1) * kKsKeys, lane, row_bytes, dm);
-            ks_copy_tile<D, PADDED>(vb + (cur ^ 1) * TILE, vrs, (j + 1) * kKsKeys, lane, row_bytes, dm);
-        }
-        f32x16 s[1][1];
-        scores<T, D, 1, 1, C::DS>(s, kb + cur * TILE, qf, l32, hh);
+    // Tile j's K sits in K buffer (j - jb) % kKBufs and its V in V buffer
+    // (j - jb) % 2. Each wave waits only for its own copies.
+    auto kbuf = [&](int j) { return kb + ((j - jb) % kKBufs) * TILE; };
+    auto vbuf = [&](int j) { return vb + ((j - jb) & 1) * TILE; };
+    auto tile_scores = [&](f32x16 (&s)[1][1], int j) {
+        scores<T, D, 1, 1, C::DS>(s, kbuf(j), qf, l32, hh);
         if (j >= u_hi) mask_scores<1, CAUSAL>(s[0], j * kKsKeys, qrow[0], Nk, hh);
-        // the wave's first tile starts the running max at its own row max,
-        // so its exponentials are taken once (no lazy-max check needed)
-        if (j == jb) m_run[0] = fmaxf(m_run[0], row_max_log2<1>(s[0], c_log2));
-        softmax_pv<T, D, 1, 1, C::DB, 2, false>(s, vb + cur * TILE, oacc, m_run, l_run, c_log2, lane, hh,
-                                                j != jb);
+    };
+    if constexpr (kPipe) {
+        // Step j computes the scores of tile j + 1 first and then the
+        // softmax and P.V of tile j, so that the wave's exponentials run while
+        // its score MFMAs are in flight; the copies of K_{j+2} and V_{j+1} are
+        // issued at its start, after the wait for K_{j+1} and V_j.
+        f32x16 sc[1][1];
+        if (jb < je) {
+            ks_copy_tile<D, PADDED>(kbuf(jb), krs, jb * kKsKeys, lane, row_bytes, dm);
+            ks_copy_tile<D, PADDED>(vbuf(jb), vrs, jb * kKsKeys, lane, row_bytes, dm);
+            if (jb + 1 < je) ks_copy_tile<D, PADDED>(kbuf(jb + 1), krs, (jb + 1) * kKsKeys, lane, row_bytes, dm);
+            __builtin_amdgcn_s_waitcnt(0);
+            asm volatile("" ::: "memory");
+            tile_scores(sc, jb);
+            // the first tile starts the running max at its own row max, so
+            // its exponentials are taken once (no lazy-max check needed)
+            m_run[0] = fmaxf(m_run[0], row_max_log2<1>(sc[0], c_log2));
+        }
+        for (int j = jb; j < je; ++j) {
+            // K_{j+1} and V_j have landed; the buffers the next copies fill
+            // were last read by the scores and the P.V of tile j - 1
+            __builtin_amdgcn_s_waitcnt(0);
+            asm volatile("" ::: "memory");
+            if (j + 2 < je) ks_copy_tile<D, PADDED>(kbuf(j + 2), krs, (j + 2) * kKsKeys, lane, row_bytes, dm);
+            if (j + 1 < je) ks_copy_tile<D, PADDED>(vbuf(j + 1), vrs, (j + 1) * kKsKeys, lane, row_bytes, dm);
+            f32x16 sn[1][1];
+            if (j + 1 < je) tile_scores(sn, j + 1);
+            softmax_pv<T, D, 1, 1, C::DB, 2, false>(sc, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh, j != jb);
+            if (j + 1 < je) sc[0][0] = sn[0][0];
+        }
+    } else {
+        if (jb < je) {
+            ks_copy_tile<D, PADDED>(kbuf(jb), krs, jb * kKsKeys, lane, row_bytes, dm);
+            ks_copy_tile<D, PADDED>(vbuf(jb), vrs, jb * kKsKeys, lane, row_bytes, dm);
+        }
+        for (int j = jb; j < je; ++j) {
+            // tile j has landed (and the zeroed chunks are written); the
+            // other buffers were last read by tile j - 1, whose reads have
+            // completed
+            __builtin_amdgcn_s_waitcnt(0);
+            asm volatile("" ::: "memory");
+            if (j + 1 < je) {
+                ks_copy_tile<D, PADDED>(kbuf(j + 1), krs, (j + 1) * kKsKeys, lane, row_bytes, dm);
+                ks_copy_tile<D, PADDED>(vbuf(j + 1), vrs, (j + 1) * kKsKeys, lane, row_bytes, dm);
+            }
+            f32x16 s[1][1];
+            tile_scores(s, j);
+            // the wave's first tile starts the running max at its own row
+            // max, so its exponentials are taken once (no lazy-max check)
+            if (j == jb) m_run[0] = fmaxf(m_run[0], row_max_log2<1>(s[0], c_log2));
+            softmax_pv<T, D, 1, 1, C::DB, 2, false>(s, vbuf(j), oacc, m_run, l_run, c_log2, lane, hh, j != jb);
+        }
     }
 
     // merge: every wave's partial O (its accumulator layout), row max m (log2

@@ -56,7 +56,7 @@ inline int compute_dim(int d) { return (d + 31) / 32 * 32; }
 // Whether an unmasked direct launch runs the key-split kernel (fa_fwd_ks.h):
 // more than 32 query rows (fewer go to the split-key path), every 32-row
 // workgroup resident at once (256 at head dims above 64, where one workgroup's
-// 128 KB of LDS fills a CU, 512 below), and at most 2048 keys seen by the
+// 128-160 KB of LDS fills a CU, 512 below), and at most 2048 keys seen by the
 // longest query block (causal: min(Nq, Nk)). Measured on MI355X against the
 // direct and split launches (bf16, B*H from 1 to 64, 128 to 4096 query rows,
 // 128 to 16384 keys): it is the fastest inside these bounds (B2 H4 N1000
@@ -71,9 +71,10 @@ inline bool uses_key_split(int B, int H, int Nq, int Nk, int d, bool causal)
     return Nq > 32 && blocks <= resident && keys <= 2048;
 }
 
-// LDS per key-split workgroup: two K and two V tiles of 32 keys for each of
-// its four waves (the merge reuses less than that).
-inline int ks_lds_bytes(int d) { return 4 * 4 * 32 * kernel_dim(d) * 2; }
+// LDS per key-split workgroup: two K (three when it computes 128 dims) and
+// two V tiles of 32 keys for each of its four waves (the merge reuses less
+// than that).
+inline int ks_lds_bytes(int d) { return 4 * (compute_dim(d) == 128 ? 5 : 4) * 32 * kernel_dim(d) * 2; }
 
 Shape pick_shape(int B, int H, int n_queries, int d, bool causal);
 // The shape of a masked launch: pick_shape's, except that a kernel head dim
