@@ -91,6 +91,28 @@ def test_config_parity(cfg, causal):
     check(q, k, v, causal, label=label)
 
 
+# Beyond the workload list, on every element: the other input type at the
+# headline shape (fp16 has a 3-bit longer mantissa, so its bar is 8x tighter),
+# and heavy-tailed scores (q x 4) through the 8-wave non-causal kernel, whose
+# lazy running max the causal q x 4 configuration above does not reach.
+EXTRA = [
+    ("fp16 N4096 d128", 4, 16, 4096, 128, "fp16", 10, 1.0, (False, True)),
+    ("fp16 N4096 d128 q*4", 2, 16, 4096, 128, "fp16", 11, 4.0, (False, True)),
+    ("bf16 N4096 d128 q*4", 2, 16, 4096, 128, "bf16", 12, 4.0, (False,)),
+    ("fp16 N4096 d64 q*4", 2, 16, 4096, 64, "fp16", 13, 4.0, (False, True)),
+]
+EXTRA_CASES = [(c, causal) for c in EXTRA for causal in c[8]]
+
+
+@pytest.mark.parametrize("cfg,causal", EXTRA_CASES,
+                         ids=[f"{c[0]} {'causal' if f else 'noncausal'}" for c, f in EXTRA_CASES])
+def test_more_parity_every_row(cfg, causal):
+    label, B, H, N, d, dtype, seed, qs, _ = cfg
+    print(f"[case] {label} causal={causal} (every row)", flush=True)
+    q, k, v = make_qkv(B, H, N, d, dtype, seed, q_scale=qs)
+    check(q, k, v, causal, label=label)
+
+
 @pytest.mark.parametrize("normalised", [False, True], ids=["raw-q", "unit-q"])
 def test_one_late_key_dominates_each_row(normalised):
     # Row i's own key dominates its row: k_i = g * q_i, so s_ii = g*|q_i|^2/sqrt(d)
