@@ -4,7 +4,8 @@ drawn from a fixed generator, so that one run crosses the launch choices
 (direct 4- and 8-wave, key-split, split-key with its merge) at shapes no
 other test names. Each case is checked against the fp64 oracle at the forward
 tests' bars (4e-3 fp16 / 3.2e-2 bf16 on O, 1e-3 relative on lse) through
-fa.fwd with the suggested split count.
+fa.fwd with the suggested split count. Two more draws add padding lengths and
+windows, and heavy-tailed scores (q x 4).
 """
 
 import random
@@ -120,5 +121,47 @@ def test_random_masked_shape(case):
     err_o = float(np.abs(og - o64).max())
     err_l = float((np.abs(lg[fin] - l64[fin]) / np.maximum(1.0, np.abs(l64[fin]))).max()) if fin.any() else 0.0
     print(f"[parity] random masked {case} max|dO|={err_o:.3e} ({100 * err_o / TOL_O[q.dtype]:.0f}% of bar) "
+          f"max rel dlse={err_l:.3e}", flush=True)
+    assert err_o <= TOL_O[q.dtype] and err_l <= 1e-3
+
+
+def draw_heavy_cases(n, seed):
+    rng = random.Random(seed)
+    cases = []
+    while len(cases) < n:
+        B, H = rng.choice([1, 2, 4]), rng.choice([1, 4, 8, 16])
+        Nq = rng.choice([1, 33, 257, 640, 1000, 1500, 2048])
+        Nk = rng.choice([64, 511, 1000, 2048, 3000])
+        d = rng.choice([32, 64, 96, 128])
+        dtype = rng.choice(["bf16", "fp16"])
+        causal = rng.random() < 0.5
+        if B * H * Nq * Nk > 40_000_000:
+            continue
+        cases.append((B, H, Nq, Nk, d, dtype, causal))
+    return cases
+
+
+HEAVY_CASES = draw_heavy_cases(12, 2026)
+
+
+@pytest.mark.parametrize("case", HEAVY_CASES, ids=[f"B{c[0]}H{c[1]}q{c[2]}k{c[3]}d{c[4]}{c[5]}{'c' if c[6] else ''}"
+                                                   for c in HEAVY_CASES])
+def test_random_heavy_tailed_shape(case):
+    # q x 4 spreads the scores over about 4x the log2 range, so later key tiles
+    # raise the running max and the lazy-max refresh runs in every launch kind
+    B, H, Nq, Nk, d, dtype, causal = case
+    q = make_qkv(B, H, Nq, d, dtype, 1000 + Nq + d, q_scale=4.0)[0]
+    _, k, v = make_qkv(B, H, Nk, d, dtype, 1001 + Nk)
+    splits = fa.fa_split_count(B, H, Nq, Nk, d, int(causal))
+    print(f"[case] heavy {case} splits={splits}", flush=True)
+    scale = fa.default_scale(d)
+    o, lse = fa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o64, l64 = oracle.attention_fwd(q, k, v, causal, scale)
+    og = o.cpu().float().numpy().astype(np.float64)
+    lg = lse.cpu().numpy().astype(np.float64)
+    err_o = float(np.abs(og - o64).max())
+    err_l = float((np.abs(lg - l64) / np.maximum(1.0, np.abs(l64))).max())
+    print(f"[parity] random heavy {case} max|dO|={err_o:.3e} ({100 * err_o / TOL_O[q.dtype]:.0f}% of bar) "
           f"max rel dlse={err_l:.3e}", flush=True)
     assert err_o <= TOL_O[q.dtype] and err_l <= 1e-3
