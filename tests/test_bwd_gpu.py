@@ -9,6 +9,8 @@ covers one rounding of P or dS per product and one of the output; measured
 errors are 2e-3 to 5e-3 (bf16) and 2e-4 to 7e-4 (fp16).
 """
 
+import random
+
 import numpy as np
 import pytest
 import torch
@@ -230,3 +232,32 @@ def test_backward_head_dim_masks_and_guard_regions():
         assert err <= TOL[torch.float16]
     # keys past a batch's length get zero gradients
     assert torch.all(outs[1][1][1, :, 300:] == 0) and torch.all(outs[2][1][1, :, 300:] == 0)
+
+
+def draw_bwd_cases(n, seed):
+    rng = random.Random(seed)
+    cases = []
+    while len(cases) < n:
+        B, H = rng.choice([1, 2, 3]), rng.choice([1, 2, 4])
+        Nq = rng.choice([1, 31, 64, 100, 257, 600])
+        Nk = rng.choice([1, 33, 64, 200, 511, 900])
+        d = rng.choice([16, 24, 40, 64, 80, 96, 128])
+        dtype = rng.choice(["bf16", "fp16"])
+        causal = rng.random() < 0.5
+        if B * H * Nq * Nk > 4_000_000:
+            continue
+        cases.append((B, H, Nq, Nk, d, dtype, causal))
+    return cases
+
+
+RANDOM_CASES = draw_bwd_cases(16, 2027)
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[f"B{c[0]}H{c[1]}q{c[2]}k{c[3]}d{c[4]}{c[5]}{'c' if c[6] else ''}"
+                                                    for c in RANDOM_CASES])
+def test_backward_random_shapes(case):
+    # seeded random shapes: ragged query and key counts both ways, every
+    # head-dim class, both input types and flags
+    B, H, Nq, Nk, d, dtype, causal = case
+    print(f"[case] bwd random {case}", flush=True)
+    check_bwd(B, H, Nq, d, dtype, causal, 580 + Nq % 70, Nk=Nk)
